@@ -1,0 +1,242 @@
+"""Benchmark of the NVFP4 block-scaled grouped GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload I] [--all]
+
+A step is one call of the grouped GEMM (the whole hot path) on one batch of
+seeded synthetic input that is already resident in HBM. The headline workload
+is the largest grouped configuration (G=2: 4096x4096x8192 and 2048x7168x4096).
+Timed calls rotate over enough input/output sets (>= 1 GiB in total) that the
+256 MiB last-level cache cannot serve repeated calls ("cold"); the same-buffer
+("hot") number is reported beside it.
+
+Prints ONE JSON line on stdout. The roofline fraction uses the MI355X dense
+f16 MFMA peak (the MFMA precision of the kernel) and the kernel's average
+duration, timed with HIP events on the stream the kernel is launched on.
+``cpu_baseline`` times the CPU oracle on the host cores on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "TFLOPS (2·Σm·n·k) and µs/call per grouped-GEMM config; % of MFMA peak"
+PEAK_F16_TFLOPS = 2500.0  # MI355X dense f16/bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0
+COLD_BYTES = 1 << 30
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(shapes):
+    """FLOPs (2*m*n*k*l, real m) and bytes (A, B, tiled SFA/SFB and C, each once)."""
+    fl = sum(2 * m * n * k * l for (m, n, k, l) in shapes)
+    by = 0
+    for (m, n, k, l) in shapes:
+        by += l * (m * k // 2 + n * k // 2 + 2 * m * n)
+        by += l * (-(-m // 128) * 128 + -(-n // 128) * 128) * (k // 16)
+    return fl, by
+
+
+def percentile(v, p):
+    return float(np.percentile(np.asarray(v), p))
+
+
+def time_workload(idx, steps, warmup, tile_config=-1, cold=True):
+    import torch
+
+    import moe_matmul_amd as mm
+    from moe_matmul_amd import device as dev
+    from moe_matmul_amd import synth
+
+    shapes, groups = synth.make_workload(idx)
+    base = dev.upload(shapes, groups)
+    flops, nbytes = algorithmic(shapes)
+    sets = [base]
+    if cold:
+        nsets = max(1, -(-COLD_BYTES // nbytes))
+        for _ in range(nsets - 1):
+            cp = []
+            for d in base:
+                e = {k: (v.clone() if hasattr(v, "clone") else v) for k, v in d.items() if k != "c"}
+                e["c"] = e["c_store"][d["c_guard"]: d["c_guard"] + d["c"].numel()]
+                cp.append(e)
+            sets.append(cp)
+    stream = torch.cuda.current_stream()
+    ptrs = [dev.pointer_tables(s) for s in sets]
+
+    def call(i):
+        abc, sf = ptrs[i % len(ptrs)]
+        mm.nvfp4_grouped_gemm_config(shapes, abc, sf, len(shapes), stream, tile_config)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(steps):
+        call(i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]  # ms
+    total_ms = evs[0].elapsed_time(evs[steps])
+    geo = mm.nvfp4_launch_geometry(shapes, torch.cuda.get_device_properties(0).multi_processor_count, tile_config)
+    avg_s = total_ms / steps / 1e3
+    return dict(
+        workload=synth.WORKLOADS[idx]["name"], shapes=[list(s) for s in shapes], flops=flops, bytes=nbytes,
+        total_ms=total_ms, wall_s=wall, ms_per_call=total_ms / steps,
+        us_median=percentile(per, 50) * 1e3, us_p10=percentile(per, 10) * 1e3, us_p90=percentile(per, 90) * 1e3,
+        tflops=flops / avg_s / 1e12, gbs=nbytes / avg_s / 1e9, sets=len(sets), tile_config=geo["config"],
+        tiles=geo["total_tiles"], grid=geo["grid"],
+    )
+
+
+def cpu_baseline(idx, max_rows=None):
+    """The CPU oracle, as it stands, on workload ``idx`` (rows capped per group)."""
+    from threadpoolctl import threadpool_info
+
+    import oracle.nvfp4_oracle as O
+    from moe_matmul_amd import synth
+
+    shapes, groups = synth.make_workload(idx)
+    fl = 0
+    t0 = time.perf_counter()
+    for (m, n, k, l), g in zip(shapes, groups):
+        rows = m if max_rows is None else min(m, max_rows)
+        O.gemm_group(m, n, k, l, g["a"], g["b"], g["sfa"], g["sfb"], rows=np.arange(rows))
+        fl += 2 * rows * n * k * l
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    sample = (f"{synth.WORKLOADS[idx]['name']}, " +
+              ("all rows" if max_rows is None else f"first {max_rows} rows per group") +
+              f" ({fl / 1e9:.1f} GFLOP of C; float64 dequant + BLAS, C and S)")
+    return dict(value=fl / dt / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle", sample=sample,
+                seconds=dt, cpu_count=os.cpu_count())
+
+
+def load_traffic(workload_name):
+    """HBM traffic per launch measured with rocprofv3 counters, if it was taken
+    on the current kernel source (matched by hash); else None."""
+    import hashlib
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    src = os.path.join(ROOT, "moe_matmul_amd", "csrc", "nvfp4_grouped_gemm.hip")
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    rec = json.load(open(p)).get(workload_name)
+    if not rec or rec.get("source_sha256") != digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=4)
+    ap.add_argument("--tile-config", type=int, default=-1)
+    ap.add_argument("--all", action="store_true", help="also time every workload (to stderr / --out)")
+    ap.add_argument("--out", default=None, help="write the per-workload details as JSON here")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=None, help="cap rows per group of the CPU sample")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the grouped GEMM has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_matmul_amd as mm
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    mm.load_library()
+
+    head = time_workload(args.workload, args.steps, args.warmup, args.tile_config, cold=True)
+    hot = time_workload(args.workload, args.steps, args.warmup, args.tile_config, cold=False)
+    log(f"[bench] cold {head['tflops']:.1f} TFLOP/s {head['us_median']:.1f} us/call; "
+        f"hot {hot['tflops']:.1f} TFLOP/s")
+    details = {"headline": head, "hot": hot}
+    if args.all:
+        allres = []
+        for i in range(5):
+            r = time_workload(i, max(20, args.steps // 2), 5, -1, cold=True)
+            allres.append(r)
+            log(f"[bench] workload {i} {r['workload']}: {r['tflops']:.1f} TFLOP/s, {r['us_median']:.1f} us/call "
+                f"(p10 {r['us_p10']:.1f}, p90 {r['us_p90']:.1f}), {r['gbs']:.0f} GB/s, cfg {r['tile_config']}, "
+                f"{r['tiles']} tiles")
+        details["all"] = allres
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.workload, args.cpu_rows)
+        log(f"[bench] cpu oracle {cpu['value'] * 1e3:.1f} GFLOP/s on {cpu['cores']} threads in {cpu['seconds']:.1f} s")
+
+    achieved = head["flops"] / (head["total_ms"] / args.steps / 1e3) / 1e12
+    traffic = load_traffic(head["workload"])
+    line = {
+        "metric": METRIC,
+        "value": round(head["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_call"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": head["workload"],
+            "groups": len(head["shapes"]),
+            "shapes_mnkl": head["shapes"],
+            "operands": "FP4 E2M1 A/B, E4M3 scale per 16 K, fp32 accumulate, fp16 C",
+            "mfma": "v_mfma_f32_32x32x16_f16 on exactly dequantised operands",
+            "tile_config": head["tile_config"],
+            "tiles": head["tiles"],
+            "grid": head["grid"],
+            "cache": f"cold: {head['sets']} rotating input/output sets",
+        },
+        "us_per_call": {"median": round(head["us_median"], 2), "p10": round(head["us_p10"], 2),
+                        "p90": round(head["us_p90"], 2)},
+        "hot": {"value": round(hot["tflops"], 2), "us_median": round(hot["us_median"], 2)},
+        "algorithmic_gbs": round(head["gbs"], 1),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_F16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_F16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": None if cpu is None else {k: (round(v, 6) if isinstance(v, float) else v)
+                                                  for k, v in cpu.items() if k in ("value", "unit", "cores",
+                                                                                   "kind", "sample")},
+    }
+    if args.out:
+        with open(args.out, "w") as f:
+            json.dump(dict(details, cpu_baseline=cpu, line=line), f, indent=1)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

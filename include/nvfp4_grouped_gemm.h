@@ -1,0 +1,134 @@
+/*
+ * nvfp4_grouped_gemm.h - C ABI of the NVFP4 block-scaled grouped GEMM for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Operation (the contraction stated in the mainloop comment of submission
+ * 499344 and built as a block-scaled MMA in my_kernel of submission 506336,
+ * kernelindex.com "kernelbot nvfp4 group gemm"): for every group g
+ *
+ *     C_g[m, n, l] = sum_k (a_g[m, k, l] * sfa_g[m, k/16, l])
+ *                        * (b_g[n, k, l] * sfb_g[n, k/16, l])
+ *
+ * accumulated in fp32 and written as fp16 (round to nearest even, overflow to
+ * +-inf).
+ *
+ * Layouts (the operand and scale layouts built in kernel of submission 385043;
+ * tensor shapes from the custom_kernel docstring of submission 499344):
+ *   A   uint8 [l][m][k/2]  two FP4 E2M1 codes per byte, K-major; the low
+ *                          nibble holds the even K element.
+ *   B   uint8 [l][n][k/2]  same.
+ *   SFA uint8, tiled: one FP8 E4M3FN scale per row per 16 K-elements. The byte
+ *       of row r, 16-block kb, batch li sits at
+ *         li*Mt*Kt*512 + (r/128)*Kt*512 + (kb/4)*512
+ *           + (r%32)*16 + ((r/32)%4)*4 + kb%4
+ *       with Mt = ceil(m/128) and Kt = ceil(k/64); the tensor is padded to
+ *       whole 128-row atoms (see nvfp4_sf_bytes). Padded rows are never used.
+ *   SFB same with n in place of m.
+ *   C   fp16 [l][m][n], row-major.
+ *
+ * Ownership and threading: the caller owns every buffer. The library keeps no
+ * per-call state and allocates nothing; the host tables are read before the
+ * call returns, so they may be reused at once. The only global state is a
+ * per-device cache of the compute-unit count. Calls are stream-ordered and
+ * asynchronous (they do not synchronise).
+ */
+#ifndef NVFP4_GROUPED_GEMM_H
+#define NVFP4_GROUPED_GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_MAX_GROUPS 8
+
+/* Return codes. */
+#define NVFP4_OK 0
+#define NVFP4_ERR_INVALID (-1)    /* bad group count, size, divisibility or null pointer */
+#define NVFP4_ERR_MISALIGNED (-2) /* a device pointer is not 16-byte aligned */
+#define NVFP4_ERR_HIP (-3)        /* the HIP runtime reported an error; see nvfp4_last_hip_error */
+#define NVFP4_ERR_CONFIG (-4)     /* unknown tile configuration id */
+
+/*
+ * nvfp4_grouped_gemm - run the grouped GEMM on `stream`.
+ *
+ *   problem_sizes  host int32 [num_groups][4] = (m, n, k, l) per group.
+ *   ptrs_abc       host uint64 [num_groups][3] = device addresses of A, B, C.
+ *   ptrs_sfa_sfb   host uint64 [num_groups][2] = device addresses of SFA, SFB.
+ *   num_groups     1 .. NVFP4_MAX_GROUPS.
+ *   stream         a hipStream_t (NULL = the default stream).
+ *
+ * Requirements, checked before any HIP call (else NVFP4_ERR_INVALID or
+ * NVFP4_ERR_MISALIGNED, and nothing is launched):
+ *   m, n, k >= 0, l >= 1; k % 64 == 0; n % 8 == 0; k <= 2^22; the bytes of
+ *   each of A, B, SFA and SFB (all l batches) below 2^31; m*n*l <= 2^40.
+ *   For a group with m > 0 and n > 0, C must be
+ *   non-null and 16-byte aligned, and when k > 0 also A, B, SFA and SFB.
+ * Semantics at the edges: a group with m == 0 or n == 0 leaves C untouched;
+ * k == 0 writes C = 0 (the empty sum).
+ * Returns NVFP4_OK once the kernel is enqueued, NVFP4_ERR_HIP if the launch
+ * failed.
+ */
+int nvfp4_grouped_gemm(const int32_t* problem_sizes, const uint64_t* ptrs_abc,
+                       const uint64_t* ptrs_sfa_sfb, int num_groups, void* stream);
+
+/*
+ * nvfp4_grouped_gemm_config - as nvfp4_grouped_gemm, with the tile
+ * configuration chosen by the caller (0 .. nvfp4_num_tile_configs()-1) instead
+ * of by the built-in heuristic; -1 means "heuristic". For tests and tuning.
+ * Returns NVFP4_ERR_CONFIG for an unknown id.
+ */
+int nvfp4_grouped_gemm_config(const int32_t* problem_sizes, const uint64_t* ptrs_abc,
+                              const uint64_t* ptrs_sfa_sfb, int num_groups, void* stream,
+                              int tile_config);
+
+/*
+ * nvfp4_grouped_gemm_validate - the argument checks of nvfp4_grouped_gemm
+ * alone. Makes no HIP call (usable without a GPU). Same return codes.
+ */
+int nvfp4_grouped_gemm_validate(const int32_t* problem_sizes, const uint64_t* ptrs_abc,
+                                const uint64_t* ptrs_sfa_sfb, int num_groups);
+
+/* Number of compiled tile configurations. */
+int nvfp4_num_tile_configs(void);
+
+/*
+ * nvfp4_tile_config_info - tile shape of configuration `cfg`: output tile
+ * bm x bn, K-step bk, threads per workgroup. Any output pointer may be NULL.
+ * Returns NVFP4_ERR_CONFIG for an unknown id.
+ */
+int nvfp4_tile_config_info(int cfg, int* bm, int* bn, int* bk, int* threads);
+
+/*
+ * nvfp4_select_tile_config - the configuration the heuristic picks for these
+ * problem sizes on a device with `num_cus` compute units (host only, no HIP
+ * call). Returns a config id, or NVFP4_ERR_INVALID.
+ */
+int nvfp4_select_tile_config(const int32_t* problem_sizes, int num_groups, int num_cus);
+
+/*
+ * nvfp4_launch_geometry - for configuration `cfg` (-1 = heuristic) and these
+ * sizes: total output tiles and the persistent grid size on `num_cus` compute
+ * units (host only, no HIP call). Returns the config id used, or an error.
+ */
+int nvfp4_launch_geometry(const int32_t* problem_sizes, int num_groups, int num_cus, int cfg,
+                          int64_t* total_tiles, int* grid);
+
+/* Size in bytes of one tiled scale tensor for `rows` rows and `k` K-elements,
+ * l batches: ceil(rows/128)*128 * ceil(k/64)*4 * l. Returns 0 if any is < 0. */
+size_t nvfp4_sf_bytes(int rows, int k, int l);
+
+/* The hipError_t of the last failed HIP call made by this library on the
+ * calling thread (0 if none). */
+int nvfp4_last_hip_error(void);
+
+/* Static text for a return code. */
+const char* nvfp4_error_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_GROUPED_GEMM_H */

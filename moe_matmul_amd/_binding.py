@@ -1,0 +1,144 @@
+"""ctypes binding of the C ABI in include/nvfp4_grouped_gemm.h.
+
+Argument marshalling only: every step of the computation runs in the HIP
+library. The names mirror the C entry points. The library must have been
+built (``python -m moe_matmul_amd.build``); there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4_grouped_gemm.so")
+
+NVFP4_OK = 0
+NVFP4_ERR_INVALID = -1
+NVFP4_ERR_MISALIGNED = -2
+NVFP4_ERR_HIP = -3
+NVFP4_ERR_CONFIG = -4
+NVFP4_MAX_GROUPS = 8
+
+_lib = None
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what} failed: {code} ({nvfp4_error_string(code)})"
+                         + (f", hip error {nvfp4_last_hip_error()}" if code == NVFP4_ERR_HIP else ""))
+
+
+def load_library() -> ctypes.CDLL:
+    """Load the built library (raises if it is missing)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run `python -m moe_matmul_amd.build` "
+                          "(the NVFP4 grouped GEMM has no non-HIP implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    u64p = ctypes.POINTER(ctypes.c_uint64)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    ip = ctypes.POINTER(ctypes.c_int)
+    sig = {
+        "nvfp4_grouped_gemm": (ctypes.c_int, [i32p, u64p, u64p, ctypes.c_int, ctypes.c_void_p]),
+        "nvfp4_grouped_gemm_config": (ctypes.c_int, [i32p, u64p, u64p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int]),
+        "nvfp4_grouped_gemm_validate": (ctypes.c_int, [i32p, u64p, u64p, ctypes.c_int]),
+        "nvfp4_num_tile_configs": (ctypes.c_int, []),
+        "nvfp4_tile_config_info": (ctypes.c_int, [ctypes.c_int, ip, ip, ip, ip]),
+        "nvfp4_select_tile_config": (ctypes.c_int, [i32p, ctypes.c_int, ctypes.c_int]),
+        "nvfp4_launch_geometry": (ctypes.c_int, [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, i64p, ip]),
+        "nvfp4_sf_bytes": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int, ctypes.c_int]),
+        "nvfp4_last_hip_error": (ctypes.c_int, []),
+        "nvfp4_error_string": (ctypes.c_char_p, [ctypes.c_int]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _sizes(problem_sizes):
+    flat = [int(v) for row in problem_sizes for v in row]
+    return (ctypes.c_int32 * max(len(flat), 1))(*flat), len(flat) // 4
+
+
+def _u64(rows, width):
+    flat = [int(v) for row in rows for v in row]
+    if len(flat) % width:
+        raise ValueError(f"pointer table rows must have {width} entries")
+    return (ctypes.c_uint64 * max(len(flat), 1))(*flat)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        return ctypes.c_void_p(0)
+    if hasattr(stream, "cuda_stream"):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def nvfp4_grouped_gemm(problem_sizes, ptrs_abc, ptrs_sfa_sfb, num_groups=None, stream=None) -> None:
+    """Enqueue the grouped GEMM; ``problem_sizes`` rows (m, n, k, l), ``ptrs_abc``
+    rows (A, B, C) device addresses, ``ptrs_sfa_sfb`` rows (SFA, SFB)."""
+    nvfp4_grouped_gemm_config(problem_sizes, ptrs_abc, ptrs_sfa_sfb, num_groups, stream, -1)
+
+
+def nvfp4_grouped_gemm_config(problem_sizes, ptrs_abc, ptrs_sfa_sfb, num_groups=None, stream=None,
+                              tile_config=-1) -> None:
+    lib = load_library()
+    ps, g = _sizes(problem_sizes)
+    g = g if num_groups is None else int(num_groups)
+    rc = lib.nvfp4_grouped_gemm_config(ps, _u64(ptrs_abc, 3), _u64(ptrs_sfa_sfb, 2), g,
+                                       _stream(stream), int(tile_config))
+    if rc != NVFP4_OK:
+        raise Nvfp4Error(rc, "nvfp4_grouped_gemm")
+
+
+def nvfp4_grouped_gemm_validate(problem_sizes, ptrs_abc, ptrs_sfa_sfb, num_groups=None) -> int:
+    lib = load_library()
+    ps, g = _sizes(problem_sizes)
+    g = g if num_groups is None else int(num_groups)
+    return lib.nvfp4_grouped_gemm_validate(ps, _u64(ptrs_abc, 3), _u64(ptrs_sfa_sfb, 2), g)
+
+
+def nvfp4_num_tile_configs() -> int:
+    return load_library().nvfp4_num_tile_configs()
+
+
+def nvfp4_tile_config_info(cfg: int):
+    v = [ctypes.c_int() for _ in range(4)]
+    rc = load_library().nvfp4_tile_config_info(int(cfg), *[ctypes.byref(x) for x in v])
+    if rc != NVFP4_OK:
+        raise Nvfp4Error(rc, "nvfp4_tile_config_info")
+    return dict(bm=v[0].value, bn=v[1].value, bk=v[2].value, threads=v[3].value)
+
+
+def nvfp4_select_tile_config(problem_sizes, num_cus: int, num_groups=None) -> int:
+    ps, g = _sizes(problem_sizes)
+    return load_library().nvfp4_select_tile_config(ps, g if num_groups is None else num_groups, int(num_cus))
+
+
+def nvfp4_launch_geometry(problem_sizes, num_cus: int, cfg: int = -1, num_groups=None):
+    ps, g = _sizes(problem_sizes)
+    tiles, grid = ctypes.c_int64(), ctypes.c_int()
+    rc = load_library().nvfp4_launch_geometry(ps, g if num_groups is None else num_groups, int(num_cus),
+                                              int(cfg), ctypes.byref(tiles), ctypes.byref(grid))
+    if rc < 0:
+        raise Nvfp4Error(rc, "nvfp4_launch_geometry")
+    return dict(config=rc, total_tiles=tiles.value, grid=grid.value)
+
+
+def nvfp4_sf_bytes(rows: int, k: int, l: int = 1) -> int:
+    return int(load_library().nvfp4_sf_bytes(int(rows), int(k), int(l)))
+
+
+def nvfp4_last_hip_error() -> int:
+    return load_library().nvfp4_last_hip_error()
+
+
+def nvfp4_error_string(code: int) -> str:
+    return load_library().nvfp4_error_string(int(code)).decode()

@@ -1,0 +1,71 @@
+"""Device-memory plumbing (PyTorch) for the grouped GEMM: upload seeded byte
+arrays, build the host pointer tables and call the library. No arithmetic."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from ._binding import nvfp4_grouped_gemm_config
+
+FP16_NAN_BITS = 0xFFFF
+
+
+def upload(shapes, groups, device="cuda", c_fill_bits=FP16_NAN_BITS, c_guard=0):
+    """Copy each group's bytes to ``device``; allocate C (pre-filled with
+    ``c_fill_bits``), optionally inside a guard band of ``c_guard`` fp16 elements
+    on each side (kept for canary checks)."""
+    if c_guard % 8:
+        raise ValueError("c_guard must be a multiple of 8 elements (C stays 16-byte aligned)")
+    out = []
+    for (m, n, k, l), g in zip(shapes, groups):
+        d = {}
+        for key in ("a", "b", "sfa", "sfb"):
+            arr = np.ascontiguousarray(g[key]).reshape(-1)
+            t = torch.empty(max(arr.size, 16), dtype=torch.uint8, device=device)
+            if arr.size:
+                t[: arr.size].copy_(torch.from_numpy(arr))
+            d[key] = t
+        numel = l * m * n
+        fill = int(np.array(c_fill_bits, dtype=np.uint16).view(np.int16))
+        store = torch.full((numel + 2 * c_guard + 8,), fill, dtype=torch.int16, device=device)
+        d["c_store"] = store
+        d["c"] = store[c_guard: c_guard + numel]
+        d["c_guard"] = c_guard
+        out.append(d)
+    return out
+
+
+def pointer_tables(dev_groups):
+    abc = [(d["a"].data_ptr(), d["b"].data_ptr(), d["c"].data_ptr()) for d in dev_groups]
+    sf = [(d["sfa"].data_ptr(), d["sfb"].data_ptr()) for d in dev_groups]
+    return abc, sf
+
+
+def run(shapes, dev_groups, stream=None, tile_config=-1):
+    """Enqueue one grouped GEMM on ``stream`` (default: torch's current stream)."""
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    abc, sf = pointer_tables(dev_groups)
+    nvfp4_grouped_gemm_config(shapes, abc, sf, len(shapes), stream, tile_config)
+
+
+def c_as_numpy(shapes, dev_groups):
+    """Copy every C back as numpy float16 [l][m][n]."""
+    res = []
+    for (m, n, k, l), d in zip(shapes, dev_groups):
+        bits = d["c"].cpu().numpy().view(np.uint16)
+        res.append(bits.view(np.float16).reshape(l, m, n))
+    return res
+
+
+def guards_intact(dev_groups, c_fill_bits=FP16_NAN_BITS):
+    """True when the guard bands around every C still hold the fill pattern."""
+    for d in dev_groups:
+        g = d["c_guard"]
+        if g == 0:
+            continue
+        st = d["c_store"].cpu().numpy().view(np.uint16)
+        n = d["c"].numel()
+        if not (np.all(st[:g] == c_fill_bits) and np.all(st[g + n:] == c_fill_bits)):
+            return False
+    return True

@@ -1,0 +1,143 @@
+"""The C-ABI library on the CPU: it loads, exports every declared entry point,
+and its host-side logic (argument validation, tile geometry, sizes) behaves as
+the header states. No compute call is made (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_matmul_amd as mm
+from moe_matmul_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4_grouped_gemm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = mm.load_library()
+    names = declared_functions()
+    assert "nvfp4_grouped_gemm" in names and len(names) >= 8
+    for name in names:
+        assert hasattr(lib, name), name
+    # every exported nvfp4_ symbol of the binary is declared (nothing undocumented)
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", mm.LIB_PATH], capture_output=True, text=True).stdout
+    exported = sorted(set(re.findall(r"\bT (nvfp4_\w+)", out)))
+    assert exported == names
+
+
+def _ptrs(g, base=0x10000):
+    abc = [(base + 0x1000 * i, base + 0x2000 * i + 0x100000, base + 0x3000 * i + 0x200000) for i in range(g)]
+    sf = [(base + 0x4000 * i + 0x300000, base + 0x5000 * i + 0x400000) for i in range(g)]
+    return abc, sf
+
+
+def test_validate_accepts_workloads():
+    for idx in range(5):
+        shapes = synth.workload_shapes(idx)
+        abc, sf = _ptrs(len(shapes))
+        assert mm.nvfp4_grouped_gemm_validate(shapes, abc, sf) == mm.NVFP4_OK
+
+
+@pytest.mark.parametrize("shapes,code", [
+    ([(128, 128, 96, 1)], mm.NVFP4_ERR_INVALID),        # k % 64
+    ([(128, 100, 128, 1)], mm.NVFP4_ERR_INVALID),       # n % 8
+    ([(-1, 128, 128, 1)], mm.NVFP4_ERR_INVALID),
+    ([(128, -8, 128, 1)], mm.NVFP4_ERR_INVALID),
+    ([(128, 128, -64, 1)], mm.NVFP4_ERR_INVALID),
+    ([(128, 128, 128, 0)], mm.NVFP4_ERR_INVALID),       # l >= 1
+    ([(128, 128, 1 << 23, 1)], mm.NVFP4_ERR_INVALID),   # k <= 2^22
+    ([(1 << 20, 128, 4096, 1)], mm.NVFP4_ERR_INVALID),  # A bytes >= 2^31
+])
+def test_validate_rejects_bad_sizes(shapes, code):
+    abc, sf = _ptrs(len(shapes))
+    assert mm.nvfp4_grouped_gemm_validate(shapes, abc, sf) == code
+
+
+def test_validate_group_count_and_nulls():
+    lib = mm.load_library()
+    shapes = [(64, 64, 64, 1)] * 9
+    abc, sf = _ptrs(9)
+    assert mm.nvfp4_grouped_gemm_validate(shapes, abc, sf, 9) == mm.NVFP4_ERR_INVALID
+    assert mm.nvfp4_grouped_gemm_validate(shapes[:1], abc[:1], sf[:1], 0) == mm.NVFP4_ERR_INVALID
+    null = ctypes.POINTER(ctypes.c_int32)()
+    assert lib.nvfp4_grouped_gemm_validate(null, None, None, 1) == mm.NVFP4_ERR_INVALID
+    for col in range(3):
+        abc2 = [list(r) for r in abc[:1]]
+        abc2[0][col] = 0
+        assert mm.nvfp4_grouped_gemm_validate(shapes[:1], abc2, sf[:1]) == mm.NVFP4_ERR_INVALID
+    for col in range(2):
+        sf2 = [list(r) for r in sf[:1]]
+        sf2[0][col] = 0
+        assert mm.nvfp4_grouped_gemm_validate(shapes[:1], abc[:1], sf2) == mm.NVFP4_ERR_INVALID
+
+
+def test_validate_alignment():
+    shapes = [(64, 64, 64, 1)]
+    abc, sf = _ptrs(1)
+    for col in range(3):
+        abc2 = [list(abc[0])]
+        abc2[0][col] += 8
+        assert mm.nvfp4_grouped_gemm_validate(shapes, abc2, sf) == mm.NVFP4_ERR_MISALIGNED
+    for col in range(2):
+        sf2 = [list(sf[0])]
+        sf2[0][col] += 4
+        assert mm.nvfp4_grouped_gemm_validate(shapes, abc, sf2) == mm.NVFP4_ERR_MISALIGNED
+
+
+def test_validate_edge_semantics():
+    abc, sf = _ptrs(3)
+    # empty groups may carry null pointers; k = 0 needs only C
+    assert mm.nvfp4_grouped_gemm_validate([(0, 64, 64, 1), (64, 0, 64, 1), (8, 8, 64, 1)],
+                                          [(0, 0, 0), (0, 0, 0), abc[2]], [(0, 0), (0, 0), sf[2]]) == mm.NVFP4_OK
+    assert mm.nvfp4_grouped_gemm_validate([(8, 8, 0, 1)], [(0, 0, abc[0][2])], [(0, 0)]) == mm.NVFP4_OK
+    assert mm.nvfp4_grouped_gemm_validate([(8, 8, 0, 1)], [(0, 0, 0)], [(0, 0)]) == mm.NVFP4_ERR_INVALID
+
+
+def test_compute_call_validates_before_any_hip_call():
+    # an invalid call must fail in validation (no device needed)
+    with pytest.raises(mm.Nvfp4Error) as e:
+        mm.nvfp4_grouped_gemm([(128, 100, 128, 1)], *_ptrs(1))
+    assert e.value.code == mm.NVFP4_ERR_INVALID
+    with pytest.raises(mm.Nvfp4Error) as e:
+        mm.nvfp4_grouped_gemm_config([(128, 128, 128, 1)], *_ptrs(1), tile_config=99)
+    assert e.value.code in (mm.NVFP4_ERR_CONFIG,)
+
+
+def test_sf_bytes_matches_atom_padding():
+    for rows, k, l in [(1, 64, 1), (128, 256, 1), (129, 64, 2), (300, 7168, 1), (0, 64, 1), (5, 0, 1)]:
+        assert mm.nvfp4_sf_bytes(rows, k, l) == synth.sf_buffer_bytes(rows, k, l)
+    assert mm.nvfp4_sf_bytes(-1, 64, 1) == 0
+
+
+def test_tile_configs_and_geometry():
+    n = mm.nvfp4_num_tile_configs()
+    assert n >= 1
+    for c in range(n):
+        info = mm.nvfp4_tile_config_info(c)
+        assert info["bm"] % 128 == 0 and info["bn"] % 128 == 0 and info["threads"] == 256
+    with pytest.raises(mm.Nvfp4Error):
+        mm.nvfp4_tile_config_info(n)
+    shapes = synth.workload_shapes(2)
+    for c in range(n):
+        info = mm.nvfp4_tile_config_info(c)
+        geo = mm.nvfp4_launch_geometry(shapes, 256, c)
+        expect = sum(-(-m // info["bm"]) * -(-nn // info["bn"]) * l for (m, nn, k, l) in shapes)
+        assert geo["config"] == c and geo["total_tiles"] == expect and geo["grid"] == min(expect, 256)
+    # empty groups own no tiles, wherever they sit
+    geo = mm.nvfp4_launch_geometry([(0, 128, 64, 1), (128, 128, 64, 1), (128, 0, 64, 1)], 256, 0)
+    assert geo["total_tiles"] == 1
+    sel = mm.nvfp4_select_tile_config(synth.workload_shapes(4), 256)
+    assert 0 <= sel < n
+
+
+def test_error_strings():
+    for code in (0, -1, -2, -3, -4, 7):
+        assert isinstance(mm.nvfp4_error_string(code), str)
