@@ -104,7 +104,7 @@ def time_workload(idx, steps, warmup, tile_config=-1, cold=True):
     )
 
 
-def cpu_baseline(idx, max_rows=None):
+def cpu_baseline(idx, max_rows=None, min_seconds=10.0):
     """The CPU oracle, as it stands, on workload ``idx`` (rows capped per group)."""
     from threadpoolctl import threadpool_info
 
@@ -113,18 +113,36 @@ def cpu_baseline(idx, max_rows=None):
 
     shapes, groups = synth.make_workload(idx)
     fl = 0
+    reps = 0
     t0 = time.perf_counter()
-    for (m, n, k, l), g in zip(shapes, groups):
-        rows = m if max_rows is None else min(m, max_rows)
-        O.gemm_group(m, n, k, l, g["a"], g["b"], g["sfa"], g["sfb"], rows=np.arange(rows))
-        fl += 2 * rows * n * k * l
+    # repeat the whole sample until at least min_seconds of CPU work
+    while reps == 0 or time.perf_counter() - t0 < min_seconds:
+        for (m, n, k, l), g in zip(shapes, groups):
+            rows = m if max_rows is None else min(m, max_rows)
+            O.gemm_group(m, n, k, l, g["a"], g["b"], g["sfa"], g["sfb"], rows=np.arange(rows))
+            fl += 2 * rows * n * k * l
+        reps += 1
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     sample = (f"{synth.WORKLOADS[idx]['name']}, " +
               ("all rows" if max_rows is None else f"first {max_rows} rows per group") +
-              f" ({fl / 1e9:.1f} GFLOP of C; float64 dequant + BLAS, C and S)")
+              f", {reps} pass(es), {fl / 1e9:.1f} GFLOP of C in {dt:.1f} s (float64 dequant + BLAS, C and S)")
     return dict(value=fl / dt / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle", sample=sample,
                 seconds=dt, cpu_count=os.cpu_count())
+
+
+def copy_calibration(nbytes=256 << 20, reps=5):
+    """A plain device-to-device copy of known size, for scaling the HBM traffic
+    counters (FETCH_SIZE / WRITE_SIZE) of the GEMM kernel."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.random_(0, 256)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: {reps} copies of {nbytes} bytes")
 
 
 def load_traffic(workload_name):
@@ -153,6 +171,9 @@ def main():
     ap.add_argument("--out", default=None, help="write the per-workload details as JSON here")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=None, help="cap rows per group of the CPU sample")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU work of the baseline leg")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of known size (counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -170,6 +191,8 @@ def main():
     torch.cuda.set_device(0)
     mm.load_library()
 
+    if args.copy_calibration:
+        copy_calibration()
     head = time_workload(args.workload, args.steps, args.warmup, args.tile_config, cold=True)
     hot = time_workload(args.workload, args.steps, args.warmup, args.tile_config, cold=False)
     log(f"[bench] cold {head['tflops']:.1f} TFLOP/s {head['us_median']:.1f} us/call; "
@@ -187,7 +210,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args.workload, args.cpu_rows)
+        cpu = cpu_baseline(args.workload, args.cpu_rows, args.cpu_seconds)
         log(f"[bench] cpu oracle {cpu['value'] * 1e3:.1f} GFLOP/s on {cpu['cores']} threads in {cpu['seconds']:.1f} s")
 
     achieved = head["flops"] / (head["total_ms"] / args.steps / 1e3) / 1e12
