@@ -52,7 +52,7 @@ def percentile(v, p):
     return float(np.percentile(np.asarray(v), p))
 
 
-def time_workload(idx, steps, warmup, tile_config=-1, cold=True):
+def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None):
     import torch
 
     import moe_matmul_amd as mm
@@ -74,10 +74,15 @@ def time_workload(idx, steps, warmup, tile_config=-1, cold=True):
             sets.append(cp)
     stream = torch.cuda.current_stream()
     ptrs = [dev.pointer_tables(s) for s in sets]
+    ws = dev.workspace_for(shapes) if split_mode is not None else None
 
     def call(i):
         abc, sf = ptrs[i % len(ptrs)]
-        mm.nvfp4_grouped_gemm_config(shapes, abc, sf, len(shapes), stream, tile_config)
+        if split_mode is None:
+            mm.nvfp4_grouped_gemm_config(shapes, abc, sf, len(shapes), stream, tile_config)
+        else:
+            mm.nvfp4_grouped_gemm_ex(shapes, abc, sf, len(shapes), ws.data_ptr(), ws.numel(), tile_config,
+                                     split_mode, stream)
 
     for i in range(warmup):
         call(i)
@@ -93,14 +98,15 @@ def time_workload(idx, steps, warmup, tile_config=-1, cold=True):
     wall = time.perf_counter() - t0
     per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]  # ms
     total_ms = evs[0].elapsed_time(evs[steps])
-    geo = mm.nvfp4_launch_geometry(shapes, torch.cuda.get_device_properties(0).multi_processor_count, tile_config)
+    geo = mm.nvfp4_launch_geometry(shapes, torch.cuda.get_device_properties(0).multi_processor_count, tile_config,
+                                   -1 if split_mode is None else split_mode)
     avg_s = total_ms / steps / 1e3
     return dict(
         workload=synth.WORKLOADS[idx]["name"], shapes=[list(s) for s in shapes], flops=flops, bytes=nbytes,
         total_ms=total_ms, wall_s=wall, ms_per_call=total_ms / steps,
         us_median=percentile(per, 50) * 1e3, us_p10=percentile(per, 10) * 1e3, us_p90=percentile(per, 90) * 1e3,
         tflops=flops / avg_s / 1e12, gbs=nbytes / avg_s / 1e9, sets=len(sets), tile_config=geo["config"],
-        tiles=geo["total_tiles"], grid=geo["grid"],
+        tiles=geo["total_tiles"], grid=geo["grid"], split=geo["split"],
     )
 
 
@@ -168,6 +174,8 @@ def main():
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--tile-config", type=int, default=-1)
     ap.add_argument("--all", action="store_true", help="also time every workload (to stderr / --out)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every workload under every tile configuration and split mode (to stderr / --out)")
     ap.add_argument("--out", default=None, help="write the per-workload details as JSON here")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=None, help="cap rows per group of the CPU sample")
@@ -201,12 +209,26 @@ def main():
     if args.all:
         allres = []
         for i in range(5):
-            r = time_workload(i, max(20, args.steps // 2), 5, -1, cold=True)
-            allres.append(r)
-            log(f"[bench] workload {i} {r['workload']}: {r['tflops']:.1f} TFLOP/s, {r['us_median']:.1f} us/call "
-                f"(p10 {r['us_p10']:.1f}, p90 {r['us_p90']:.1f}), {r['gbs']:.0f} GB/s, cfg {r['tile_config']}, "
-                f"{r['tiles']} tiles")
+            for sm in (None, 0, 1):
+                r = time_workload(i, max(20, args.steps // 2), 5, -1, cold=True, split_mode=sm)
+                r["forced_split"] = sm
+                allres.append(r)
+                log(f"[bench] workload {i} {r['workload']} split={'auto' if sm is None else sm}: "
+                    f"{r['tflops']:.1f} TFLOP/s, {r['us_median']:.1f} us/call "
+                    f"(p10 {r['us_p10']:.1f}, p90 {r['us_p90']:.1f}), {r['gbs']:.0f} GB/s, cfg {r['tile_config']}, "
+                    f"split {r['split']}, {r['tiles']} tiles, grid {r['grid']}")
         details["all"] = allres
+
+    if args.sweep:
+        sweep = []
+        for i in range(5):
+            for cfg in range(mm.nvfp4_num_tile_configs()):
+                for sm in (0, 1):
+                    r = time_workload(i, 20, 3, cfg, cold=True, split_mode=sm)
+                    sweep.append(r)
+                    log(f"[sweep] wl{i} cfg{cfg} split{sm}: {r['us_median']:8.1f} us {r['tflops']:7.1f} TFLOP/s "
+                        f"tiles {r['tiles']} grid {r['grid']}")
+        details["sweep"] = sweep
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -235,6 +257,7 @@ def main():
             "operands": "FP4 E2M1 A/B, E4M3 scale per 16 K, fp32 accumulate, fp16 C",
             "mfma": "v_mfma_f32_32x32x16_f16 on exactly dequantised operands",
             "tile_config": head["tile_config"],
+            "stream_k": bool(head["split"]),
             "tiles": head["tiles"],
             "grid": head["grid"],
             "cache": f"cold: {head['sets']} rotating input/output sets",

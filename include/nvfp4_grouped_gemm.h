@@ -26,11 +26,21 @@
  *   SFB same with n in place of m.
  *   C   fp16 [l][m][n], row-major.
  *
- * Ownership and threading: the caller owns every buffer. The library keeps no
- * per-call state and allocates nothing; the host tables are read before the
- * call returns, so they may be reused at once. The only global state is a
- * per-device cache of the compute-unit count. Calls are stream-ordered and
- * asynchronous (they do not synchronise).
+ * Work decomposition: output tiles (one of a few compiled shapes) are spread
+ * over a persistent grid of one workgroup per compute unit, either whole
+ * (workgroup b takes tiles b, b + grid, ...) or stream-K (each workgroup takes
+ * an equal share of all (tile, 128-K stage) units; a tile split between
+ * workgroups is summed, in a fixed order, by the last one to finish). Stream-K
+ * needs a workspace: an arrival counter per tile and two fp32 tile-sized slots
+ * per workgroup.
+ *
+ * Ownership and threading: the caller owns every buffer. Host tables are read
+ * before a call returns. Calls are stream-ordered and asynchronous. The
+ * library's global state is a per-device cache of the compute-unit count and,
+ * for nvfp4_grouped_gemm / nvfp4_grouped_gemm_config only, a stream-K
+ * workspace per (device, stream) that the library allocates with hipMalloc on
+ * first need (grown when a call needs more, kept until the process ends).
+ * nvfp4_grouped_gemm_ex takes a caller workspace and allocates nothing.
  */
 #ifndef NVFP4_GROUPED_GEMM_H
 #define NVFP4_GROUPED_GEMM_H
@@ -49,7 +59,8 @@ extern "C" {
 #define NVFP4_ERR_INVALID (-1)    /* bad group count, size, divisibility or null pointer */
 #define NVFP4_ERR_MISALIGNED (-2) /* a device pointer is not 16-byte aligned */
 #define NVFP4_ERR_HIP (-3)        /* the HIP runtime reported an error; see nvfp4_last_hip_error */
-#define NVFP4_ERR_CONFIG (-4)     /* unknown tile configuration id */
+#define NVFP4_ERR_CONFIG (-4)     /* unknown tile configuration id or split mode */
+#define NVFP4_ERR_WORKSPACE (-5)  /* stream-K requested without a large enough workspace */
 
 /*
  * nvfp4_grouped_gemm - run the grouped GEMM on `stream`.
@@ -69,10 +80,34 @@ extern "C" {
  * Semantics at the edges: a group with m == 0 or n == 0 leaves C untouched;
  * k == 0 writes C = 0 (the empty sum).
  * Returns NVFP4_OK once the kernel is enqueued, NVFP4_ERR_HIP if the launch
- * failed.
+ * (or the first allocation of the stream-K workspace) failed.
  */
 int nvfp4_grouped_gemm(const int32_t* problem_sizes, const uint64_t* ptrs_abc,
                        const uint64_t* ptrs_sfa_sfb, int num_groups, void* stream);
+
+/*
+ * nvfp4_grouped_gemm_ex - as nvfp4_grouped_gemm, with the caller's workspace
+ * and explicit choices; allocates nothing.
+ *   workspace        device buffer (256-byte aligned) or NULL; its first
+ *                    bytes (the per-tile counters) must be zero before the
+ *                    first use, and every completed call leaves them zero.
+ *                    Calls that may overlap in time need distinct workspaces.
+ *   workspace_bytes  its size; see nvfp4_workspace_bytes.
+ *   tile_config      -1 (heuristic) or 0 .. nvfp4_num_tile_configs()-1.
+ *   split_mode       -1 (heuristic), 0 (whole tiles), 1 (stream-K).
+ * With split_mode -1 and no (or too small a) workspace the call uses whole
+ * tiles; split_mode 1 without enough workspace returns NVFP4_ERR_WORKSPACE.
+ */
+int nvfp4_grouped_gemm_ex(const int32_t* problem_sizes, const uint64_t* ptrs_abc,
+                          const uint64_t* ptrs_sfa_sfb, int num_groups, void* workspace,
+                          size_t workspace_bytes, int tile_config, int split_mode, void* stream);
+
+/*
+ * nvfp4_workspace_bytes - workspace that covers every plan the library may
+ * choose for these sizes on `num_cus` compute units (host only, no HIP call);
+ * 0 for invalid sizes.
+ */
+size_t nvfp4_workspace_bytes(const int32_t* problem_sizes, int num_groups, int num_cus);
 
 /*
  * nvfp4_grouped_gemm_config - as nvfp4_grouped_gemm, with the tile
@@ -109,12 +144,14 @@ int nvfp4_tile_config_info(int cfg, int* bm, int* bn, int* bk, int* threads);
 int nvfp4_select_tile_config(const int32_t* problem_sizes, int num_groups, int num_cus);
 
 /*
- * nvfp4_launch_geometry - for configuration `cfg` (-1 = heuristic) and these
- * sizes: total output tiles and the persistent grid size on `num_cus` compute
- * units (host only, no HIP call). Returns the config id used, or an error.
+ * nvfp4_launch_geometry - the plan for configuration `cfg` and split mode
+ * `split` (-1 = heuristic for either) on `num_cus` compute units, assuming a
+ * workspace is available (host only, no HIP call): total output tiles,
+ * persistent grid size, whether stream-K is used and the workspace it needs.
+ * Any output pointer may be NULL. Returns the config id used, or an error.
  */
-int nvfp4_launch_geometry(const int32_t* problem_sizes, int num_groups, int num_cus, int cfg,
-                          int64_t* total_tiles, int* grid);
+int nvfp4_launch_geometry(const int32_t* problem_sizes, int num_groups, int num_cus, int cfg, int split,
+                          int64_t* total_tiles, int* grid, int* split_used, size_t* workspace_bytes);
 
 /* Size in bytes of one tiled scale tensor for `rows` rows and `k` K-elements,
  * l batches: ceil(rows/128)*128 * ceil(k/64)*4 * l. Returns 0 if any is < 0. */

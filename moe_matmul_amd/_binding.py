@@ -16,6 +16,7 @@ NVFP4_ERR_INVALID = -1
 NVFP4_ERR_MISALIGNED = -2
 NVFP4_ERR_HIP = -3
 NVFP4_ERR_CONFIG = -4
+NVFP4_ERR_WORKSPACE = -5
 NVFP4_MAX_GROUPS = 8
 
 _lib = None
@@ -48,7 +49,11 @@ def load_library() -> ctypes.CDLL:
         "nvfp4_num_tile_configs": (ctypes.c_int, []),
         "nvfp4_tile_config_info": (ctypes.c_int, [ctypes.c_int, ip, ip, ip, ip]),
         "nvfp4_select_tile_config": (ctypes.c_int, [i32p, ctypes.c_int, ctypes.c_int]),
-        "nvfp4_launch_geometry": (ctypes.c_int, [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, i64p, ip]),
+        "nvfp4_launch_geometry": (ctypes.c_int, [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                 i64p, ip, ip, ctypes.POINTER(ctypes.c_size_t)]),
+        "nvfp4_grouped_gemm_ex": (ctypes.c_int, [i32p, u64p, u64p, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
+                                                 ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
+        "nvfp4_workspace_bytes": (ctypes.c_size_t, [i32p, ctypes.c_int, ctypes.c_int]),
         "nvfp4_sf_bytes": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int, ctypes.c_int]),
         "nvfp4_last_hip_error": (ctypes.c_int, []),
         "nvfp4_error_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -122,14 +127,33 @@ def nvfp4_select_tile_config(problem_sizes, num_cus: int, num_groups=None) -> in
     return load_library().nvfp4_select_tile_config(ps, g if num_groups is None else num_groups, int(num_cus))
 
 
-def nvfp4_launch_geometry(problem_sizes, num_cus: int, cfg: int = -1, num_groups=None):
+def nvfp4_launch_geometry(problem_sizes, num_cus: int, cfg: int = -1, split: int = -1, num_groups=None):
     ps, g = _sizes(problem_sizes)
-    tiles, grid = ctypes.c_int64(), ctypes.c_int()
+    tiles, grid, used = ctypes.c_int64(), ctypes.c_int(), ctypes.c_int()
+    ws = ctypes.c_size_t()
     rc = load_library().nvfp4_launch_geometry(ps, g if num_groups is None else num_groups, int(num_cus),
-                                              int(cfg), ctypes.byref(tiles), ctypes.byref(grid))
+                                              int(cfg), int(split), ctypes.byref(tiles), ctypes.byref(grid),
+                                              ctypes.byref(used), ctypes.byref(ws))
     if rc < 0:
         raise Nvfp4Error(rc, "nvfp4_launch_geometry")
-    return dict(config=rc, total_tiles=tiles.value, grid=grid.value)
+    return dict(config=rc, total_tiles=tiles.value, grid=grid.value, split=used.value, workspace_bytes=ws.value)
+
+
+def nvfp4_grouped_gemm_ex(problem_sizes, ptrs_abc, ptrs_sfa_sfb, num_groups=None, workspace=0, workspace_bytes=0,
+                          tile_config=-1, split_mode=-1, stream=None) -> None:
+    """Grouped GEMM with a caller workspace (device address) and explicit choices."""
+    lib = load_library()
+    ps, g = _sizes(problem_sizes)
+    g = g if num_groups is None else int(num_groups)
+    rc = lib.nvfp4_grouped_gemm_ex(ps, _u64(ptrs_abc, 3), _u64(ptrs_sfa_sfb, 2), g, ctypes.c_void_p(int(workspace)),
+                                   int(workspace_bytes), int(tile_config), int(split_mode), _stream(stream))
+    if rc != NVFP4_OK:
+        raise Nvfp4Error(rc, "nvfp4_grouped_gemm_ex")
+
+
+def nvfp4_workspace_bytes(problem_sizes, num_cus: int, num_groups=None) -> int:
+    ps, g = _sizes(problem_sizes)
+    return int(load_library().nvfp4_workspace_bytes(ps, g if num_groups is None else num_groups, int(num_cus)))
 
 
 def nvfp4_sf_bytes(rows: int, k: int, l: int = 1) -> int:

@@ -37,8 +37,11 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
+#include <vector>
 
 #include "nvfp4_grouped_gemm.h"
 
@@ -49,6 +52,7 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 template <int N>
 using ScaleVec = uint32_t __attribute__((ext_vector_type(N)));
 
@@ -67,13 +71,18 @@ struct GroupArgs {
   const uint8_t* sfb;
   int32_t m, n, k, l;
   int32_t tiles_m, tiles_n;
-  int32_t pad0, pad1;
+  int32_t nk;  // 128-K stages per tile
+  int32_t pad;
 };
 
 struct KernelArgs {
   GroupArgs g[kMaxGroups];
-  int32_t prefix[kMaxGroups + 1];  // prefix[g] = first tile of group g
+  int32_t tile_prefix[kMaxGroups + 1];  // first tile of group g (tiles numbered group by group)
+  int32_t unit_prefix[kMaxGroups + 1];  // first (tile, stage) unit of group g
   int32_t num_groups;
+  int32_t split;        // 0: whole tiles strided over the grid; 1: stream-K over units
+  int32_t grid;         // workgroups of the main kernel
+  float* partials;      // split: two fp32 tile-sized slots per workgroup
 };
 
 // 8 FP4 codes (one dword) -> 8 f16 values a * s, exact.
@@ -105,11 +114,21 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t num_bytes) 
   return i32x4{(int32_t)(uint32_t)b, (int32_t)((uint32_t)(b >> 32) & 0xFFFFu), n, kBufferWord3};
 }
 
+// The same resource as the builtin buffer-access type (for compiler-issued
+// buffer loads and stores).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_buffer(const void* base, int64_t num_bytes) {
+  const int n = num_bytes <= 0 ? 0 : (num_bytes >= 0x7fffffff ? 0x7fffffff : (int)num_bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kBufferWord3);
+}
+
 // 16 bytes per lane from global (buffer, bounds-checked) straight into LDS at
 // lds_block + 16 * lane (M0 holds the wave's LDS base). Issued as inline asm so
 // the compiler does not treat it as an LDS write it must wait for: the kernel
 // tracks these loads itself with exact vmcnt waits.
 __device__ __forceinline__ void load_lds16(i32x4 rsrc, uint8_t* lds_block, int voffset) {
+  // every operand but the offset is wave-uniform; say so, so they stay in SGPRs
+  rsrc = i32x4{__builtin_amdgcn_readfirstlane(rsrc[0]), __builtin_amdgcn_readfirstlane(rsrc[1]),
+               __builtin_amdgcn_readfirstlane(rsrc[2]), __builtin_amdgcn_readfirstlane(rsrc[3])};
   const uint32_t lds_addr = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds_block));
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(lds_addr), "v"(voffset), "s"(rsrc) : "memory", "m0");
@@ -146,6 +165,22 @@ struct TileCtx {
   int M, N, kbytes, nk, row0, col0;
 };
 
+// A run of 128-K stages [s0, s1) of one tile, processed by one workgroup.
+struct Segment {
+  int tile, s0, s1;
+  int64_t u;  // stream-K: first work unit of the segment
+  bool valid;
+};
+
+__device__ __forceinline__ int search_prefix(const int32_t* prefix, int num_groups, int64_t x) {
+  int lo = 0, hi = num_groups - 1;  // last group whose prefix entry is <= x
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (prefix[mid] <= x) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
 template <int BM, int BN, int WM, int WN, int NS>
 struct GemmKernel {
   static constexpr int MB = WM / 32;
@@ -157,6 +192,7 @@ struct GemmKernel {
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SF_ATOMS * 1024;
   static constexpr int A_INSTR = A_BYTES / 1024 / 4;  // 1 KiB direct loads per wave per stage
   static constexpr int B_INSTR = B_BYTES / 1024 / 4;
+  static constexpr int TILE_FLOATS = BM * BN;
   static_assert((BM / WM) * (BN / WN) == kThreads / 64, "four waves per workgroup");
   static_assert(WM <= 128 && WN <= 128 && 128 % WM == 0 && 128 % WN == 0, "wave tile inside one scale atom");
   static_assert(A_INSTR >= 1 && B_INSTR >= 1 && SF_ATOMS <= 4, "tile shape");
@@ -182,20 +218,86 @@ struct GemmKernel {
     f16x8 b[NB];
   };
 
+  const KernelArgs& args;
   uint8_t* smem;
   int wave, wm, wn, h, lr, lane;
 
-  __device__ __forceinline__ TileCtx setup(const KernelArgs& args, int tile) const {
-    int lo = 0, hi = args.num_groups - 1;
-    while (lo < hi) {  // group of the tile: binary search over the tile prefix sum
-      const int mid = (lo + hi + 1) >> 1;
-      if (args.prefix[mid] <= tile) lo = mid; else hi = mid - 1;
+  __device__ GemmKernel(const KernelArgs& a, uint8_t* sm) : args(a), smem(sm) {
+    const int tid = threadIdx.x;
+    lane = tid & 63;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    wm = wave / WAVES_N;
+    wn = wave % WAVES_N;
+    h = lane >> 5;
+    lr = lane & 31;
+  }
+
+  // ---------------- work decomposition ----------------
+  // Tiles are numbered group by group, M-fastest inside a group (the raster of
+  // the persistent scheduler in submission 506336). A unit is one 128-K stage of
+  // one tile; units are numbered tile by tile.
+  __device__ __forceinline__ int group_of_tile(int tile) const {
+    return search_prefix(args.tile_prefix, args.num_groups, tile);
+  }
+  __device__ __forceinline__ int total_tiles() const { return args.tile_prefix[args.num_groups]; }
+  __device__ __forceinline__ int64_t total_units() const { return args.unit_prefix[args.num_groups]; }
+  __device__ __forceinline__ int64_t unit_begin(int wg) const { return (int64_t)wg * total_units() / args.grid; }
+  // the workgroup whose unit range holds unit u
+  __device__ __forceinline__ int owner_of_unit(int64_t u) const {
+    return (int)(((u + 1) * (int64_t)args.grid - 1) / total_units());
+  }
+  __device__ __forceinline__ int64_t first_unit_of_tile(int tile) const {
+    const int g = group_of_tile(tile);
+    return args.unit_prefix[g] + (int64_t)(tile - args.tile_prefix[g]) * args.g[g].nk;
+  }
+  __device__ __forceinline__ int tile_of_unit(int64_t u, int* stage) const {
+    const int g = search_prefix(args.unit_prefix, args.num_groups, u);
+    const int nk = args.g[g].nk;
+    const int local = (int)(u - args.unit_prefix[g]);
+    *stage = local % nk;
+    return args.tile_prefix[g] + local / nk;
+  }
+
+  __device__ __forceinline__ void locate(Segment& s, int64_t u, int64_t u_end) const {
+    s.u = u;
+    s.valid = u < u_end;
+    if (!s.valid) return;
+    int stage;
+    s.tile = tile_of_unit(u, &stage);
+    const int nk = args.g[group_of_tile(s.tile)].nk;
+    s.s0 = stage;
+    s.s1 = (int)min((int64_t)nk, stage + (u_end - u));
+  }
+
+  __device__ __forceinline__ void first_segment(Segment& s) const {
+    if (args.split) {
+      locate(s, unit_begin(blockIdx.x), unit_begin(blockIdx.x + 1));
+    } else {
+      s.tile = blockIdx.x;
+      s.valid = s.tile < total_tiles();
+      s.s0 = 0;
+      s.s1 = s.valid ? args.g[group_of_tile(s.tile)].nk : 0;
     }
-    const GroupArgs& G = args.g[lo];
+  }
+
+  __device__ __forceinline__ void next_segment(Segment& s) const {
+    if (args.split) {
+      locate(s, s.u + (s.s1 - s.s0), unit_begin(blockIdx.x + 1));
+    } else {
+      s.tile += args.grid;
+      s.valid = s.tile < total_tiles();
+      s.s0 = 0;
+      s.s1 = s.valid ? args.g[group_of_tile(s.tile)].nk : 0;
+    }
+  }
+
+  __device__ __forceinline__ TileCtx setup(int tile) const {
+    const int gi = group_of_tile(tile);
+    const GroupArgs& G = args.g[gi];
     const int M = G.m, N = G.n, K = G.k;
     const int tiles_m = G.tiles_m;
     const int per_l = tiles_m * G.tiles_n;
-    const int rest = tile - args.prefix[lo];
+    const int rest = tile - args.tile_prefix[gi];
     const int li = rest / per_l;
     const int r2 = rest - li * per_l;
     const int tm = r2 % tiles_m;  // M-fastest raster inside the group
@@ -208,7 +310,7 @@ struct GemmKernel {
     t.M = M;
     t.N = N;
     t.kbytes = kbytes;
-    t.nk = (K + kBK - 1) / kBK;
+    t.nk = G.nk;
     t.row0 = tm * BM;
     t.col0 = tn * BN;
     t.a_tile = G.a + ((size_t)li * M + (size_t)tm * BM) * kbytes;
@@ -230,6 +332,7 @@ struct GemmKernel {
     return t;
   }
 
+  // ---------------- operand staging ----------------
   // Direct loads of stage kt (A, B and the scale atoms) into LDS buffer buf.
   __device__ __forceinline__ void issue_stage(const TileCtx& t, int kt, int buf) const {
     uint8_t* st = smem + buf * STAGE_BYTES;
@@ -253,6 +356,51 @@ struct GemmKernel {
     }
   }
 
+  // The loader walks the workgroup's segments ahead of the compute. Global stage
+  // X (counted over all segments) lives in LDS buffer X % NS.
+  struct Loader {
+    Segment seg;
+    TileCtx ctx;
+    int stage;   // next stage of seg to issue
+    int issued;  // stages issued so far
+  };
+
+  __device__ __forceinline__ void loader_skip_empty(Loader& ld) const {
+    while (ld.seg.valid && ld.seg.s0 == ld.seg.s1) next_segment(ld.seg);  // k = 0 tiles load nothing
+    if (ld.seg.valid) {
+      ld.ctx = setup(ld.seg.tile);
+      ld.stage = ld.seg.s0;
+    }
+  }
+
+  __device__ __forceinline__ void loader_init(Loader& ld) const {
+    first_segment(ld.seg);
+    ld.issued = 0;
+    loader_skip_empty(ld);
+  }
+
+  __device__ __forceinline__ void issue_next(Loader& ld) const {
+    issue_stage(ld.ctx, ld.stage, ld.issued % NS);
+    ++ld.issued;
+    if (++ld.stage == ld.seg.s1) {
+      next_segment(ld.seg);
+      loader_skip_empty(ld);
+    }
+  }
+
+  // Wait until at most `stages` stages of this wave's loads are outstanding.
+  __device__ __forceinline__ void wait_stages(int stages) const {
+    const int n = stages * (wave < SF_ATOMS ? L1 : L0);
+    switch (n) {
+      case L0: wait_vmem<L0>(); break;
+      case L1: wait_vmem<L1>(); break;
+      case 2 * L0: wait_vmem<2 * L0>(); break;
+      case 2 * L1: wait_vmem<2 * L1>(); break;
+      default: wait_vmem<0>(); break;
+    }
+  }
+
+  // ---------------- dequantisation and MFMA ----------------
   // ds_reads of one half stage (kk) from LDS buffer buf.
   __device__ __forceinline__ void read_half(Raw& r, int buf, int kk) const {
     const uint8_t* As = smem + buf * STAGE_BYTES;
@@ -302,7 +450,7 @@ struct GemmKernel {
 
   // One substep, in a scheduling region of its own: the MFMAs of `use`
   // interleaved with the dequantisation of the next substep into `fill`
-  // (8 VALU per pair of fragments: VALU_PER_MFMA = 4 for 128x128 wave tiles).
+  // (8 VALU per pair of fragments: 4 VALU per MFMA for 128x128 wave tiles).
   // With CONVERT, the next half's scales are converted here as well.
   template <int NEXT_S, bool CONVERT>
   __device__ __forceinline__ void step(f32x16 (&acc)[MB][NB], const Frags& use, Frags& fill, const Raw& src,
@@ -320,49 +468,21 @@ struct GemmKernel {
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // ---- the stage stream ----
-  // The stages of a workgroup's tiles form one sequence; global stage X lives in
-  // LDS buffer X % NS. Loads run up to NS stages ahead and may run into the next
-  // tile (never further). `issued` is the next global stage to issue.
-  struct Stream {
-    int issued;  // next global stage to issue
-    int g0;      // first global stage of the current tile
-    int end;     // one past the last issuable stage (end of the next tile)
-  };
-
-  __device__ __forceinline__ void issue_global(Stream& q, const TileCtx& t, const TileCtx& tn) const {
-    const int x = q.issued++;
-    if (x < q.g0 + t.nk) issue_stage(t, x - q.g0, x % NS);
-    else issue_stage(tn, x - q.g0 - t.nk, x % NS);
-  }
-
-  // Wait until at most `stages` stages of this wave's loads are outstanding.
-  __device__ __forceinline__ void wait_stages(int stages) const {
-    const int n = stages * (wave < SF_ATOMS ? L1 : L0);
-    switch (n) {
-      case L0: wait_vmem<L0>(); break;
-      case L1: wait_vmem<L1>(); break;
-      case 2 * L0: wait_vmem<2 * L0>(); break;
-      case 2 * L1: wait_vmem<2 * L1>(); break;
-      default: wait_vmem<0>(); break;
-    }
-  }
-
-  // One tile. On entry the stream holds this tile's first stages (issued earlier).
-  __device__ __forceinline__ void mainloop(f32x16 (&acc)[MB][NB], const TileCtx& t, const TileCtx& tn,
-                                           Stream& q) const {
+  // n stages of one segment, whose first stage is global stage g0. On entry
+  // the loader has issued at least stage g0.
+  __device__ __forceinline__ void mainloop(f32x16 (&acc)[MB][NB], int n, int g0, Loader& ld) const {
     Raw r0, r1;
     Scales s0, s1;
     Frags f0, f1;
-    wait_vmem_all();  // stage g0 landed (and the last tile's C stores are done)
+    wait_vmem_all();  // stage g0 landed (and earlier C or partial stores are done)
     block_sync();
     // top up: every buffer of a stage before g0 is free now
-    while (q.issued < q.end && q.issued < q.g0 + NS) issue_global(q, t, tn);
-    read_half(r0, q.g0 % NS, 0);
+    while (ld.seg.valid && ld.issued < g0 + NS) issue_next(ld);
+    read_half(r0, g0 % NS, 0);
     convert_scales(s0, r0);
     dequant<0>(f0, r0, s0);
-    for (int kt = 0; kt < t.nk; ++kt) {
-      const int g = q.g0 + kt;
+    for (int kt = 0; kt < n; ++kt) {
+      const int g = g0 + kt;
       // ---- first half (K 0..63 of the stage): raw data in r0 ----
       read_half(r1, g % NS, 1);
       __builtin_amdgcn_sched_group_barrier(kSchedDSRead, MB + NB + 2, 0);
@@ -373,12 +493,12 @@ struct GemmKernel {
       // ---- second half: raw data in r1. Stage g+1 must have landed before its
       // first half is read; every wave is done with stage g's buffer here, so
       // stage g + NS can take it.
-      if (kt + 1 < t.nk) {
-        const int after = q.issued - (g + 2);  // stages issued after g+1
+      if (kt + 1 < n) {
+        const int after = ld.issued - (g + 2);  // stages issued after g+1
         wait_stages(after < 0 ? 0 : after);
       }
       block_sync();
-      if (q.issued < q.end && q.issued <= g + NS) issue_global(q, t, tn);
+      if (ld.seg.valid && ld.issued <= g + NS) issue_next(ld);
       read_half(r0, (g + 1) % NS, 0);  // unused after the last stage
       __builtin_amdgcn_sched_group_barrier(kSchedDSRead, MB + NB + 2, 0);
       step<1, false>(acc, f0, f1, r1, s1);
@@ -388,6 +508,7 @@ struct GemmKernel {
     }
   }
 
+  // ---------------- output ----------------
   // fp32 -> fp16 (RNE), 8-byte stores masked to m and n.
   __device__ __forceinline__ void epilogue(const f32x16 (&acc)[MB][NB], const TileCtx& t) const {
     const int row0 = t.row0 + wm * WM;
@@ -412,6 +533,70 @@ struct GemmKernel {
       }
     }
   }
+
+  // Stream-K partials. Workgroup wg owns two fp32 tile-sized slots: slot 0 for
+  // its first segment, slot 1 for its last. Each lane's 16 floats of block
+  // (i, j) are four 16-byte words at
+  // ((((wave * MB + i) * NB + j) * 4 + q) * 64 + lane) * 16 bytes of the slot.
+  __device__ __forceinline__ static int partial_off(int wave_, int i, int j, int q, int lane_) {
+    return ((((wave_ * MB + i) * NB + j) * 4 + q) * 64 + lane_) * 16;
+  }
+
+  // This workgroup computed stages [s0, s1) of a tile, not all of it: store the
+  // fp32 partial sum; the reduction kernel adds the partials up.
+  __device__ __forceinline__ void write_partial(const f32x16 (&acc)[MB][NB], bool first_seg) const {
+    uint8_t* slot = reinterpret_cast<uint8_t*>(args.partials) +
+                    ((size_t)blockIdx.x * 2 + (first_seg ? 0 : 1)) * TILE_FLOATS * 4;
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          *reinterpret_cast<f32x4*>(slot + partial_off(wave, i, j, q, lane)) = v;
+        }
+  }
+
+  // Stream-K leaves the tiles of k = 0 groups (no units) to a strided pass.
+  __device__ __forceinline__ void zero_k_tiles() const {
+    f32x16 zero[MB][NB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) zero[i][j] = f32x16{};
+    for (int gi = 0; gi < args.num_groups; ++gi) {
+      if (args.g[gi].nk != 0) continue;
+      for (int tile = args.tile_prefix[gi] + blockIdx.x; tile < args.tile_prefix[gi + 1]; tile += gridDim.x)
+        epilogue(zero, setup(tile));
+    }
+  }
+
+  __device__ __forceinline__ void run() const {
+    Loader ld;
+    loader_init(ld);
+    while (ld.seg.valid && ld.issued < NS) issue_next(ld);  // every buffer is free
+    Segment seg;
+    first_segment(seg);
+    bool first_seg = true;
+    int g0 = 0;
+    while (seg.valid) {
+      const TileCtx t = setup(seg.tile);
+      const int n = seg.s1 - seg.s0;
+      f32x16 acc[MB][NB];
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
+      if (n > 0) mainloop(acc, n, g0, ld);
+      if (seg.s0 == 0 && seg.s1 == t.nk) epilogue(acc, t);
+      else write_partial(acc, first_seg);
+      g0 += n;
+      first_seg = false;
+      next_segment(seg);
+    }
+    if (args.split) zero_k_tiles();
+  }
 };
 
 // Stage layout in LDS (bytes): [A: BM rows x 64][B: BN rows x 64]
@@ -421,63 +606,105 @@ template <int BM, int BN, int WM, int WN, int NS>
 __global__ __launch_bounds__(kThreads, 1) void nvfp4_grouped_gemm_kernel(KernelArgs args) {
   using K = GemmKernel<BM, BN, WM, WN, NS>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * K::STAGE_BYTES];
-  K k;
-  k.smem = smem;
-  const int tid = threadIdx.x;
-  k.lane = tid & 63;
-  k.wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  k.wm = k.wave / K::WAVES_N;
-  k.wn = k.wave % K::WAVES_N;
-  k.h = k.lane >> 5;
-  k.lr = k.lane & 31;
-  const int total = args.prefix[args.num_groups];
+  const K k(args, smem);
+  k.run();
+}
 
-  int tile = blockIdx.x;
-  if (tile >= total) return;
-  TileCtx t = k.setup(args, tile);
-  int next = tile + gridDim.x;
-  TileCtx tn = next < total ? k.setup(args, next) : t;
-  typename K::Stream q;
-  q.issued = 0;
-  q.g0 = 0;
-  q.end = t.nk + (next < total ? tn.nk : 0);
-  while (q.issued < q.end && q.issued < NS) k.issue_global(q, t, tn);  // all buffers are free
-  while (true) {
-    f32x16 acc[K::MB][K::NB];
+// Stream-K reduction. Every split tile contains the start of some workgroup's
+// unit range; the first such boundary inside the tile (workgroup c_first + 1)
+// names it. Workgroup (boundary b, chunk x) reduces 16 KiB of the partial
+// layout of that tile: the partials of its contributors are added in
+// contributor order (so the result does not depend on timing), converted to
+// fp16 (RNE) and stored, masked to m and n. Loads of up to four contributors
+// are in flight before they are folded.
+constexpr int kReduceWordsPerThread = 4;
+constexpr int kReduceChunkWords = kThreads * kReduceWordsPerThread;
+
+template <int BM, int BN, int WM, int WN, int NS>
+__global__ __launch_bounds__(kThreads) void nvfp4_streamk_reduce_kernel(KernelArgs args) {
+  using K = GemmKernel<BM, BN, WM, WN, NS>;
+  constexpr int WORDS = K::TILE_FLOATS / 4;
+  constexpr int CHUNKS = WORDS / kReduceChunkWords;
+  static_assert(WORDS % kReduceChunkWords == 0, "chunking");
+  const K k(args, nullptr);
+  const int boundary = 1 + (int)(blockIdx.x / CHUNKS);  // workgroup whose range starts inside the tile
+  const int chunk = (int)(blockIdx.x % CHUNKS);
+  const int64_t ub = k.unit_begin(boundary);
+  int stage;
+  const int tile = k.tile_of_unit(ub, &stage);
+  if (stage == 0) return;  // the boundary falls between tiles: nothing split here
+  const int64_t u_first = ub - stage;
+  const int nk = args.g[k.group_of_tile(tile)].nk;
+  const int c_first = k.owner_of_unit(u_first);
+  const int c_last = k.owner_of_unit(u_first + nk - 1);
+  if (boundary != c_first + 1) return;  // another boundary of this tile does the work
+  const TileCtx t = k.setup(tile);
+  const uint8_t* parts = reinterpret_cast<const uint8_t*>(args.partials);
+  f32x4 sum[kReduceWordsPerThread];
+  for (int c0 = c_first; c0 <= c_last; c0 += 4) {
+    f32x4 v[4][kReduceWordsPerThread];
 #pragma unroll
-    for (int i = 0; i < K::MB; ++i)
+    for (int d = 0; d < 4; ++d) {
+      const int c = c0 + d;
+      if (c > c_last) break;
+      const int slot = k.tile_of_unit(k.unit_begin(c), &stage) == tile ? 0 : 1;
+      const uint8_t* base = parts + ((size_t)c * 2 + slot) * K::TILE_FLOATS * 4;
 #pragma unroll
-      for (int j = 0; j < K::NB; ++j) acc[i][j] = f32x16{};
-    if (t.nk > 0) k.mainloop(acc, t, tn, q);
-    k.epilogue(acc, t);
-    if (next >= total) break;
-    // advance: the next tile becomes current, the one after it joins the stream
-    q.g0 += t.nk;
-    tile = next;
-    t = tn;
-    next = tile + gridDim.x;
-    if (next < total) tn = k.setup(args, next);
-    q.end = q.g0 + t.nk + (next < total ? tn.nk : 0);
+      for (int x = 0; x < kReduceWordsPerThread; ++x) {
+        const int w = chunk * kReduceChunkWords + x * kThreads + (int)threadIdx.x;
+        v[d][x] = *reinterpret_cast<const f32x4*>(base + (size_t)w * 16);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      if (c0 + d > c_last) break;
+#pragma unroll
+      for (int x = 0; x < kReduceWordsPerThread; ++x) sum[x] = (c0 + d == c_first) ? v[d][x] : sum[x] + v[d][x];
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < kReduceWordsPerThread; ++x) {
+    const int w = chunk * kReduceChunkWords + x * kThreads + (int)threadIdx.x;
+    // word w of the layout belongs to (wave, i, j, q, lane)
+    const int ln = w & 63;
+    int rest = w >> 6;
+    const int q = rest & 3;
+    rest >>= 2;
+    const int j = rest % K::NB;
+    rest /= K::NB;
+    const int i = rest % K::MB;
+    const int wv = rest / K::MB;
+    const int row = t.row0 + (wv / K::WAVES_N) * WM + i * 32 + (ln & 31);
+    const int col = t.col0 + (wv % K::WAVES_N) * WN + j * 32 + q * 8 + (ln >> 5) * 4;
+    if (row < t.M && col < t.N) {
+      const f16x4 o = {(_Float16)sum[x][0], (_Float16)sum[x][1], (_Float16)sum[x][2], (_Float16)sum[x][3]};
+      *reinterpret_cast<f16x4*>(t.c + (size_t)row * t.N + col) = o;
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Tile configurations
+// Host side: tile configurations, planning, workspace
 // ---------------------------------------------------------------------------
 
 struct TileConfig {
   int bm, bn, wm, wn;
   void (*kernel)(KernelArgs);
+  void (*reduce)(KernelArgs);
 };
 
 constexpr int kStages = 4;  // LDS pipeline depth (4 x 36 KiB for 256x256 tiles)
 
+#define NVFP4_TILE_CONFIG(bm, bn, wm, wn)                                                       \
+  { bm, bn, wm, wn, nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, kStages>,                     \
+    nvfp4_streamk_reduce_kernel<bm, bn, wm, wn, kStages> }
 const TileConfig kConfigs[] = {
-    {256, 256, 128, 128, nvfp4_grouped_gemm_kernel<256, 256, 128, 128, kStages>},
-    {128, 256, 64, 128, nvfp4_grouped_gemm_kernel<128, 256, 64, 128, kStages>},
-    {256, 128, 128, 64, nvfp4_grouped_gemm_kernel<256, 128, 128, 64, kStages>},
-    {128, 128, 64, 64, nvfp4_grouped_gemm_kernel<128, 128, 64, 64, kStages>},
+    NVFP4_TILE_CONFIG(256, 256, 128, 128),
+    NVFP4_TILE_CONFIG(128, 256, 64, 128),
+    NVFP4_TILE_CONFIG(256, 128, 128, 64),
+    NVFP4_TILE_CONFIG(128, 128, 64, 64),
 };
+#undef NVFP4_TILE_CONFIG
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
 thread_local int t_last_hip_error = 0;
@@ -502,53 +729,201 @@ int device_cu_count(int* out) {
 
 int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-int64_t tiles_of(const int32_t* ps, int g, int cfg) {
+// How one call is carried out.
+struct Plan {
+  int cfg;        // tile configuration
+  int split;      // 0: whole tiles strided over the grid, 1: stream-K
+  int grid;       // persistent workgroups
+  int64_t tiles;  // output tiles
+  int64_t units;  // (tile, 128-K stage) units
+  size_t ws_bytes;  // workspace the plan needs (0 without stream-K)
+  double cost;    // modelled makespan
+};
+
+int64_t group_tiles(const int32_t* ps, int g, int cfg) {
   const int32_t m = ps[4 * g + 0], n = ps[4 * g + 1], l = ps[4 * g + 3];
   if (m == 0 || n == 0) return 0;
   return ceil_div64(m, kConfigs[cfg].bm) * ceil_div64(n, kConfigs[cfg].bn) * l;
 }
 
-// Makespan estimate (in units of 128x128x64 MFMA work) of strided assignment of
-// the tiles to `slots` persistent workgroups, plus a per-tile overhead and a
-// penalty for the smaller wave tiles' extra dequantisation work.
-double estimate_cost(const int32_t* ps, int G, int slots, int cfg) {
-  const TileConfig& tc = kConfigs[cfg];
-  const double unit = (double)tc.bm * tc.bn / (128.0 * 128.0);
-  // dequant work per MFMA grows with 1/wm + 1/wn; 128x128 wave tiles are the reference
-  const double eff = 1.0 + 0.35 * ((128.0 / tc.wm + 128.0 / tc.wn) / 2.0 - 1.0);
-  double load[1024];
-  const int ns = slots < 1024 ? slots : 1024;
-  for (int s = 0; s < ns; ++s) load[s] = 0.0;
-  int64_t t = 0;
-  for (int g = 0; g < G; ++g) {
-    const int64_t nt = tiles_of(ps, g, cfg);
-    const double work = unit * eff * (ps[4 * g + 2] / 64.0 + 4.0);
-    for (int64_t i = 0; i < nt; ++i, ++t) load[t % ns] += work;
-  }
-  double mx = 0.0;
-  for (int s = 0; s < ns; ++s) mx = load[s] > mx ? load[s] : mx;
-  return mx;
+int group_stages(const int32_t* ps, int g) { return (int)ceil_div64(ps[4 * g + 2], kBK); }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t workspace_bytes_for(int cfg, int grid) {
+  return (size_t)grid * 2 * kConfigs[cfg].bm * kConfigs[cfg].bn * 4;
 }
 
-int select_config(const int32_t* ps, int G, int cus) {
-  int best = 0;
-  double best_cost = 0.0;
-  for (int c = 0; c < kNumConfigs; ++c) {
-    const double cost = estimate_cost(ps, G, cus, c);
-    if (c == 0 || cost < best_cost) { best = c; best_cost = cost; }
+// Cost model, in units of one 128x128 tile-stage of MFMA work. Smaller wave
+// tiles dequantise more per MFMA; a tile costs a fixed prologue/epilogue on top
+// of its stages; a stream-K fixup costs a partial write plus, for the last
+// arriver, the reads of the other partials.
+double tile_unit(int cfg) {
+  const TileConfig& tc = kConfigs[cfg];
+  const double size = (double)tc.bm * tc.bn / (128.0 * 128.0);
+  const double eff = 1.0 + 0.35 * ((128.0 / tc.wm + 128.0 / tc.wn) / 2.0 - 1.0);
+  return size * eff;
+}
+
+Plan plan_for(const int32_t* ps, int G, int cus, int cfg, int split) {
+  Plan p{};
+  p.cfg = cfg;
+  p.split = split;
+  const double unit = tile_unit(cfg);
+  const double tile_overhead = 1.5;  // stages' worth of epilogue and pipeline fill per tile
+  int64_t tiles = 0, units = 0;
+  for (int g = 0; g < G; ++g) {
+    tiles += group_tiles(ps, g, cfg);
+    units += group_tiles(ps, g, cfg) * group_stages(ps, g);
   }
-  return best;
+  p.tiles = tiles;
+  p.units = units;
+  if (!split) {
+    p.grid = (int)(tiles < cus ? tiles : cus);
+    // strided assignment of whole tiles
+    static thread_local double load[1024];
+    const int ns = p.grid < 1024 ? (p.grid > 0 ? p.grid : 1) : 1024;
+    for (int s = 0; s < ns; ++s) load[s] = 0.0;
+    int64_t t = 0;
+    for (int g = 0; g < G; ++g) {
+      const int64_t nt = group_tiles(ps, g, cfg);
+      const double work = unit * (group_stages(ps, g) + tile_overhead);
+      for (int64_t i = 0; i < nt; ++i, ++t) load[t % ns] += work;
+    }
+    double mx = 0.0;
+    for (int s = 0; s < ns; ++s) mx = load[s] > mx ? load[s] : mx;
+    p.cost = mx;
+    p.ws_bytes = 0;
+  } else {
+    p.grid = (int)(units < cus ? units : cus);
+    const double per = p.grid > 0 ? (double)units / p.grid : 0.0;
+    // a workgroup's range touches about per/stages + 1 tiles, two of them split
+    double avg_stages = 0.0;
+    for (int g = 0; g < G; ++g) avg_stages += (double)group_tiles(ps, g, cfg) * group_stages(ps, g);
+    avg_stages = tiles > 0 ? avg_stages / tiles : 1.0;
+    const double segments = per / (avg_stages > 0 ? avg_stages : 1.0) + 1.0;
+    const double fixup = 2.0;          // partial write, in stages
+    const double reduce_kernel = 12.0;  // the second kernel and the partial traffic (measured)
+    p.cost = unit * (std::ceil(per) + tile_overhead * segments + fixup) + reduce_kernel;
+    p.ws_bytes = workspace_bytes_for(cfg, p.grid);
+  }
+  return p;
+}
+
+// Picks the cheapest (config, mode): the best whole-tile plan, unless the best
+// stream-K plan is modelled at least 15% cheaper (measured on the workloads:
+// stream-K only pays when whole tiles would leave most compute units idle for
+// long, e.g. few tiles with a long K). Forced values are honoured.
+Plan choose_plan(const int32_t* ps, int G, int cus, int force_cfg, int force_split, bool split_allowed) {
+  Plan best[2] = {};
+  bool have[2] = {false, false};
+  for (int c = 0; c < kNumConfigs; ++c) {
+    if (force_cfg >= 0 && c != force_cfg) continue;
+    for (int sp = 0; sp < 2; ++sp) {
+      if ((force_split >= 0 && sp != force_split) || (sp == 1 && !split_allowed)) continue;
+      const Plan p = plan_for(ps, G, cus, c, sp);
+      if (sp == 1 && p.units == 0) continue;  // nothing to split (all k = 0)
+      if (!have[sp] || p.cost < best[sp].cost) {
+        best[sp] = p;
+        have[sp] = true;
+      }
+    }
+  }
+  if (have[1] && (!have[0] || best[1].cost < 0.85 * best[0].cost)) return best[1];
+  if (have[0]) return best[0];
+  return plan_for(ps, G, cus, force_cfg >= 0 ? force_cfg : 0, 0);
 }
 
 bool aligned16(uint64_t p) { return (p & 15u) == 0; }
 
-}  // namespace
+// Library-owned stream-K workspaces, one per (device, stream), grown on demand
+// and kept until the process ends.
+struct Workspace {
+  int dev;
+  void* stream;
+  void* ptr;
+  size_t bytes;
+};
+std::mutex g_ws_mutex;
+std::vector<Workspace> g_ws;
 
-extern "C" {
+int internal_workspace(void* stream, size_t need, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) { t_last_hip_error = (int)e; return NVFP4_ERR_HIP; }
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  for (Workspace& w : g_ws) {
+    if (w.dev != dev || w.stream != stream) continue;
+    if (w.bytes >= need) { *out = w.ptr; return NVFP4_OK; }
+    // grow: the old buffer may still be in use by earlier calls on this stream
+    e = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
+    if (e == hipSuccess) e = hipFree(w.ptr);
+    if (e != hipSuccess) { t_last_hip_error = (int)e; return NVFP4_ERR_HIP; }
+    w.ptr = nullptr;
+    w.bytes = 0;
+    e = hipMalloc(&w.ptr, need);
+    if (e != hipSuccess) { t_last_hip_error = (int)e; return NVFP4_ERR_HIP; }
+    w.bytes = need;
+    *out = w.ptr;
+    return NVFP4_OK;
+  }
+  void* ptr = nullptr;
+  e = hipMalloc(&ptr, need);
+  if (e != hipSuccess) { t_last_hip_error = (int)e; return NVFP4_ERR_HIP; }
+  g_ws.push_back(Workspace{dev, stream, ptr, need});
+  *out = ptr;
+  return NVFP4_OK;
+}
 
-int nvfp4_grouped_gemm_validate(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G) {
-  if (G < 1 || G > kMaxGroups || ps == nullptr || abc == nullptr || sf == nullptr) return NVFP4_ERR_INVALID;
-  int64_t total = 0;
+int launch(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, void* stream, const Plan& plan,
+           void* workspace) {
+  const TileConfig& tc = kConfigs[plan.cfg];
+  KernelArgs args;
+  std::memset(&args, 0, sizeof(args));
+  int64_t tiles = 0, units = 0;
+  for (int g = 0; g < G; ++g) {
+    GroupArgs& ga = args.g[g];
+    ga.m = ps[4 * g + 0];
+    ga.n = ps[4 * g + 1];
+    ga.k = ps[4 * g + 2];
+    ga.l = ps[4 * g + 3];
+    ga.a = reinterpret_cast<const uint8_t*>(abc[3 * g + 0]);
+    ga.b = reinterpret_cast<const uint8_t*>(abc[3 * g + 1]);
+    ga.c = reinterpret_cast<uint16_t*>(abc[3 * g + 2]);
+    ga.sfa = reinterpret_cast<const uint8_t*>(sf[2 * g + 0]);
+    ga.sfb = reinterpret_cast<const uint8_t*>(sf[2 * g + 1]);
+    ga.tiles_m = (int32_t)ceil_div64(ga.m, tc.bm);
+    ga.tiles_n = (int32_t)ceil_div64(ga.n, tc.bn);
+    ga.nk = group_stages(ps, g);
+    args.tile_prefix[g] = (int32_t)tiles;
+    args.unit_prefix[g] = (int32_t)units;
+    tiles += group_tiles(ps, g, plan.cfg);
+    units += group_tiles(ps, g, plan.cfg) * ga.nk;
+  }
+  for (int g = G; g <= kMaxGroups; ++g) {
+    args.tile_prefix[g] = (int32_t)tiles;
+    args.unit_prefix[g] = (int32_t)units;
+  }
+  args.num_groups = G;
+  args.split = plan.split;
+  args.grid = plan.grid;
+  if (plan.split) args.partials = reinterpret_cast<float*>(workspace);
+  if (tiles == 0 || plan.grid == 0) return NVFP4_OK;
+  const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(tc.kernel, dim3(plan.grid), dim3(kThreads), 0, st, args);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && plan.split && plan.grid > 1) {
+    const int chunks = tc.bm * tc.bn / 4 / kReduceChunkWords;
+    hipLaunchKernelGGL(tc.reduce, dim3((unsigned)(plan.grid - 1) * chunks), dim3(kThreads), 0, st, args);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) { t_last_hip_error = (int)e; return NVFP4_ERR_HIP; }
+  return NVFP4_OK;
+}
+
+int sizes_ok(const int32_t* ps, int G) {
+  if (G < 1 || G > kMaxGroups || ps == nullptr) return NVFP4_ERR_INVALID;
+  int64_t tiles = 0, units = 0;
   for (int g = 0; g < G; ++g) {
     const int64_t m = ps[4 * g + 0], n = ps[4 * g + 1], k = ps[4 * g + 2], l = ps[4 * g + 3];
     if (m < 0 || n < 0 || k < 0 || l < 1) return NVFP4_ERR_INVALID;
@@ -561,8 +936,48 @@ int nvfp4_grouped_gemm_validate(const int32_t* ps, const uint64_t* abc, const ui
         m > (int64_t(1) << 30) || n > (int64_t(1) << 30) || m * n * l > (int64_t(1) << 40))
       return NVFP4_ERR_INVALID;
     if (m == 0 || n == 0) continue;
-    total += ceil_div64(m, 128) * ceil_div64(n, 128) * l;
-    if (total > (int64_t(1) << 30)) return NVFP4_ERR_INVALID;
+    // tile and unit counts (of the smallest tile) stay within int32
+    tiles += ceil_div64(m, 128) * ceil_div64(n, 128) * l;
+    units += ceil_div64(m, 128) * ceil_div64(n, 128) * l * ceil_div64(k, kBK);
+    if (tiles > (int64_t(1) << 30) || units > (int64_t(1) << 30)) return NVFP4_ERR_INVALID;
+  }
+  return NVFP4_OK;
+}
+
+int run_call(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, void* stream, int cfg, int split,
+             void* workspace, size_t ws_bytes, bool internal_ws) {
+  const int rc = nvfp4_grouped_gemm_validate(ps, abc, sf, G);
+  if (rc != NVFP4_OK) return rc;
+  if (cfg < -1 || cfg >= kNumConfigs || split < -1 || split > 1) return NVFP4_ERR_CONFIG;
+  int cus = 0;
+  const int crc = device_cu_count(&cus);
+  if (crc != NVFP4_OK) return crc;
+  const bool can_split = internal_ws || workspace != nullptr;
+  if (split == 1 && !can_split) return NVFP4_ERR_WORKSPACE;
+  Plan plan = choose_plan(ps, G, cus, cfg, split, can_split);
+  if (plan.split) {
+    if (internal_ws) {
+      const int wrc = internal_workspace(stream, plan.ws_bytes, &workspace);
+      if (wrc != NVFP4_OK) return wrc;
+    } else if (ws_bytes < plan.ws_bytes) {
+      if (split == 1) return NVFP4_ERR_WORKSPACE;
+      plan = choose_plan(ps, G, cus, cfg, 0, false);  // too small: whole tiles instead
+    }
+  }
+  return launch(ps, abc, sf, G, stream, plan, workspace);
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_grouped_gemm_validate(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G) {
+  const int src = sizes_ok(ps, G);
+  if (src != NVFP4_OK) return src;
+  if (abc == nullptr || sf == nullptr) return NVFP4_ERR_INVALID;
+  for (int g = 0; g < G; ++g) {
+    const int64_t m = ps[4 * g + 0], n = ps[4 * g + 1], k = ps[4 * g + 2];
+    if (m == 0 || n == 0) continue;
     const uint64_t a = abc[3 * g + 0], b = abc[3 * g + 1], c = abc[3 * g + 2];
     const uint64_t sa = sf[2 * g + 0], sb = sf[2 * g + 1];
     if (c == 0) return NVFP4_ERR_INVALID;
@@ -587,64 +1002,46 @@ int nvfp4_tile_config_info(int cfg, int* bm, int* bn, int* bk, int* threads) {
 }
 
 int nvfp4_select_tile_config(const int32_t* ps, int G, int num_cus) {
-  if (G < 1 || G > kMaxGroups || ps == nullptr || num_cus < 1) return NVFP4_ERR_INVALID;
-  return select_config(ps, G, num_cus);
+  if (sizes_ok(ps, G) != NVFP4_OK || num_cus < 1) return NVFP4_ERR_INVALID;
+  return choose_plan(ps, G, num_cus, -1, -1, true).cfg;
 }
 
-int nvfp4_launch_geometry(const int32_t* ps, int G, int num_cus, int cfg, int64_t* total_tiles, int* grid) {
-  if (G < 1 || G > kMaxGroups || ps == nullptr || num_cus < 1) return NVFP4_ERR_INVALID;
-  if (cfg < -1 || cfg >= kNumConfigs) return NVFP4_ERR_CONFIG;
-  if (cfg < 0) cfg = select_config(ps, G, num_cus);
-  int64_t total = 0;
-  for (int g = 0; g < G; ++g) total += tiles_of(ps, g, cfg);
-  if (total_tiles) *total_tiles = total;
-  if (grid) *grid = (int)(total < num_cus ? total : num_cus);
-  return cfg;
+int nvfp4_launch_geometry(const int32_t* ps, int G, int num_cus, int cfg, int split, int64_t* total_tiles,
+                          int* grid, int* split_used, size_t* workspace_bytes) {
+  if (sizes_ok(ps, G) != NVFP4_OK || num_cus < 1) return NVFP4_ERR_INVALID;
+  if (cfg < -1 || cfg >= kNumConfigs || split < -1 || split > 1) return NVFP4_ERR_CONFIG;
+  const Plan p = choose_plan(ps, G, num_cus, cfg, split, true);
+  if (total_tiles) *total_tiles = p.tiles;
+  if (grid) *grid = p.grid;
+  if (split_used) *split_used = p.split;
+  if (workspace_bytes) *workspace_bytes = p.ws_bytes;
+  return p.cfg;
 }
 
-int nvfp4_grouped_gemm_config(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G,
-                              void* stream, int cfg) {
-  const int rc = nvfp4_grouped_gemm_validate(ps, abc, sf, G);
-  if (rc != NVFP4_OK) return rc;
-  if (cfg < -1 || cfg >= kNumConfigs) return NVFP4_ERR_CONFIG;
-  int cus = 0;
-  const int crc = device_cu_count(&cus);
-  if (crc != NVFP4_OK) return crc;
-  if (cfg < 0) cfg = select_config(ps, G, cus);
-  const TileConfig& tc = kConfigs[cfg];
-
-  KernelArgs args;
-  std::memset(&args, 0, sizeof(args));
-  int64_t total = 0;
-  for (int g = 0; g < G; ++g) {
-    GroupArgs& ga = args.g[g];
-    ga.m = ps[4 * g + 0];
-    ga.n = ps[4 * g + 1];
-    ga.k = ps[4 * g + 2];
-    ga.l = ps[4 * g + 3];
-    ga.a = reinterpret_cast<const uint8_t*>(abc[3 * g + 0]);
-    ga.b = reinterpret_cast<const uint8_t*>(abc[3 * g + 1]);
-    ga.c = reinterpret_cast<uint16_t*>(abc[3 * g + 2]);
-    ga.sfa = reinterpret_cast<const uint8_t*>(sf[2 * g + 0]);
-    ga.sfb = reinterpret_cast<const uint8_t*>(sf[2 * g + 1]);
-    ga.tiles_m = (int32_t)ceil_div64(ga.m, tc.bm);
-    ga.tiles_n = (int32_t)ceil_div64(ga.n, tc.bn);
-    args.prefix[g] = (int32_t)total;
-    total += tiles_of(ps, g, cfg);
+size_t nvfp4_workspace_bytes(const int32_t* ps, int G, int num_cus) {
+  if (sizes_ok(ps, G) != NVFP4_OK || num_cus < 1) return 0;
+  // enough for any plan the library may pick on this many compute units
+  size_t need = 0;
+  for (int c = 0; c < kNumConfigs; ++c) {
+    const Plan p = plan_for(ps, G, num_cus, c, 1);
+    need = p.ws_bytes > need ? p.ws_bytes : need;
   }
-  for (int g = G; g <= kMaxGroups; ++g) args.prefix[g] = (int32_t)total;
-  args.num_groups = G;
-  if (total == 0) return NVFP4_OK;
+  return need;
+}
 
-  const int grid = (int)(total < cus ? total : cus);
-  hipLaunchKernelGGL(tc.kernel, dim3(grid), dim3(kThreads), 0, reinterpret_cast<hipStream_t>(stream), args);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) { t_last_hip_error = (int)e; return NVFP4_ERR_HIP; }
-  return NVFP4_OK;
+int nvfp4_grouped_gemm_config(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, void* stream,
+                              int cfg) {
+  return run_call(ps, abc, sf, G, stream, cfg, -1, nullptr, 0, true);
 }
 
 int nvfp4_grouped_gemm(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, void* stream) {
-  return nvfp4_grouped_gemm_config(ps, abc, sf, G, stream, -1);
+  return run_call(ps, abc, sf, G, stream, -1, -1, nullptr, 0, true);
+}
+
+int nvfp4_grouped_gemm_ex(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, void* workspace,
+                          size_t workspace_bytes, int tile_config, int split_mode, void* stream) {
+  if (workspace != nullptr && (reinterpret_cast<uint64_t>(workspace) & 255u) != 0) return NVFP4_ERR_MISALIGNED;
+  return run_call(ps, abc, sf, G, stream, tile_config, split_mode, workspace, workspace_bytes, false);
 }
 
 size_t nvfp4_sf_bytes(int rows, int k, int l) {
@@ -658,9 +1055,10 @@ const char* nvfp4_error_string(int code) {
   switch (code) {
     case NVFP4_OK: return "ok";
     case NVFP4_ERR_INVALID: return "invalid argument (group count, sizes, divisibility or null pointer)";
-    case NVFP4_ERR_MISALIGNED: return "device pointer not 16-byte aligned";
+    case NVFP4_ERR_MISALIGNED: return "pointer not aligned (16 bytes; 256 for a workspace)";
     case NVFP4_ERR_HIP: return "HIP runtime error (see nvfp4_last_hip_error)";
-    case NVFP4_ERR_CONFIG: return "unknown tile configuration";
+    case NVFP4_ERR_CONFIG: return "unknown tile configuration or split mode";
+    case NVFP4_ERR_WORKSPACE: return "stream-K requested without a large enough workspace";
     default: return "unknown error code";
   }
 }

@@ -5,7 +5,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from ._binding import nvfp4_grouped_gemm_config
+from ._binding import nvfp4_grouped_gemm_config, nvfp4_grouped_gemm_ex
 
 FP16_NAN_BITS = 0xFFFF
 
@@ -41,12 +41,30 @@ def pointer_tables(dev_groups):
     return abc, sf
 
 
-def run(shapes, dev_groups, stream=None, tile_config=-1):
-    """Enqueue one grouped GEMM on ``stream`` (default: torch's current stream)."""
+def run(shapes, dev_groups, stream=None, tile_config=-1, split_mode=None, workspace=None):
+    """Enqueue one grouped GEMM on ``stream`` (default: torch's current stream).
+
+    With ``split_mode`` or ``workspace`` given, the call goes through
+    nvfp4_grouped_gemm_ex with that (uint8 tensor) workspace; otherwise through
+    nvfp4_grouped_gemm_config (library-owned workspace)."""
     if stream is None:
         stream = torch.cuda.current_stream()
     abc, sf = pointer_tables(dev_groups)
-    nvfp4_grouped_gemm_config(shapes, abc, sf, len(shapes), stream, tile_config)
+    if split_mode is None and workspace is None:
+        nvfp4_grouped_gemm_config(shapes, abc, sf, len(shapes), stream, tile_config)
+    else:
+        ws_ptr = 0 if workspace is None else workspace.data_ptr()
+        ws_bytes = 0 if workspace is None else workspace.numel()
+        nvfp4_grouped_gemm_ex(shapes, abc, sf, len(shapes), ws_ptr, ws_bytes, tile_config,
+                              -1 if split_mode is None else split_mode, stream)
+
+
+def workspace_for(shapes, device="cuda"):
+    """A uint8 workspace tensor large enough for any plan on this device."""
+    from ._binding import nvfp4_workspace_bytes
+    cus = torch.cuda.get_device_properties(torch.device(device)).multi_processor_count
+    n = max(nvfp4_workspace_bytes(shapes, cus), 256)
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def c_as_numpy(shapes, dev_groups):

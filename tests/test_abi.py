@@ -128,16 +128,38 @@ def test_tile_configs_and_geometry():
     shapes = synth.workload_shapes(2)
     for c in range(n):
         info = mm.nvfp4_tile_config_info(c)
-        geo = mm.nvfp4_launch_geometry(shapes, 256, c)
         expect = sum(-(-m // info["bm"]) * -(-nn // info["bn"]) * l for (m, nn, k, l) in shapes)
+        units = sum(-(-m // info["bm"]) * -(-nn // info["bn"]) * l * -(-k // 128) for (m, nn, k, l) in shapes)
+        geo = mm.nvfp4_launch_geometry(shapes, 256, c, 0)
         assert geo["config"] == c and geo["total_tiles"] == expect and geo["grid"] == min(expect, 256)
+        assert geo["split"] == 0 and geo["workspace_bytes"] == 0
+        geo = mm.nvfp4_launch_geometry(shapes, 256, c, 1)
+        assert geo["split"] == 1 and geo["grid"] == min(units, 256)
+        assert geo["workspace_bytes"] == geo["grid"] * 2 * info["bm"] * info["bn"] * 4
+        assert mm.nvfp4_workspace_bytes(shapes, 256) >= geo["workspace_bytes"]
     # empty groups own no tiles, wherever they sit
-    geo = mm.nvfp4_launch_geometry([(0, 128, 64, 1), (128, 128, 64, 1), (128, 0, 64, 1)], 256, 0)
+    geo = mm.nvfp4_launch_geometry([(0, 128, 64, 1), (128, 128, 64, 1), (128, 0, 64, 1)], 256, 0, 0)
     assert geo["total_tiles"] == 1
+    with pytest.raises(mm.Nvfp4Error):
+        mm.nvfp4_launch_geometry(shapes, 256, 0, 2)
     sel = mm.nvfp4_select_tile_config(synth.workload_shapes(4), 256)
     assert 0 <= sel < n
 
 
+def test_ex_entry_point_checks_before_any_hip_call():
+    shapes = [(128, 128, 128, 1)]
+    abc, sf = _ptrs(1)
+    with pytest.raises(mm.Nvfp4Error) as e:  # workspace not 256-byte aligned
+        mm.nvfp4_grouped_gemm_ex(shapes, abc, sf, workspace=0x10010, workspace_bytes=1 << 20)
+    assert e.value.code == mm.NVFP4_ERR_MISALIGNED
+    with pytest.raises(mm.Nvfp4Error) as e:
+        mm.nvfp4_grouped_gemm_ex(shapes, abc, sf, split_mode=3)
+    assert e.value.code == mm.NVFP4_ERR_CONFIG
+    with pytest.raises(mm.Nvfp4Error) as e:
+        mm.nvfp4_grouped_gemm_ex([(128, 100, 128, 1)], abc, sf)
+    assert e.value.code == mm.NVFP4_ERR_INVALID
+
+
 def test_error_strings():
-    for code in (0, -1, -2, -3, -4, 7):
+    for code in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(mm.nvfp4_error_string(code), str)

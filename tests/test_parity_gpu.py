@@ -45,11 +45,12 @@ def poison_padding(shapes, groups):
     return out
 
 
-def check(shapes, groups, tile_config=-1, label="", ref=None):
+def check(shapes, groups, tile_config=-1, label="", ref=None, split_mode=None):
     groups = poison_padding(shapes, groups)
-    announce(f"{label} shapes={shapes} tile_config={tile_config}")
+    announce(f"{label} shapes={shapes} tile_config={tile_config} split_mode={split_mode}")
     d = dev.upload(shapes, groups, c_guard=GUARD)
-    dev.run(shapes, d, tile_config=tile_config)
+    ws = None if split_mode is None else dev.workspace_for(shapes)
+    dev.run(shapes, d, tile_config=tile_config, split_mode=split_mode, workspace=ws)
     torch.cuda.synchronize()
     got = dev.c_as_numpy(shapes, d)
     assert dev.guards_intact(d), "store outside C"
@@ -97,15 +98,61 @@ def test_edge_shapes(name):
             assert np.all(c == 0), "k = 0 must write zeros"
 
 
+@pytest.mark.parametrize("split", [0, 1])
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3])
-def test_every_tile_config(cfg):
+def test_every_tile_config(cfg, split):
+    """Each compiled tile configuration, with whole tiles and with stream-K."""
     if cfg >= mm.nvfp4_num_tile_configs():
         pytest.skip("config not compiled")
     for idx in (0, 1):
         shapes, groups = synth.make_workload(idx)
-        check(shapes, groups, tile_config=cfg, label=f"workload {idx}")
-    shapes = EDGE_CASES["g8_ragged"]
-    check(shapes, synth.make_custom(shapes, seed=77), tile_config=cfg, label="g8_ragged")
+        check(shapes, groups, tile_config=cfg, split_mode=split, label=f"workload {idx}")
+    for name in ("g8_ragged", "empty_groups_in_middle", "k_zero", "batch_l2"):
+        shapes = EDGE_CASES[name]
+        check(shapes, synth.make_custom(shapes, seed=77), tile_config=cfg, split_mode=split, label=name)
+
+
+@pytest.mark.parametrize("idx", [2, 3, 4])
+def test_streamk_full_workloads(idx):
+    shapes, groups = synth.make_workload(idx)
+    check(shapes, groups, split_mode=1, label=f"workload {idx} stream-K")
+
+
+def test_heuristic_streamk_with_library_workspace():
+    """Few tiles with a long K: the heuristic splits K over the whole grid, using
+    the workspace the library allocates itself (default entry point)."""
+    shapes = [(256, 256, 16384, 1), (40, 136, 64, 1)]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert mm.nvfp4_launch_geometry(shapes, cus)["split"] == 1
+    check(shapes, synth.make_custom(shapes, seed=12), label="long-K heuristic stream-K")
+
+
+def test_streamk_is_deterministic_and_workspace_rules():
+    shapes, groups = synth.make_workload(1)
+    announce("stream-K determinism workload 1")
+    d = dev.upload(shapes, groups)
+    ws = dev.workspace_for(shapes)
+    outs = []
+    for _ in range(3):
+        for dd in d:
+            dd["c"].fill_(0)
+        dev.run(shapes, d, split_mode=1, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append([c.copy() for c in dev.c_as_numpy(shapes, d)])
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    tiny = torch.empty(256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(mm.Nvfp4Error) as e:
+        dev.run(shapes, d, split_mode=1, workspace=tiny)
+    assert e.value.code == mm.NVFP4_ERR_WORKSPACE
+    for dd in d:
+        dd["c"].fill_(-1)
+    dev.run(shapes, d, workspace=tiny)  # the heuristic falls back to whole tiles
+    torch.cuda.synchronize()
+    ref = O.grouped_gemm(shapes, groups)
+    for c, r in zip(dev.c_as_numpy(shapes, d), ref):
+        assert not O.tolerance_violations(c, r["c16"], r["s"]).any()
 
 
 def test_full_e4m3_range_scales():
