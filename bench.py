@@ -137,17 +137,21 @@ def cpu_baseline(idx, max_rows=None, min_seconds=10.0):
                 seconds=dt, cpu_count=os.cpu_count())
 
 
-def copy_calibration(nbytes=256 << 20, reps=5):
-    """A plain device-to-device copy of known size, for scaling the HBM traffic
-    counters (FETCH_SIZE / WRITE_SIZE) of the GEMM kernel."""
+def copy_calibration(nbytes=1 << 30, reps=3):
+    """A plain device-to-device copy of known size (nbytes read, nbytes written),
+    for scaling the HBM traffic counters (FETCH_SIZE / WRITE_SIZE) of the GEMM
+    kernel. Before each copy a 512 MiB buffer is overwritten, so the source is
+    not resident in the 256 MiB last-level cache."""
     import torch
     src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     src.random_(0, 256)
     dst = torch.empty_like(src)
-    torch.cuda.synchronize()
-    for _ in range(reps):
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    for r in range(reps):
+        flush.fill_(r)
+        torch.cuda.synchronize()
         dst.copy_(src)
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
     log(f"[bench] copy calibration: {reps} copies of {nbytes} bytes")
 
 
