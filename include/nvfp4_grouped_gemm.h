@@ -28,11 +28,12 @@
  *
  * Work decomposition: output tiles (one of a few compiled shapes) are spread
  * over a persistent grid of one workgroup per compute unit, either whole
- * (workgroup b takes tiles b, b + grid, ...) or stream-K (each workgroup takes
- * an equal share of all (tile, 128-K stage) units; a tile split between
- * workgroups is summed, in a fixed order, by the last one to finish). Stream-K
- * needs a workspace: an arrival counter per tile and two fp32 tile-sized slots
- * per workgroup.
+ * (each workgroup takes every grid-th tile) or stream-K (each workgroup takes
+ * an equal share of all (tile, 128-K stage) units and stores the fp32 partial
+ * sums of the tiles it shares; a second kernel, on the same stream, adds them
+ * in workgroup order, so results do not depend on timing). Stream-K needs a
+ * workspace of two fp32 tile-sized slots per workgroup; it holds no state
+ * between calls.
  *
  * Ownership and threading: the caller owns every buffer. Host tables are read
  * before a call returns. Calls are stream-ordered and asynchronous. The
@@ -88,10 +89,9 @@ int nvfp4_grouped_gemm(const int32_t* problem_sizes, const uint64_t* ptrs_abc,
 /*
  * nvfp4_grouped_gemm_ex - as nvfp4_grouped_gemm, with the caller's workspace
  * and explicit choices; allocates nothing.
- *   workspace        device buffer (256-byte aligned) or NULL; its first
- *                    bytes (the per-tile counters) must be zero before the
- *                    first use, and every completed call leaves them zero.
- *                    Calls that may overlap in time need distinct workspaces.
+ *   workspace        device buffer (256-byte aligned) or NULL; its contents
+ *                    need no initialisation. Calls that may overlap in time
+ *                    need distinct workspaces.
  *   workspace_bytes  its size; see nvfp4_workspace_bytes.
  *   tile_config      -1 (heuristic) or 0 .. nvfp4_num_tile_configs()-1.
  *   split_mode       -1 (heuristic), 0 (whole tiles), 1 (stream-K).

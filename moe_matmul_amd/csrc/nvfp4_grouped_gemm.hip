@@ -6,18 +6,20 @@
 // gemm"; layouts as in the header).
 //
 // Design (gfx950 first, not a translation of the pages' Blackwell kernels):
-//  * Persistent grid of one 256-thread workgroup per compute unit. A workgroup
-//    walks output tiles t = blockIdx.x, blockIdx.x + gridDim.x, ...; the group
-//    of a tile is found by binary search over the per-group tile prefix sum
-//    (the scheduler of submission 506336 keeps the same prefix), and tiles are
-//    rastered M-fastest inside a group.
-//  * Packed FP4 operand tiles are staged through two LDS buffers with 128-bit
-//    loads. Each 64-byte row slab is stored with its four 16-byte chunks XOR
-//    swizzled by (row >> 1) & 3, so the 128-bit reads of eight consecutive rows
-//    touch all 32 banks.
-//  * Scales come straight from the tiled layout into VGPRs: the 16-byte chunk
-//    (r % 32) of a 512-byte atom holds rows r, r+32, r+64, r+96 for four
-//    16-blocks, exactly the rows one lane feeds to a 32x32 MFMA.
+//  * Persistent grid of one 256-thread workgroup per compute unit. Workgroup
+//    b gets a virtual index that gives each of the 8 XCDs a contiguous run of
+//    indices. Whole tiles: virtual index v takes tiles v, v + grid, ...
+//    Stream-K: v takes an equal share of all (tile, 128-K stage) units. The
+//    group of a tile is found by binary search over the per-group tile prefix
+//    sum (the scheduler of submission 506336 keeps the same prefix); inside a
+//    group, tiles run down columns of 8-tile-wide super-columns.
+//  * Packed FP4 operand tiles and their scale atoms go straight from global
+//    memory to LDS (buffer_load ... lds), four stages deep, streamed across
+//    tile boundaries. Each 64-byte row slab has its four 16-byte chunks XOR
+//    swizzled so that the 128-bit reads of a wave are bank-conflict free.
+//  * Scales are read from the tiled layout in LDS: the 16-byte chunk (r % 32)
+//    of a 512-byte atom holds rows r, r+32, r+64, r+96 for four 16-blocks,
+//    exactly the rows one lane feeds to a 32x32 MFMA.
 //  * Exact dequantisation to f16 in registers: v_cvt_scalef32_pk_f16_fp4 with
 //    scale 1.0 (E2M1 values are exact in f16), then one v_pk_mul_f16 by the
 //    E4M3 scale (converted exactly with v_cvt_scalef32_pk_f16_fp8). |a*s| has
@@ -26,13 +28,17 @@
 //    exponent of its f32 scale, so the E4M3 mantissa needs the separate
 //    multiply.)
 //  * v_mfma_f32_32x32x16_f16 with B as the first operand, so each lane ends up
-//    holding four consecutive columns of one output row.
+//    holding four consecutive columns of one output row. A wave skips the
+//    LDS reads, dequantisation and MFMAs of its 32-row blocks that lie wholly
+//    past m (ragged M of the expert groups).
 //  * Inside each 64-K group the K order fed to the MFMA is permuted so that a
 //    lane reads 32 consecutive FP4 codes (16 bytes) of its row: lane half h
 //    takes K elements [32h, 32h+32) in four steps of 8. A and B use the same
 //    permutation, so the sum is unchanged; each step of 8 lies inside one
 //    16-block, so one scale covers it.
 //  * Epilogue: fp32 -> fp16 (RNE) fused, 8-byte stores masked to m and n.
+//    Tiles split by stream-K store fp32 partials; a second kernel adds them in
+//    a fixed order and writes fp16.
 
 #include <hip/hip_runtime.h>
 
@@ -62,6 +68,8 @@ constexpr int kBK = 128;          // K elements per pipeline stage
 constexpr int kRowBytes = kBK / 2; // packed bytes per row per stage
 constexpr int kAtomBytes = 512;    // one 128-row x 64-K scale atom
 constexpr int kBufferWord3 = 0x00020000;  // gfx9 buffer resource word 3 (raw, 32-bit data)
+constexpr int kXcds = 8;                  // accelerator complex dies: workgroups go round-robin over them
+constexpr int kRasterWidth = 8;           // n-tiles per raster super-column
 
 struct GroupArgs {
   const uint8_t* a;
@@ -221,6 +229,19 @@ struct GemmKernel {
   const KernelArgs& args;
   uint8_t* smem;
   int wave, wm, wn, h, lr, lane;
+  int vwg;  // this workgroup's virtual index
+  // Per-lane byte offsets inside a stage of the lane's first A and B chunk for
+  // half kk, and of its scale words. A row's swizzle depends only on its bits
+  // 1..3, so 32-row block i adds exactly i * 32 * kRowBytes to these.
+  int a_base[2], b_base[2], sa_base, sb_base;
+
+  // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+  // L2). The virtual index gives each XCD a contiguous run of indices, hence of
+  // tiles (or units), which the raster below turns into compact 2-D blocks.
+  __device__ __forceinline__ int virtual_wg(int b) const {
+    const int P = args.grid, q = P / kXcds, r = P % kXcds, x = b % kXcds;
+    return x * q + (x < r ? x : r) + b / kXcds;
+  }
 
   __device__ GemmKernel(const KernelArgs& a, uint8_t* sm) : args(a), smem(sm) {
     const int tid = threadIdx.x;
@@ -230,6 +251,14 @@ struct GemmKernel {
     wn = wave % WAVES_N;
     h = lane >> 5;
     lr = lane & 31;
+    vwg = blockIdx.x < (unsigned)a.grid ? virtual_wg(blockIdx.x) : 0;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      a_base[kk] = lds_off(wm * WM + lr, kk * 2 + h);
+      b_base[kk] = A_BYTES + lds_off(wn * WN + lr, kk * 2 + h);
+    }
+    sa_base = A_BYTES + B_BYTES + ((wm * WM) >> 7) * 1024 + lr * 16 + (((wm * WM) & 127) >> 5) * 4;
+    sb_base = A_BYTES + B_BYTES + (BM / 128 + ((wn * WN) >> 7)) * 1024 + lr * 16 + (((wn * WN) & 127) >> 5) * 4;
   }
 
   // ---------------- work decomposition ----------------
@@ -271,9 +300,9 @@ struct GemmKernel {
 
   __device__ __forceinline__ void first_segment(Segment& s) const {
     if (args.split) {
-      locate(s, unit_begin(blockIdx.x), unit_begin(blockIdx.x + 1));
+      locate(s, unit_begin(vwg), unit_begin(vwg + 1));
     } else {
-      s.tile = blockIdx.x;
+      s.tile = vwg;
       s.valid = s.tile < total_tiles();
       s.s0 = 0;
       s.s1 = s.valid ? args.g[group_of_tile(s.tile)].nk : 0;
@@ -282,7 +311,7 @@ struct GemmKernel {
 
   __device__ __forceinline__ void next_segment(Segment& s) const {
     if (args.split) {
-      locate(s, s.u + (s.s1 - s.s0), unit_begin(blockIdx.x + 1));
+      locate(s, s.u + (s.s1 - s.s0), unit_begin(vwg + 1));
     } else {
       s.tile += args.grid;
       s.valid = s.tile < total_tiles();
@@ -300,8 +329,16 @@ struct GemmKernel {
     const int rest = tile - args.tile_prefix[gi];
     const int li = rest / per_l;
     const int r2 = rest - li * per_l;
-    const int tm = r2 % tiles_m;  // M-fastest raster inside the group
-    const int tn = r2 / tiles_m;
+    // Raster inside the group: super-columns of kRasterWidth n-tiles, taken
+    // left to right; inside one, rows of up to kRasterWidth tiles, top to
+    // bottom. Consecutive tiles then share A rows and B columns: 32 of them
+    // (one XCD's share of a 256-workgroup wave) span 4 A and 8 B panels.
+    const int tiles_n = G.tiles_n;
+    const int sc = r2 / (tiles_m * kRasterWidth);
+    const int in_sc = r2 - sc * tiles_m * kRasterWidth;
+    const int width = min(kRasterWidth, tiles_n - sc * kRasterWidth);
+    const int tm = in_sc / width;
+    const int tn = sc * kRasterWidth + in_sc % width;
     const int kbytes = K >> 1;
     const int Kt = K >> 6;
     const int Mt = (M + 127) >> 7;
@@ -401,48 +438,55 @@ struct GemmKernel {
   }
 
   // ---------------- dequantisation and MFMA ----------------
+  // The compute below is instantiated for AMB = number of this wave's 32-row
+  // blocks that hold rows below m (0 .. MB): blocks past m cost no LDS reads,
+  // no dequantisation and no MFMAs. A wave with AMB = 0 still issues its share
+  // of the loads and joins every barrier.
+
   // ds_reads of one half stage (kk) from LDS buffer buf.
+  template <int AMB>
   __device__ __forceinline__ void read_half(Raw& r, int buf, int kk) const {
-    const uint8_t* As = smem + buf * STAGE_BYTES;
-    const uint8_t* Bs = As + A_BYTES;
-    const uint8_t* Ss = Bs + B_BYTES;
+    if (AMB == 0) return;
+    const uint8_t* St = smem + buf * STAGE_BYTES;
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
-      r.a[i] = *reinterpret_cast<const u32x4*>(As + lds_off(wm * WM + i * 32 + lr, kk * 2 + h));
+    for (int i = 0; i < AMB; ++i)
+      r.a[i] = *reinterpret_cast<const u32x4*>(St + a_base[kk] + i * 32 * kRowBytes);
 #pragma unroll
     for (int j = 0; j < NB; ++j)
-      r.b[j] = *reinterpret_cast<const u32x4*>(Bs + lds_off(wn * WN + j * 32 + lr, kk * 2 + h));
-    const ScaleVec<MB> sa = *reinterpret_cast<const ScaleVec<MB>*>(
-        Ss + ((wm * WM) >> 7) * 1024 + kk * 512 + lr * 16 + (((wm * WM) & 127) >> 5) * 4);
-    const ScaleVec<NB> sb = *reinterpret_cast<const ScaleVec<NB>*>(
-        Ss + (BM / 128 + ((wn * WN) >> 7)) * 1024 + kk * 512 + lr * 16 + (((wn * WN) & 127) >> 5) * 4);
+      r.b[j] = *reinterpret_cast<const u32x4*>(St + b_base[kk] + j * 32 * kRowBytes);
+    const ScaleVec<MB> sa = *reinterpret_cast<const ScaleVec<MB>*>(St + sa_base + kk * 512);
+    const ScaleVec<NB> sb = *reinterpret_cast<const ScaleVec<NB>*>(St + sb_base + kk * 512);
 #pragma unroll
-    for (int i = 0; i < MB; ++i) r.sa[i] = sa[i];
+    for (int i = 0; i < AMB; ++i) r.sa[i] = sa[i];
 #pragma unroll
     for (int j = 0; j < NB; ++j) r.sb[j] = sb[j];
   }
 
   // The lane's two E4M3 scales (16-blocks 2h, 2h+1 of the half) -> f16, exactly.
+  template <int AMB>
   __device__ __forceinline__ void convert_scales(Scales& s, const Raw& r) const {
+    if (AMB == 0) return;
     const int hshift = h * 16;
 #pragma unroll
-    for (int i = 0; i < MB; ++i) s.a[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sa[i] >> hshift, 1.0f, false);
+    for (int i = 0; i < AMB; ++i) s.a[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sa[i] >> hshift, 1.0f, false);
 #pragma unroll
     for (int j = 0; j < NB; ++j) s.b[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sb[j] >> hshift, 1.0f, false);
   }
 
   // Operand fragments of substep S (K elements 8S..8S+7 of the lane's 32).
-  template <int S>
+  template <int S, int AMB>
   __device__ __forceinline__ void dequant(Frags& f, const Raw& r, const Scales& s) const {
+    if (AMB == 0) return;
 #pragma unroll
-    for (int i = 0; i < MB; ++i) f.a[i] = dequant8(r.a[i][S], s.a[i][S >> 1]);
+    for (int i = 0; i < AMB; ++i) f.a[i] = dequant8(r.a[i][S], s.a[i][S >> 1]);
 #pragma unroll
     for (int j = 0; j < NB; ++j) f.b[j] = dequant8(r.b[j][S], s.b[j][S >> 1]);
   }
 
+  template <int AMB>
   __device__ __forceinline__ static void mfmas(f32x16 (&acc)[MB][NB], const Frags& f) {
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
+    for (int i = 0; i < AMB; ++i)
 #pragma unroll
       for (int j = 0; j < NB; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
@@ -452,16 +496,17 @@ struct GemmKernel {
   // interleaved with the dequantisation of the next substep into `fill`
   // (8 VALU per pair of fragments: 4 VALU per MFMA for 128x128 wave tiles).
   // With CONVERT, the next half's scales are converted here as well.
-  template <int NEXT_S, bool CONVERT>
+  template <int NEXT_S, bool CONVERT, int AMB>
   __device__ __forceinline__ void step(f32x16 (&acc)[MB][NB], const Frags& use, Frags& fill, const Raw& src,
                                        Scales& ssrc) const {
-    constexpr int VALU = (MB + NB) * 8 + (CONVERT ? 2 * (MB + NB) : 0);
-    constexpr int PER = (VALU + MB * NB - 1) / (MB * NB);
-    if (CONVERT) convert_scales(ssrc, src);
-    dequant<NEXT_S>(fill, src, ssrc);
-    mfmas(acc, use);
+    if (AMB == 0) return;
+    constexpr int VALU = (AMB + NB) * 8 + (CONVERT ? 2 * (AMB + NB) : 0);
+    constexpr int PER = (VALU + AMB * NB - 1) / (AMB * NB > 0 ? AMB * NB : 1);
+    if (CONVERT) convert_scales<AMB>(ssrc, src);
+    dequant<NEXT_S, AMB>(fill, src, ssrc);
+    mfmas<AMB>(acc, use);
 #pragma unroll
-    for (int q = 0; q < MB * NB; ++q) {
+    for (int q = 0; q < AMB * NB; ++q) {
       __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedVALU, PER, 0);
     }
@@ -470,6 +515,7 @@ struct GemmKernel {
 
   // n stages of one segment, whose first stage is global stage g0. On entry
   // the loader has issued at least stage g0.
+  template <int AMB>
   __device__ __forceinline__ void mainloop(f32x16 (&acc)[MB][NB], int n, int g0, Loader& ld) const {
     Raw r0, r1;
     Scales s0, s1;
@@ -478,18 +524,18 @@ struct GemmKernel {
     block_sync();
     // top up: every buffer of a stage before g0 is free now
     while (ld.seg.valid && ld.issued < g0 + NS) issue_next(ld);
-    read_half(r0, g0 % NS, 0);
-    convert_scales(s0, r0);
-    dequant<0>(f0, r0, s0);
+    read_half<AMB>(r0, g0 % NS, 0);
+    convert_scales<AMB>(s0, r0);
+    dequant<0, AMB>(f0, r0, s0);
     for (int kt = 0; kt < n; ++kt) {
       const int g = g0 + kt;
       // ---- first half (K 0..63 of the stage): raw data in r0 ----
-      read_half(r1, g % NS, 1);
-      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, MB + NB + 2, 0);
-      step<1, false>(acc, f0, f1, r0, s0);
-      step<2, false>(acc, f1, f0, r0, s0);
-      step<3, false>(acc, f0, f1, r0, s0);
-      step<0, true>(acc, f1, f0, r1, s1);
+      read_half<AMB>(r1, g % NS, 1);
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, AMB + NB + 2, 0);
+      step<1, false, AMB>(acc, f0, f1, r0, s0);
+      step<2, false, AMB>(acc, f1, f0, r0, s0);
+      step<3, false, AMB>(acc, f0, f1, r0, s0);
+      step<0, true, AMB>(acc, f1, f0, r1, s1);
       // ---- second half: raw data in r1. Stage g+1 must have landed before its
       // first half is read; every wave is done with stage g's buffer here, so
       // stage g + NS can take it.
@@ -499,12 +545,27 @@ struct GemmKernel {
       }
       block_sync();
       if (ld.seg.valid && ld.issued <= g + NS) issue_next(ld);
-      read_half(r0, (g + 1) % NS, 0);  // unused after the last stage
-      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, MB + NB + 2, 0);
-      step<1, false>(acc, f0, f1, r1, s1);
-      step<2, false>(acc, f1, f0, r1, s1);
-      step<3, false>(acc, f0, f1, r1, s1);
-      step<0, true>(acc, f1, f0, r0, s0);
+      read_half<AMB>(r0, (g + 1) % NS, 0);  // unused after the last stage
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, AMB + NB + 2, 0);
+      step<1, false, AMB>(acc, f0, f1, r1, s1);
+      step<2, false, AMB>(acc, f1, f0, r1, s1);
+      step<3, false, AMB>(acc, f0, f1, r1, s1);
+      step<0, true, AMB>(acc, f1, f0, r0, s0);
+    }
+  }
+
+  // Dispatch on this wave's active 32-row blocks (rows below m).
+  __device__ __forceinline__ void mainloop_rows(f32x16 (&acc)[MB][NB], const TileCtx& t, int n, int g0,
+                                                Loader& ld) const {
+    const int rows = t.M - (t.row0 + wm * WM);
+    const int amb = rows <= 0 ? 0 : (rows >= WM ? MB : (rows + 31) / 32);
+    static_assert(MB <= 4, "active-block dispatch covers MB <= 4");
+    switch (amb) {
+      case 0: mainloop<0>(acc, n, g0, ld); break;
+      case 1: mainloop<(MB >= 1 ? 1 : MB)>(acc, n, g0, ld); break;
+      case 2: mainloop<(MB >= 2 ? 2 : MB)>(acc, n, g0, ld); break;
+      case 3: mainloop<(MB >= 3 ? 3 : MB)>(acc, n, g0, ld); break;
+      default: mainloop<MB>(acc, n, g0, ld); break;
     }
   }
 
@@ -546,7 +607,7 @@ struct GemmKernel {
   // fp32 partial sum; the reduction kernel adds the partials up.
   __device__ __forceinline__ void write_partial(const f32x16 (&acc)[MB][NB], bool first_seg) const {
     uint8_t* slot = reinterpret_cast<uint8_t*>(args.partials) +
-                    ((size_t)blockIdx.x * 2 + (first_seg ? 0 : 1)) * TILE_FLOATS * 4;
+                    ((size_t)vwg * 2 + (first_seg ? 0 : 1)) * TILE_FLOATS * 4;
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -567,7 +628,7 @@ struct GemmKernel {
       for (int j = 0; j < NB; ++j) zero[i][j] = f32x16{};
     for (int gi = 0; gi < args.num_groups; ++gi) {
       if (args.g[gi].nk != 0) continue;
-      for (int tile = args.tile_prefix[gi] + blockIdx.x; tile < args.tile_prefix[gi + 1]; tile += gridDim.x)
+      for (int tile = args.tile_prefix[gi] + vwg; tile < args.tile_prefix[gi + 1]; tile += args.grid)
         epilogue(zero, setup(tile));
     }
   }
@@ -588,7 +649,7 @@ struct GemmKernel {
       for (int i = 0; i < MB; ++i)
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
-      if (n > 0) mainloop(acc, n, g0, ld);
+      if (n > 0) mainloop_rows(acc, t, n, g0, ld);
       if (seg.s0 == 0 && seg.s1 == t.nk) epilogue(acc, t);
       else write_partial(acc, first_seg);
       g0 += n;
@@ -602,11 +663,19 @@ struct GemmKernel {
 // Stage layout in LDS (bytes): [A: BM rows x 64][B: BN rows x 64]
 // [scale atoms: (BM + BN) / 128 atom rows x 2 k-groups x 512]; A and B rows are
 // swizzled by lds_off, the scale atoms are stored as in global memory.
+// The kernels' single argument, read in place from the kernarg segment (where
+// it starts at offset 0). Binding the by-value parameter to a reference makes
+// the compiler keep a private copy of it once the argument has many readers;
+// reads through this pointer stay uniform constant loads.
+__device__ __forceinline__ const KernelArgs& kernel_args() {
+  return *(const KernelArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+}
+
 template <int BM, int BN, int WM, int WN, int NS>
-__global__ __launch_bounds__(kThreads, 1) void nvfp4_grouped_gemm_kernel(KernelArgs args) {
+__global__ __launch_bounds__(kThreads, 1) void nvfp4_grouped_gemm_kernel(KernelArgs) {
   using K = GemmKernel<BM, BN, WM, WN, NS>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * K::STAGE_BYTES];
-  const K k(args, smem);
+  const K k(kernel_args(), smem);
   k.run();
 }
 
@@ -621,11 +690,12 @@ constexpr int kReduceWordsPerThread = 4;
 constexpr int kReduceChunkWords = kThreads * kReduceWordsPerThread;
 
 template <int BM, int BN, int WM, int WN, int NS>
-__global__ __launch_bounds__(kThreads) void nvfp4_streamk_reduce_kernel(KernelArgs args) {
+__global__ __launch_bounds__(kThreads) void nvfp4_streamk_reduce_kernel(KernelArgs) {
   using K = GemmKernel<BM, BN, WM, WN, NS>;
   constexpr int WORDS = K::TILE_FLOATS / 4;
   constexpr int CHUNKS = WORDS / kReduceChunkWords;
   static_assert(WORDS % kReduceChunkWords == 0, "chunking");
+  const KernelArgs& args = kernel_args();
   const K k(args, nullptr);
   const int boundary = 1 + (int)(blockIdx.x / CHUNKS);  // workgroup whose range starts inside the tile
   const int chunk = (int)(blockIdx.x % CHUNKS);

@@ -112,6 +112,18 @@ def test_every_tile_config(cfg, split):
         check(shapes, synth.make_custom(shapes, seed=77), tile_config=cfg, split_mode=split, label=name)
 
 
+@pytest.mark.parametrize("split", [0, 1])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+def test_masked_row_blocks(cfg, split):
+    """M tails that leave each wave 0, 1, 2, 3 or 4 active 32-row blocks, in the
+    first and second wave row of a tile (waves skip blocks wholly past m)."""
+    if cfg >= mm.nvfp4_num_tile_configs():
+        pytest.skip("config not compiled")
+    shapes = [(m, 136, 384, 1) for m in (1, 33, 65, 97, 129, 161, 225)] + [(193, 72, 128, 2)]
+    check(shapes, synth.make_custom(shapes, seed=31 + cfg), tile_config=cfg, split_mode=split,
+          label="masked row blocks")
+
+
 @pytest.mark.parametrize("idx", [2, 3, 4])
 def test_streamk_full_workloads(idx):
     shapes, groups = synth.make_workload(idx)
