@@ -142,11 +142,20 @@ __device__ __forceinline__ void load_lds16(i32x4 rsrc, uint8_t* lds_block, int v
                :: "s"(lds_addr), "v"(voffset), "s"(rsrc) : "memory", "m0");
 }
 
+// The waits are emitted with the builtin (not as asm text) so that the
+// compiler's own wait insertion knows the counters are clear afterwards; the
+// empty asm keeps memory accesses from moving across the wait.
 // Workgroup barrier without the compiler's release fence (which would wait for
 // every outstanding load): LDS reads of this wave are complete, then s_barrier.
-__device__ __forceinline__ void block_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ void block_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
 
-__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void wait_vmem_all() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  asm volatile("" ::: "memory");
+}
 
 // s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt and
 // lgkmcnt left at their maximum, i.e. not waited for).
@@ -492,6 +501,17 @@ struct GemmKernel {
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
   }
 
+  // Keeps the fragments and scales of the next substep computed before this
+  // point: without it the compiler sinks their conversion past the barrier,
+  // next to their first use, where it cannot overlap any MFMA.
+  template <int AMB>
+  __device__ __forceinline__ static void pin(const Frags& f, const Scales& s) {
+#pragma unroll
+    for (int i = 0; i < AMB; ++i) asm volatile("" ::"v"(f.a[i]), "v"(s.a[i]));
+#pragma unroll
+    for (int j = 0; j < (AMB ? NB : 0); ++j) asm volatile("" ::"v"(f.b[j]), "v"(s.b[j]));
+  }
+
   // One substep, in a scheduling region of its own: the MFMAs of `use`
   // interleaved with the dequantisation of the next substep into `fill`
   // (8 VALU per pair of fragments: 4 VALU per MFMA for 128x128 wave tiles).
@@ -536,6 +556,7 @@ struct GemmKernel {
       step<2, false, AMB>(acc, f1, f0, r0, s0);
       step<3, false, AMB>(acc, f0, f1, r0, s0);
       step<0, true, AMB>(acc, f1, f0, r1, s1);
+      pin<AMB>(f0, s1);
       // ---- second half: raw data in r1. Stage g+1 must have landed before its
       // first half is read; every wave is done with stage g's buffer here, so
       // stage g + NS can take it.
@@ -551,6 +572,7 @@ struct GemmKernel {
       step<2, false, AMB>(acc, f1, f0, r1, s1);
       step<3, false, AMB>(acc, f0, f1, r1, s1);
       step<0, true, AMB>(acc, f1, f0, r0, s0);
+      pin<AMB>(f0, s0);
     }
   }
 
