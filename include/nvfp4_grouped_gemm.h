@@ -28,7 +28,9 @@
  *
  * Work decomposition: output tiles (one of a few compiled shapes) are spread
  * over a persistent grid of one workgroup per compute unit, either whole
- * (each workgroup takes every grid-th tile) or stream-K (each workgroup takes
+ * (tiles ordered heaviest first - a group's last tile row, mostly past m,
+ * counts as lighter - and dealt out one per workgroup per round, alternately
+ * forwards and backwards) or stream-K (each workgroup takes
  * an equal share of all (tile, 128-K stage) units and stores the fp32 partial
  * sums of the tiles it shares; a second kernel, on the same stream, adds them
  * in workgroup order, so results do not depend on timing). Stream-K needs a

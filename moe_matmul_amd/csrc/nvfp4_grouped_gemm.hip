@@ -42,6 +42,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -71,27 +72,34 @@ constexpr int kBufferWord3 = 0x00020000;  // gfx9 buffer resource word 3 (raw, 3
 constexpr int kXcds = 8;                  // accelerator complex dies: workgroups go round-robin over them
 constexpr int kRasterWidth = 8;           // n-tiles per raster super-column
 
-struct GroupArgs {
-  const uint8_t* a;
+// A work class is a run of tile rows of one group: [tm0, tm0 + tiles_m). The
+// host splits a group whose last tile row is mostly past m into its full rows
+// and that lighter last row, and orders the classes by cost per tile, heaviest
+// first, so that the whole-tile walk below hands out big tiles first.
+constexpr int kMaxClasses = 2 * kMaxGroups;
+
+struct ClassArgs {
+  const uint8_t* a;  // the group's tensors and sizes
   const uint8_t* b;
   uint16_t* c;
   const uint8_t* sfa;
   const uint8_t* sfb;
   int32_t m, n, k, l;
-  int32_t tiles_m, tiles_n;
-  int32_t nk;  // 128-K stages per tile
-  int32_t pad;
+  int32_t tiles_m, tiles_n;  // tile rows of the class, tile columns of the group
+  int32_t nk;                // 128-K stages per tile
+  int32_t tm0;               // first tile row of the class within its group
 };
 
 struct KernelArgs {
-  GroupArgs g[kMaxGroups];
-  int32_t tile_prefix[kMaxGroups + 1];  // first tile of group g (tiles numbered group by group)
-  int32_t unit_prefix[kMaxGroups + 1];  // first (tile, stage) unit of group g
-  int32_t num_groups;
+  ClassArgs cls[kMaxClasses];
+  int32_t tile_prefix[kMaxClasses + 1];  // first tile of class c (tiles numbered class by class)
+  int32_t unit_prefix[kMaxClasses + 1];  // first (tile, stage) unit of class c
+  int32_t num_classes;
   int32_t split;        // 0: whole tiles strided over the grid; 1: stream-K over units
   int32_t grid;         // workgroups of the main kernel
   float* partials;      // split: two fp32 tile-sized slots per workgroup
 };
+static_assert(sizeof(KernelArgs) <= 4096, "kernel arguments must fit the kernarg segment");
 
 // 8 FP4 codes (one dword) -> 8 f16 values a * s, exact.
 __device__ __forceinline__ f16x8 dequant8(uint32_t w, _Float16 s) {
@@ -185,12 +193,12 @@ struct TileCtx {
 // A run of 128-K stages [s0, s1) of one tile, processed by one workgroup.
 struct Segment {
   int tile, s0, s1;
-  int64_t u;  // stream-K: first work unit of the segment
+  int64_t u;  // stream-K: first work unit of the segment; whole tiles: the round
   bool valid;
 };
 
-__device__ __forceinline__ int search_prefix(const int32_t* prefix, int num_groups, int64_t x) {
-  int lo = 0, hi = num_groups - 1;  // last group whose prefix entry is <= x
+__device__ __forceinline__ int search_prefix(const int32_t* prefix, int count, int64_t x) {
+  int lo = 0, hi = count - 1;  // last entry whose prefix is <= x
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (prefix[mid] <= x) lo = mid; else hi = mid - 1;
@@ -203,6 +211,8 @@ struct GemmKernel {
   static constexpr int MB = WM / 32;
   static constexpr int NB = WN / 32;
   static constexpr int WAVES_N = BN / WN;
+  static constexpr int WAVES_M = BM / WM;
+  static_assert(WAVES_M == 2, "row-block interleave assumes two wave rows");
   static constexpr int A_BYTES = BM * kRowBytes;
   static constexpr int B_BYTES = BN * kRowBytes;
   static constexpr int SF_ATOMS = (BM + BN) / 128;
@@ -239,10 +249,17 @@ struct GemmKernel {
   uint8_t* smem;
   int wave, wm, wn, h, lr, lane;
   int vwg;  // this workgroup's virtual index
+  // Row blocks are interleaved over the two wave rows: 32-row block i of wave
+  // row wm is block b = 2 i + wm of the tile (rows 32 b .. 32 b + 31), so a
+  // ragged M tail leaves both wave rows about the same number of blocks.
+  __device__ __forceinline__ static constexpr int row_block(int wm_, int i) { return i * WAVES_M + wm_; }
   // Per-lane byte offsets inside a stage of the lane's first A and B chunk for
   // half kk, and of its scale words. A row's swizzle depends only on its bits
-  // 1..3, so 32-row block i adds exactly i * 32 * kRowBytes to these.
+  // 1..3, so A block i adds exactly i * 64 * kRowBytes and B block j adds
+  // j * 32 * kRowBytes. Block b's scales sit in atom b / 4, word b % 4 of the
+  // lane's 16-byte chunk: block i of this wave adds a_scale_off(i).
   int a_base[2], b_base[2], sa_base, sb_base;
+  __device__ __forceinline__ static constexpr int a_scale_off(int i) { return (i >> 1) * 1024 + (i & 1) * 8; }
 
   // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
   // L2). The virtual index gives each XCD a contiguous run of indices, hence of
@@ -263,22 +280,23 @@ struct GemmKernel {
     vwg = blockIdx.x < (unsigned)a.grid ? virtual_wg(blockIdx.x) : 0;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      a_base[kk] = lds_off(wm * WM + lr, kk * 2 + h);
+      a_base[kk] = lds_off(row_block(wm, 0) * 32 + lr, kk * 2 + h);
       b_base[kk] = A_BYTES + lds_off(wn * WN + lr, kk * 2 + h);
     }
-    sa_base = A_BYTES + B_BYTES + ((wm * WM) >> 7) * 1024 + lr * 16 + (((wm * WM) & 127) >> 5) * 4;
+    sa_base = A_BYTES + B_BYTES + lr * 16 + row_block(wm, 0) * 4;
     sb_base = A_BYTES + B_BYTES + (BM / 128 + ((wn * WN) >> 7)) * 1024 + lr * 16 + (((wn * WN) & 127) >> 5) * 4;
   }
 
   // ---------------- work decomposition ----------------
-  // Tiles are numbered group by group, M-fastest inside a group (the raster of
-  // the persistent scheduler in submission 506336). A unit is one 128-K stage of
-  // one tile; units are numbered tile by tile.
+  // Tiles are numbered class by class (the persistent scheduler of submission
+  // 506336 numbers them group by group; here a group may be two classes, and
+  // heavier classes come first). A unit is one 128-K stage of one tile; units
+  // are numbered tile by tile.
   __device__ __forceinline__ int group_of_tile(int tile) const {
-    return search_prefix(args.tile_prefix, args.num_groups, tile);
+    return search_prefix(args.tile_prefix, args.num_classes, tile);
   }
-  __device__ __forceinline__ int total_tiles() const { return args.tile_prefix[args.num_groups]; }
-  __device__ __forceinline__ int64_t total_units() const { return args.unit_prefix[args.num_groups]; }
+  __device__ __forceinline__ int total_tiles() const { return args.tile_prefix[args.num_classes]; }
+  __device__ __forceinline__ int64_t total_units() const { return args.unit_prefix[args.num_classes]; }
   __device__ __forceinline__ int64_t unit_begin(int wg) const { return (int64_t)wg * total_units() / args.grid; }
   // the workgroup whose unit range holds unit u
   __device__ __forceinline__ int owner_of_unit(int64_t u) const {
@@ -286,11 +304,11 @@ struct GemmKernel {
   }
   __device__ __forceinline__ int64_t first_unit_of_tile(int tile) const {
     const int g = group_of_tile(tile);
-    return args.unit_prefix[g] + (int64_t)(tile - args.tile_prefix[g]) * args.g[g].nk;
+    return args.unit_prefix[g] + (int64_t)(tile - args.tile_prefix[g]) * args.cls[g].nk;
   }
   __device__ __forceinline__ int tile_of_unit(int64_t u, int* stage) const {
-    const int g = search_prefix(args.unit_prefix, args.num_groups, u);
-    const int nk = args.g[g].nk;
+    const int g = search_prefix(args.unit_prefix, args.num_classes, u);
+    const int nk = args.cls[g].nk;
     const int local = (int)(u - args.unit_prefix[g]);
     *stage = local % nk;
     return args.tile_prefix[g] + local / nk;
@@ -302,7 +320,7 @@ struct GemmKernel {
     if (!s.valid) return;
     int stage;
     s.tile = tile_of_unit(u, &stage);
-    const int nk = args.g[group_of_tile(s.tile)].nk;
+    const int nk = args.cls[group_of_tile(s.tile)].nk;
     s.s0 = stage;
     s.s1 = (int)min((int64_t)nk, stage + (u_end - u));
   }
@@ -311,10 +329,11 @@ struct GemmKernel {
     if (args.split) {
       locate(s, unit_begin(vwg), unit_begin(vwg + 1));
     } else {
+      s.u = 0;
       s.tile = vwg;
       s.valid = s.tile < total_tiles();
       s.s0 = 0;
-      s.s1 = s.valid ? args.g[group_of_tile(s.tile)].nk : 0;
+      s.s1 = s.valid ? args.cls[group_of_tile(s.tile)].nk : 0;
     }
   }
 
@@ -322,16 +341,21 @@ struct GemmKernel {
     if (args.split) {
       locate(s, s.u + (s.s1 - s.s0), unit_begin(vwg + 1));
     } else {
-      s.tile += args.grid;
+      // Round r hands tiles [r grid, (r + 1) grid) out forwards when r is
+      // even and backwards when r is odd: tiles come heaviest first, so the
+      // workgroups that drew the lightest tiles of one round draw the
+      // heaviest of the next.
+      const int r = (int)++s.u;
+      s.tile = r * args.grid + ((r & 1) ? args.grid - 1 - vwg : vwg);
       s.valid = s.tile < total_tiles();
       s.s0 = 0;
-      s.s1 = s.valid ? args.g[group_of_tile(s.tile)].nk : 0;
+      s.s1 = s.valid ? args.cls[group_of_tile(s.tile)].nk : 0;
     }
   }
 
   __device__ __forceinline__ TileCtx setup(int tile) const {
     const int gi = group_of_tile(tile);
-    const GroupArgs& G = args.g[gi];
+    const ClassArgs& G = args.cls[gi];
     const int M = G.m, N = G.n, K = G.k;
     const int tiles_m = G.tiles_m;
     const int per_l = tiles_m * G.tiles_n;
@@ -346,7 +370,7 @@ struct GemmKernel {
     const int sc = r2 / (tiles_m * kRasterWidth);
     const int in_sc = r2 - sc * tiles_m * kRasterWidth;
     const int width = min(kRasterWidth, tiles_n - sc * kRasterWidth);
-    const int tm = in_sc / width;
+    const int tm = G.tm0 + in_sc / width;
     const int tn = sc * kRasterWidth + in_sc % width;
     const int kbytes = K >> 1;
     const int Kt = K >> 6;
@@ -459,14 +483,13 @@ struct GemmKernel {
     const uint8_t* St = smem + buf * STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < AMB; ++i)
-      r.a[i] = *reinterpret_cast<const u32x4*>(St + a_base[kk] + i * 32 * kRowBytes);
+      r.a[i] = *reinterpret_cast<const u32x4*>(St + a_base[kk] + i * WAVES_M * 32 * kRowBytes);
 #pragma unroll
     for (int j = 0; j < NB; ++j)
       r.b[j] = *reinterpret_cast<const u32x4*>(St + b_base[kk] + j * 32 * kRowBytes);
-    const ScaleVec<MB> sa = *reinterpret_cast<const ScaleVec<MB>*>(St + sa_base + kk * 512);
     const ScaleVec<NB> sb = *reinterpret_cast<const ScaleVec<NB>*>(St + sb_base + kk * 512);
 #pragma unroll
-    for (int i = 0; i < AMB; ++i) r.sa[i] = sa[i];
+    for (int i = 0; i < AMB; ++i) r.sa[i] = *reinterpret_cast<const uint32_t*>(St + sa_base + kk * 512 + a_scale_off(i));
 #pragma unroll
     for (int j = 0; j < NB; ++j) r.sb[j] = sb[j];
   }
@@ -579,8 +602,9 @@ struct GemmKernel {
   // Dispatch on this wave's active 32-row blocks (rows below m).
   __device__ __forceinline__ void mainloop_rows(f32x16 (&acc)[MB][NB], const TileCtx& t, int n, int g0,
                                                 Loader& ld) const {
-    const int rows = t.M - (t.row0 + wm * WM);
-    const int amb = rows <= 0 ? 0 : (rows >= WM ? MB : (rows + 31) / 32);
+    const int rows = t.M - t.row0;
+    const int nb = rows <= 0 ? 0 : (rows + 31) >> 5;  // row blocks of the tile below m
+    const int amb = nb <= wm ? 0 : min(MB, (nb - wm + 1) >> 1);
     static_assert(MB <= 4, "active-block dispatch covers MB <= 4");
     switch (amb) {
       case 0: mainloop<0>(acc, n, g0, ld); break;
@@ -594,11 +618,10 @@ struct GemmKernel {
   // ---------------- output ----------------
   // fp32 -> fp16 (RNE), 8-byte stores masked to m and n.
   __device__ __forceinline__ void epilogue(const f32x16 (&acc)[MB][NB], const TileCtx& t) const {
-    const int row0 = t.row0 + wm * WM;
     const int col0 = t.col0 + wn * WN;
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
-      const int row = row0 + i * 32 + lr;
+      const int row = t.row0 + row_block(wm, i) * 32 + lr;
       if (row < t.M) {
         uint16_t* crow = t.c + (size_t)row * t.N;
 #pragma unroll
@@ -648,8 +671,8 @@ struct GemmKernel {
     for (int i = 0; i < MB; ++i)
 #pragma unroll
       for (int j = 0; j < NB; ++j) zero[i][j] = f32x16{};
-    for (int gi = 0; gi < args.num_groups; ++gi) {
-      if (args.g[gi].nk != 0) continue;
+    for (int gi = 0; gi < args.num_classes; ++gi) {
+      if (args.cls[gi].nk != 0) continue;
       for (int tile = args.tile_prefix[gi] + vwg; tile < args.tile_prefix[gi + 1]; tile += args.grid)
         epilogue(zero, setup(tile));
     }
@@ -726,7 +749,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_streamk_reduce_kernel(KernelAr
   const int tile = k.tile_of_unit(ub, &stage);
   if (stage == 0) return;  // the boundary falls between tiles: nothing split here
   const int64_t u_first = ub - stage;
-  const int nk = args.g[k.group_of_tile(tile)].nk;
+  const int nk = args.cls[k.group_of_tile(tile)].nk;
   const int c_first = k.owner_of_unit(u_first);
   const int c_last = k.owner_of_unit(u_first + nk - 1);
   if (boundary != c_first + 1) return;  // another boundary of this tile does the work
@@ -766,7 +789,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_streamk_reduce_kernel(KernelAr
     rest /= K::NB;
     const int i = rest % K::MB;
     const int wv = rest / K::MB;
-    const int row = t.row0 + (wv / K::WAVES_N) * WM + i * 32 + (ln & 31);
+    const int row = t.row0 + K::row_block(wv / K::WAVES_N, i) * 32 + (ln & 31);
     const int col = t.col0 + (wv % K::WAVES_N) * WN + j * 32 + q * 8 + (ln >> 5) * 4;
     if (row < t.M && col < t.N) {
       const f16x4 o = {(_Float16)sum[x][0], (_Float16)sum[x][1], (_Float16)sum[x][2], (_Float16)sum[x][3]};
@@ -842,6 +865,57 @@ int group_stages(const int32_t* ps, int g) { return (int)ceil_div64(ps[4 * g + 2
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Largest number of 32-row blocks a wave computes in a tile with `rows` rows
+// below m (row blocks alternate between the two wave rows).
+int max_active_blocks(int64_t rows, int bm) {
+  const int64_t nb = std::min<int64_t>(rows, bm) <= 0 ? 0 : (std::min<int64_t>(rows, bm) + 31) / 32;
+  return (int)((nb + 1) / 2);
+}
+
+// Share of a full stage's time that a tile stage with `amb` of `mb` active
+// blocks per wave takes: the loads, barrier and B dequantisation do not shrink
+// with m.
+double stage_fraction(int amb, int mb) {
+  const double fixed = 0.25;
+  return fixed + (1.0 - fixed) * (double)amb / (double)mb;
+}
+
+struct WorkClass {
+  int g;          // group
+  int tm0;        // first tile row
+  int tiles_m;    // tile rows
+  int64_t tiles;  // tiles_m * tiles_n * l
+  int nk;         // stages per tile
+  double cost;    // modelled time per tile, in full tile-stages
+};
+
+// The work classes of a call for tile configuration cfg, heaviest per tile
+// first (stable: groups keep their order among equals). Returns the count.
+double tile_overhead_stages() { return 1.5; }  // epilogue and pipeline fill per tile
+
+int build_classes(const int32_t* ps, int G, int cfg, WorkClass* out) {
+  const TileConfig& tc = kConfigs[cfg];
+  const int mb = tc.wm / 32;
+  int n = 0;
+  for (int g = 0; g < G; ++g) {
+    const int64_t m = ps[4 * g + 0], nn = ps[4 * g + 1], l = ps[4 * g + 3];
+    if (m == 0 || nn == 0) continue;
+    const int tiles_m = (int)ceil_div64(m, tc.bm);
+    const int64_t tiles_n = ceil_div64(nn, tc.bn);
+    const int nk = group_stages(ps, g);
+    const int tail_amb = max_active_blocks(m - (int64_t)(tiles_m - 1) * tc.bm, tc.bm);
+    const bool split_tail = tiles_m > 1 && tail_amb < mb;
+    const int body_rows = split_tail ? tiles_m - 1 : tiles_m;
+    const int body_amb = tiles_m == 1 ? tail_amb : mb;  // a one-row group is all tail
+    out[n++] = WorkClass{g, 0, body_rows, body_rows * tiles_n * l, nk,
+                         nk * stage_fraction(body_amb, mb) + tile_overhead_stages()};
+    if (split_tail)
+      out[n++] = WorkClass{g, tiles_m - 1, 1, tiles_n * l, nk, nk * stage_fraction(tail_amb, mb) + tile_overhead_stages()};
+  }
+  std::stable_sort(out, out + n, [](const WorkClass& x, const WorkClass& y) { return x.cost > y.cost; });
+  return n;
+}
+
 size_t workspace_bytes_for(int cfg, int grid) {
   return (size_t)grid * 2 * kConfigs[cfg].bm * kConfigs[cfg].bn * 4;
 }
@@ -862,7 +936,7 @@ Plan plan_for(const int32_t* ps, int G, int cus, int cfg, int split) {
   p.cfg = cfg;
   p.split = split;
   const double unit = tile_unit(cfg);
-  const double tile_overhead = 1.5;  // stages' worth of epilogue and pipeline fill per tile
+  const double tile_overhead = tile_overhead_stages();
   int64_t tiles = 0, units = 0;
   for (int g = 0; g < G; ++g) {
     tiles += group_tiles(ps, g, cfg);
@@ -872,16 +946,19 @@ Plan plan_for(const int32_t* ps, int G, int cus, int cfg, int split) {
   p.units = units;
   if (!split) {
     p.grid = (int)(tiles < cus ? tiles : cus);
-    // strided assignment of whole tiles
+    // the kernel's walk: rounds of `grid` tiles, heaviest class first,
+    // alternately forwards and backwards over the workgroups
     static thread_local double load[1024];
     const int ns = p.grid < 1024 ? (p.grid > 0 ? p.grid : 1) : 1024;
     for (int s = 0; s < ns; ++s) load[s] = 0.0;
+    WorkClass cls[kMaxClasses];
+    const int nc = build_classes(ps, G, cfg, cls);
     int64_t t = 0;
-    for (int g = 0; g < G; ++g) {
-      const int64_t nt = group_tiles(ps, g, cfg);
-      const double work = unit * (group_stages(ps, g) + tile_overhead);
-      for (int64_t i = 0; i < nt; ++i, ++t) load[t % ns] += work;
-    }
+    for (int c = 0; c < nc; ++c)
+      for (int64_t i = 0; i < cls[c].tiles; ++i, ++t) {
+        const int64_t r = t / ns, pos = t % ns;
+        load[(r & 1) ? ns - 1 - pos : pos] += unit * cls[c].cost;
+      }
     double mx = 0.0;
     for (int s = 0; s < ns; ++s) mx = load[s] > mx ? load[s] : mx;
     p.cost = mx;
@@ -972,31 +1049,35 @@ int launch(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, vo
   const TileConfig& tc = kConfigs[plan.cfg];
   KernelArgs args;
   std::memset(&args, 0, sizeof(args));
+  WorkClass cls[kMaxClasses];
+  const int nc = build_classes(ps, G, plan.cfg, cls);
   int64_t tiles = 0, units = 0;
-  for (int g = 0; g < G; ++g) {
-    GroupArgs& ga = args.g[g];
-    ga.m = ps[4 * g + 0];
-    ga.n = ps[4 * g + 1];
-    ga.k = ps[4 * g + 2];
-    ga.l = ps[4 * g + 3];
-    ga.a = reinterpret_cast<const uint8_t*>(abc[3 * g + 0]);
-    ga.b = reinterpret_cast<const uint8_t*>(abc[3 * g + 1]);
-    ga.c = reinterpret_cast<uint16_t*>(abc[3 * g + 2]);
-    ga.sfa = reinterpret_cast<const uint8_t*>(sf[2 * g + 0]);
-    ga.sfb = reinterpret_cast<const uint8_t*>(sf[2 * g + 1]);
-    ga.tiles_m = (int32_t)ceil_div64(ga.m, tc.bm);
-    ga.tiles_n = (int32_t)ceil_div64(ga.n, tc.bn);
-    ga.nk = group_stages(ps, g);
-    args.tile_prefix[g] = (int32_t)tiles;
-    args.unit_prefix[g] = (int32_t)units;
-    tiles += group_tiles(ps, g, plan.cfg);
-    units += group_tiles(ps, g, plan.cfg) * ga.nk;
+  for (int c = 0; c < nc; ++c) {
+    const int g = cls[c].g;
+    ClassArgs& ca = args.cls[c];
+    ca.m = ps[4 * g + 0];
+    ca.n = ps[4 * g + 1];
+    ca.k = ps[4 * g + 2];
+    ca.l = ps[4 * g + 3];
+    ca.a = reinterpret_cast<const uint8_t*>(abc[3 * g + 0]);
+    ca.b = reinterpret_cast<const uint8_t*>(abc[3 * g + 1]);
+    ca.c = reinterpret_cast<uint16_t*>(abc[3 * g + 2]);
+    ca.sfa = reinterpret_cast<const uint8_t*>(sf[2 * g + 0]);
+    ca.sfb = reinterpret_cast<const uint8_t*>(sf[2 * g + 1]);
+    ca.tiles_m = cls[c].tiles_m;
+    ca.tiles_n = (int32_t)ceil_div64(ca.n, tc.bn);
+    ca.nk = cls[c].nk;
+    ca.tm0 = cls[c].tm0;
+    args.tile_prefix[c] = (int32_t)tiles;
+    args.unit_prefix[c] = (int32_t)units;
+    tiles += cls[c].tiles;
+    units += cls[c].tiles * ca.nk;
   }
-  for (int g = G; g <= kMaxGroups; ++g) {
-    args.tile_prefix[g] = (int32_t)tiles;
-    args.unit_prefix[g] = (int32_t)units;
+  for (int c = nc; c <= kMaxClasses; ++c) {
+    args.tile_prefix[c] = (int32_t)tiles;
+    args.unit_prefix[c] = (int32_t)units;
   }
-  args.num_groups = G;
+  args.num_classes = nc > 0 ? nc : 1;
   args.split = plan.split;
   args.grid = plan.grid;
   if (plan.split) args.partials = reinterpret_cast<float*>(workspace);

@@ -115,8 +115,9 @@ def test_every_tile_config(cfg, split):
 @pytest.mark.parametrize("split", [0, 1])
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3])
 def test_masked_row_blocks(cfg, split):
-    """M tails that leave each wave 0, 1, 2, 3 or 4 active 32-row blocks, in the
-    first and second wave row of a tile (waves skip blocks wholly past m)."""
+    """M tails that leave each wave 0 .. 4 active 32-row blocks in both wave rows
+    (row blocks alternate between the wave rows; blocks wholly past m are
+    skipped), and groups split into a full-row class and a lighter tail class."""
     if cfg >= mm.nvfp4_num_tile_configs():
         pytest.skip("config not compiled")
     shapes = [(m, 136, 384, 1) for m in (1, 33, 65, 97, 129, 161, 225)] + [(193, 72, 128, 2)]
