@@ -141,11 +141,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_buffer(const void* base, 
 // lds_block + 16 * lane (M0 holds the wave's LDS base). Issued as inline asm so
 // the compiler does not treat it as an LDS write it must wait for: the kernel
 // tracks these loads itself with exact vmcnt waits.
-__device__ __forceinline__ void load_lds16(i32x4 rsrc, uint8_t* lds_block, int voffset) {
-  // every operand but the offset is wave-uniform; say so, so they stay in SGPRs
-  rsrc = i32x4{__builtin_amdgcn_readfirstlane(rsrc[0]), __builtin_amdgcn_readfirstlane(rsrc[1]),
-               __builtin_amdgcn_readfirstlane(rsrc[2]), __builtin_amdgcn_readfirstlane(rsrc[3])};
-  const uint32_t lds_addr = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds_block));
+__device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t lds_block, int voffset) {
+  // the resource and the LDS address are wave-uniform (the caller passes rsrc
+  // through readfirstlane); say so, so they stay in SGPRs
+  const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(lds_block);
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(lds_addr), "v"(voffset), "s"(rsrc) : "memory", "m0");
 }
@@ -223,10 +222,13 @@ struct GemmKernel {
   static_assert((BM / WM) * (BN / WN) == kThreads / 64, "four waves per workgroup");
   static_assert(WM <= 128 && WN <= 128 && 128 % WM == 0 && 128 % WN == 0, "wave tile inside one scale atom");
   static_assert(A_INSTR >= 1 && B_INSTR >= 1 && SF_ATOMS <= 4, "tile shape");
-  static_assert(NS >= 2 && NS <= 4 && NS * STAGE_BYTES <= 160 * 1024, "LDS stages");
-  // direct loads one wave issues per stage (without / with a scale atom row)
-  static constexpr int L0 = A_INSTR + B_INSTR;
-  static constexpr int L1 = A_INSTR + B_INSTR + 1;
+  // Direct loads every wave issues per stage: its A and B rows and one scale
+  // atom row (waves past the last atom row load nothing into a 1 KiB dummy).
+  static constexpr int L = A_INSTR + B_INSTR + 1;
+  static constexpr int DUMMY_OFF = NS * STAGE_BYTES;
+  static constexpr int LDS_BYTES = NS * STAGE_BYTES + 1024;
+  static_assert(NS >= 3 && NS <= 4 && LDS_BYTES <= 160 * 1024, "LDS stages");
+  static_assert((NS - 2) * L < 64, "vmcnt range");
 
   // Packed FP4 of one 64-K half stage for this lane (one 16-byte chunk per 32-row
   // block) and the lane's two E4M3 scales per block.
@@ -404,27 +406,7 @@ struct GemmKernel {
 
   // ---------------- operand staging ----------------
   // Direct loads of stage kt (A, B and the scale atoms) into LDS buffer buf.
-  __device__ __forceinline__ void issue_stage(const TileCtx& t, int kt, int buf) const {
-    uint8_t* st = smem + buf * STAGE_BYTES;
-    // Lane -> (row, chunk) of its 16 bytes in a 1 KiB direct load: 16 rows of 64
-    // bytes; the physical chunk is lane & 3, the global chunk undoes the swizzle.
-    const int voff = (wave * 16 + (lane >> 2)) * t.kbytes + (((lane & 3) ^ swz(lane >> 2)) << 4);
-    // the K offset goes into the resource base, so the range check also
-    // zero-fills past the end of the last row
-    const int64_t kb0 = (int64_t)kt * kRowBytes;
-    const i32x4 ra = make_rsrc(t.a_tile + kb0, t.a_rem - kb0);
-    const i32x4 rb = make_rsrc(t.b_tile + kb0, t.b_rem - kb0);
-#pragma unroll
-    for (int u = 0; u < A_INSTR; ++u) load_lds16(ra, st + (u * 4 + wave) * 1024, voff + u * 64 * t.kbytes);
-#pragma unroll
-    for (int u = 0; u < B_INSTR; ++u)
-      load_lds16(rb, st + A_BYTES + (u * 4 + wave) * 1024, voff + u * 64 * t.kbytes);
-    if (wave < SF_ATOMS) {
-      // two 64-K groups (1 KiB) of this atom row; groups past k read 0
-      const int64_t q0 = (int64_t)kt * 2 * kAtomBytes;
-      load_lds16(make_rsrc(t.sf_row + q0, t.sf_rem - q0), st + A_BYTES + B_BYTES + wave * 1024, lane * 16);
-    }
-  }
+
 
   // The loader walks the workgroup's segments ahead of the compute. Global stage
   // X (counted over all segments) lives in LDS buffer X % NS.
@@ -449,25 +431,80 @@ struct GemmKernel {
     loader_skip_empty(ld);
   }
 
-  __device__ __forceinline__ void issue_next(Loader& ld) const {
-    issue_stage(ld.ctx, ld.stage, ld.issued % NS);
+  // Resources and LDS targets of one stage's direct loads; the loads are
+  // issued one by one (dma<U>) between the MFMAs of the next half stage.
+  struct StageIssue {
+    i32x4 ra, rb, rs;  // A, B and scale resources (0 bytes: the loads write zeros)
+    uint32_t st;       // LDS address of the stage buffer
+    uint32_t sdst;     // LDS address of this wave's scale atom row (or the dummy)
+    int voff;          // lane offset of its 16 bytes inside a 1 KiB A or B load
+    int ustride;       // bytes between a wave's consecutive A or B loads (64 rows)
+  };
+
+  __device__ __forceinline__ static i32x4 uniform(i32x4 r) {
+    return i32x4{__builtin_amdgcn_readfirstlane(r[0]), __builtin_amdgcn_readfirstlane(r[1]),
+                 __builtin_amdgcn_readfirstlane(r[2]), __builtin_amdgcn_readfirstlane(r[3])};
+  }
+
+  // The loads of the loader's next stage into buffer issued % NS. With no
+  // stage left they read 0 bytes and write zeros into that buffer, which
+  // every wave has finished reading (it held stage issued - NS).
+  __device__ __forceinline__ StageIssue prep_issue(const Loader& ld) const {
+    const TileCtx& t = ld.ctx;
+    StageIssue si;
+    const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(smem);
+    si.st = lds0 + (uint32_t)((ld.issued % NS) * STAGE_BYTES);
+    // Lane -> (row, chunk) of its 16 bytes in a 1 KiB direct load: 16 rows of 64
+    // bytes; the physical chunk is lane & 3, the global chunk undoes the swizzle.
+    si.voff = (wave * 16 + (lane >> 2)) * t.kbytes + (((lane & 3) ^ swz(lane >> 2)) << 4);
+    si.ustride = 64 * t.kbytes;
+    // the K offset goes into the resource base, so the range check also
+    // zero-fills past the end of the last row
+    const bool live = ld.seg.valid;
+    const int64_t kb0 = (int64_t)ld.stage * kRowBytes;
+    si.ra = uniform(make_rsrc(t.a_tile + kb0, live ? t.a_rem - kb0 : 0));
+    si.rb = uniform(make_rsrc(t.b_tile + kb0, live ? t.b_rem - kb0 : 0));
+    // two 64-K groups (1 KiB) of this wave's atom row; groups past k read 0
+    const int64_t q0 = (int64_t)ld.stage * 2 * kAtomBytes;
+    const bool has_sf = wave < SF_ATOMS;
+    si.rs = uniform(make_rsrc(t.sf_row + q0, live && has_sf ? t.sf_rem - q0 : 0));
+    si.sdst = has_sf ? si.st + A_BYTES + B_BYTES + wave * 1024 : lds0 + DUMMY_OFF;
+    return si;
+  }
+
+  template <int U>
+  __device__ __forceinline__ void dma(const StageIssue& si) const {
+    if constexpr (U < A_INSTR) {
+      load_lds16(si.ra, si.st + (U * 4 + wave) * 1024, si.voff + U * si.ustride);
+    } else if constexpr (U < A_INSTR + B_INSTR) {
+      constexpr int V = U - A_INSTR;
+      load_lds16(si.rb, si.st + A_BYTES + (V * 4 + wave) * 1024, si.voff + V * si.ustride);
+    } else {
+      load_lds16(si.rs, si.sdst, lane * 16);
+    }
+  }
+
+  template <int U0, int U1>
+  __device__ __forceinline__ void dma_range(const StageIssue& si) const {
+    if constexpr (U0 < U1) {
+      dma<U0>(si);
+      dma_range<U0 + 1, U1>(si);
+    }
+  }
+
+  // After a stage was issued: the loader moves to its next stage.
+  __device__ __forceinline__ void advance(Loader& ld) const {
     ++ld.issued;
-    if (++ld.stage == ld.seg.s1) {
+    if (ld.seg.valid && ++ld.stage == ld.seg.s1) {
       next_segment(ld.seg);
       loader_skip_empty(ld);
     }
   }
 
-  // Wait until at most `stages` stages of this wave's loads are outstanding.
-  __device__ __forceinline__ void wait_stages(int stages) const {
-    const int n = stages * (wave < SF_ATOMS ? L1 : L0);
-    switch (n) {
-      case L0: wait_vmem<L0>(); break;
-      case L1: wait_vmem<L1>(); break;
-      case 2 * L0: wait_vmem<2 * L0>(); break;
-      case 2 * L1: wait_vmem<2 * L1>(); break;
-      default: wait_vmem<0>(); break;
-    }
+  __device__ __forceinline__ void issue_all(Loader& ld) const {
+    const StageIssue si = prep_issue(ld);
+    dma_range<0, L>(si);
+    advance(ld);
   }
 
   // ---------------- dequantisation and MFMA ----------------
@@ -539,9 +576,17 @@ struct GemmKernel {
   // interleaved with the dequantisation of the next substep into `fill`
   // (8 VALU per pair of fragments: 4 VALU per MFMA for 128x128 wave tiles).
   // With CONVERT, the next half's scales are converted here as well.
-  template <int NEXT_S, bool CONVERT, int AMB>
+  // Direct loads U0 .. U1-1 of the next stage go first, in a region of their
+  // own, so each step hands the memory pipeline a few loads while its MFMAs
+  // run (issued all at once, a stage's loads stall every wave behind the
+  // address unit).
+  template <int NEXT_S, bool CONVERT, int AMB, int U0 = 0, int U1 = 0>
   __device__ __forceinline__ void step(f32x16 (&acc)[MB][NB], const Frags& use, Frags& fill, const Raw& src,
-                                       Scales& ssrc) const {
+                                       Scales& ssrc, const StageIssue* si = nullptr) const {
+    if constexpr (U0 < U1) {
+      dma_range<U0, U1>(*si);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     if (AMB == 0) return;
     constexpr int VALU = (AMB + NB) * 8 + (CONVERT ? 2 * (AMB + NB) : 0);
     constexpr int PER = (VALU + AMB * NB - 1) / (AMB * NB > 0 ? AMB * NB : 1);
@@ -556,17 +601,19 @@ struct GemmKernel {
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // n stages of one segment, whose first stage is global stage g0. On entry
-  // the loader has issued at least stage g0.
+  // n stages of one segment, whose first stage is global stage g0. Every
+  // iteration issues exactly one stage (L loads per wave), so on entry stages
+  // up to g0 + NS - 1 are issued, and at the mid-stage wait of stage g the
+  // stages after g + 1 are exactly NS - 2.
   template <int AMB>
   __device__ __forceinline__ void mainloop(f32x16 (&acc)[MB][NB], int n, int g0, Loader& ld) const {
+    // split of a stage's L loads over the four steps of a half stage
+    constexpr int U1 = (L + 3) / 4, U2 = U1 + (L - U1 + 2) / 3, U3 = U2 + (L - U2 + 1) / 2;
     Raw r0, r1;
     Scales s0, s1;
     Frags f0, f1;
     wait_vmem_all();  // stage g0 landed (and earlier C or partial stores are done)
     block_sync();
-    // top up: every buffer of a stage before g0 is free now
-    while (ld.seg.valid && ld.issued < g0 + NS) issue_next(ld);
     read_half<AMB>(r0, g0 % NS, 0);
     convert_scales<AMB>(s0, r0);
     dequant<0, AMB>(f0, r0, s0);
@@ -574,7 +621,7 @@ struct GemmKernel {
       const int g = g0 + kt;
       // ---- first half (K 0..63 of the stage): raw data in r0 ----
       read_half<AMB>(r1, g % NS, 1);
-      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, AMB + NB + 2, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, AMB + NB + 1 + (AMB + 1) / 2, 0);
       step<1, false, AMB>(acc, f0, f1, r0, s0);
       step<2, false, AMB>(acc, f1, f0, r0, s0);
       step<3, false, AMB>(acc, f0, f1, r0, s0);
@@ -583,19 +630,17 @@ struct GemmKernel {
       // ---- second half: raw data in r1. Stage g+1 must have landed before its
       // first half is read; every wave is done with stage g's buffer here, so
       // stage g + NS can take it.
-      if (kt + 1 < n) {
-        const int after = ld.issued - (g + 2);  // stages issued after g+1
-        wait_stages(after < 0 ? 0 : after);
-      }
+      wait_vmem<(NS - 2) * L>();
       block_sync();
-      if (ld.seg.valid && ld.issued <= g + NS) issue_next(ld);
+      const StageIssue si = prep_issue(ld);
       read_half<AMB>(r0, (g + 1) % NS, 0);  // unused after the last stage
-      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, AMB + NB + 2, 0);
-      step<1, false, AMB>(acc, f0, f1, r1, s1);
-      step<2, false, AMB>(acc, f1, f0, r1, s1);
-      step<3, false, AMB>(acc, f0, f1, r1, s1);
-      step<0, true, AMB>(acc, f1, f0, r0, s0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, AMB + NB + 1 + (AMB + 1) / 2, 0);
+      step<1, false, AMB, 0, U1>(acc, f0, f1, r1, s1, &si);
+      step<2, false, AMB, U1, U2>(acc, f1, f0, r1, s1, &si);
+      step<3, false, AMB, U2, U3>(acc, f0, f1, r1, s1, &si);
+      step<0, true, AMB, U3, L>(acc, f1, f0, r0, s0, &si);
       pin<AMB>(f0, s0);
+      advance(ld);
     }
   }
 
@@ -681,7 +726,7 @@ struct GemmKernel {
   __device__ __forceinline__ void run() const {
     Loader ld;
     loader_init(ld);
-    while (ld.seg.valid && ld.issued < NS) issue_next(ld);  // every buffer is free
+    for (int b = 0; b < NS; ++b) issue_all(ld);  // every buffer is free
     Segment seg;
     first_segment(seg);
     bool first_seg = true;
@@ -702,12 +747,10 @@ struct GemmKernel {
       next_segment(seg);
     }
     if (args.split) zero_k_tiles();
+    wait_vmem_all();  // no direct load may still be writing LDS when the workgroup ends
   }
 };
 
-// Stage layout in LDS (bytes): [A: BM rows x 64][B: BN rows x 64]
-// [scale atoms: (BM + BN) / 128 atom rows x 2 k-groups x 512]; A and B rows are
-// swizzled by lds_off, the scale atoms are stored as in global memory.
 // The kernels' single argument, read in place from the kernarg segment (where
 // it starts at offset 0). Binding the by-value parameter to a reference makes
 // the compiler keep a private copy of it once the argument has many readers;
@@ -716,10 +759,13 @@ __device__ __forceinline__ const KernelArgs& kernel_args() {
   return *(const KernelArgs*)__builtin_amdgcn_kernarg_segment_ptr();
 }
 
+// Stage layout in LDS (bytes): [A: BM rows x 64][B: BN rows x 64]
+// [scale atoms: (BM + BN) / 128 atom rows x 2 k-groups x 512]; A and B rows are
+// swizzled by lds_off, the scale atoms are stored as in global memory.
 template <int BM, int BN, int WM, int WN, int NS>
 __global__ __launch_bounds__(kThreads, 1) void nvfp4_grouped_gemm_kernel(KernelArgs) {
   using K = GemmKernel<BM, BN, WM, WN, NS>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * K::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[K::LDS_BYTES];
   const K k(kernel_args(), smem);
   k.run();
 }
