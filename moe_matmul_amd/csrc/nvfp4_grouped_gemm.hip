@@ -235,7 +235,7 @@ struct GemmKernel {
   struct Raw {
     u32x4 a[MB];
     u32x4 b[NB];
-    uint32_t sa[MB];
+    u32x4 sa[(MB + 1) / 2];  // whole scale chunks; this wave's words are picked at conversion
     uint32_t sb[NB];
   };
   struct Scales {
@@ -256,12 +256,17 @@ struct GemmKernel {
   // ragged M tail leaves both wave rows about the same number of blocks.
   __device__ __forceinline__ static constexpr int row_block(int wm_, int i) { return i * WAVES_M + wm_; }
   // Per-lane byte offsets inside a stage of the lane's first A and B chunk for
-  // half kk, and of its scale words. A row's swizzle depends only on its bits
-  // 1..3, so A block i adds exactly i * 64 * kRowBytes and B block j adds
-  // j * 32 * kRowBytes. Block b's scales sit in atom b / 4, word b % 4 of the
-  // lane's 16-byte chunk: block i of this wave adds a_scale_off(i).
+  // half kk, and of its 16-byte scale chunks. A row's swizzle depends only on
+  // its bits 1..3, so A block i adds exactly i * 64 * kRowBytes and B block j
+  // adds j * 32 * kRowBytes. Block b's scales sit in atom b / 4, word b % 4 of
+  // the lane's chunk, so this wave's block i is word 2 (i & 1) + wm of the
+  // chunk of atom i / 2 (whole chunks are read: 16-byte lane strides are
+  // bank-conflict free, 4-byte reads at that stride are not).
   int a_base[2], b_base[2], sa_base, sb_base;
-  __device__ __forceinline__ static constexpr int a_scale_off(int i) { return (i >> 1) * 1024 + (i & 1) * 8; }
+  // v_perm_b32 selector that moves this lane's two A scale bytes (16-blocks
+  // 2h, 2h+1) of the word of wave row wm (the second source holds the word of
+  // row 0, the first that of row 1) into the low half of the result.
+  uint32_t sa_sel;
 
   // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
   // L2). The virtual index gives each XCD a contiguous run of indices, hence of
@@ -285,8 +290,9 @@ struct GemmKernel {
       a_base[kk] = lds_off(row_block(wm, 0) * 32 + lr, kk * 2 + h);
       b_base[kk] = A_BYTES + lds_off(wn * WN + lr, kk * 2 + h);
     }
-    sa_base = A_BYTES + B_BYTES + lr * 16 + row_block(wm, 0) * 4;
+    sa_base = A_BYTES + B_BYTES + lr * 16;
     sb_base = A_BYTES + B_BYTES + (BM / 128 + ((wn * WN) >> 7)) * 1024 + lr * 16 + (((wn * WN) & 127) >> 5) * 4;
+    sa_sel = (uint32_t)(wm * 4 + 2 * h) | ((uint32_t)(wm * 4 + 2 * h + 1) << 8) | 0x0C0C0000u;
   }
 
   // ---------------- work decomposition ----------------
@@ -526,7 +532,8 @@ struct GemmKernel {
       r.b[j] = *reinterpret_cast<const u32x4*>(St + b_base[kk] + j * 32 * kRowBytes);
     const ScaleVec<NB> sb = *reinterpret_cast<const ScaleVec<NB>*>(St + sb_base + kk * 512);
 #pragma unroll
-    for (int i = 0; i < AMB; ++i) r.sa[i] = *reinterpret_cast<const uint32_t*>(St + sa_base + kk * 512 + a_scale_off(i));
+    for (int a = 0; a < (AMB + 1) / 2; ++a)
+      r.sa[a] = *reinterpret_cast<const u32x4*>(St + sa_base + a * 1024 + kk * 512);
 #pragma unroll
     for (int j = 0; j < NB; ++j) r.sb[j] = sb[j];
   }
@@ -537,7 +544,11 @@ struct GemmKernel {
     if (AMB == 0) return;
     const int hshift = h * 16;
 #pragma unroll
-    for (int i = 0; i < AMB; ++i) s.a[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sa[i] >> hshift, 1.0f, false);
+    for (int i = 0; i < AMB; ++i) {
+      const u32x4& c = r.sa[i >> 1];
+      const uint32_t w = __builtin_amdgcn_perm(c[2 * (i & 1) + 1], c[2 * (i & 1)], sa_sel);
+      s.a[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+    }
 #pragma unroll
     for (int j = 0; j < NB; ++j) s.b[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sb[j] >> hshift, 1.0f, false);
   }
