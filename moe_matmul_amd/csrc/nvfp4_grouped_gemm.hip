@@ -77,6 +77,7 @@ constexpr int kRasterWidth = 8;           // n-tiles per raster super-column
 // and that lighter last row, and orders the classes by cost per tile, heaviest
 // first, so that the whole-tile walk below hands out big tiles first.
 constexpr int kMaxClasses = 2 * kMaxGroups;
+constexpr int kMaxSplitGrid = 512;  // stream-K workgroups (unit ranges passed by value)
 
 struct ClassArgs {
   const uint8_t* a;  // the group's tensors and sizes
@@ -98,6 +99,10 @@ struct KernelArgs {
   int32_t split;        // 0: whole tiles strided over the grid; 1: stream-K over units
   int32_t grid;         // workgroups of the main kernel
   float* partials;      // split: two fp32 tile-sized slots per workgroup
+  // split: workgroup w takes units [wg_unit[w], wg_unit[w + 1]), every range
+  // non-empty; the host sizes the ranges to equal modelled cost, since a stage
+  // of a tile that is mostly past m costs less than a full one.
+  int32_t wg_unit[kMaxSplitGrid + 1];
 };
 static_assert(sizeof(KernelArgs) <= 4096, "kernel arguments must fit the kernarg segment");
 
@@ -305,10 +310,15 @@ struct GemmKernel {
   }
   __device__ __forceinline__ int total_tiles() const { return args.tile_prefix[args.num_classes]; }
   __device__ __forceinline__ int64_t total_units() const { return args.unit_prefix[args.num_classes]; }
-  __device__ __forceinline__ int64_t unit_begin(int wg) const { return (int64_t)wg * total_units() / args.grid; }
+  __device__ __forceinline__ int64_t unit_begin(int wg) const { return args.wg_unit[wg]; }
   // the workgroup whose unit range holds unit u
   __device__ __forceinline__ int owner_of_unit(int64_t u) const {
-    return (int)(((u + 1) * (int64_t)args.grid - 1) / total_units());
+    int lo = 0, hi = args.grid - 1;  // last workgroup whose range starts at or before u
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (args.wg_unit[mid] <= u) lo = mid; else hi = mid - 1;
+    }
+    return lo;
   }
   __device__ __forceinline__ int64_t first_unit_of_tile(int tile) const {
     const int g = group_of_tile(tile);
@@ -950,6 +960,54 @@ struct WorkClass {
 // first (stable: groups keep their order among equals). Returns the count.
 double tile_overhead_stages() { return 1.5; }  // epilogue and pipeline fill per tile
 
+int build_classes(const int32_t* ps, int G, int cfg, WorkClass* out);
+
+// Stream-K ranges: ranges[w] .. ranges[w + 1] are the units of workgroup w,
+// cut so that every workgroup gets the same modelled cost (a unit of class c
+// costs cls[c].cost / nk) and at least one unit. Needs 1 <= grid <= units.
+// Returns the largest modelled cost of one range, in full tile-stages.
+double split_ranges(const WorkClass* cls, int nc, int grid, int32_t* ranges) {
+  // piecewise-linear cumulative cost over the units, one piece per class
+  double cost_at[kMaxClasses + 1];
+  int64_t unit_at[kMaxClasses + 1];
+  cost_at[0] = 0.0;
+  unit_at[0] = 0;
+  for (int c = 0; c < nc; ++c) {
+    const int64_t n = cls[c].nk ? cls[c].tiles * cls[c].nk : 0;
+    unit_at[c + 1] = unit_at[c] + n;
+    cost_at[c + 1] = cost_at[c] + (n ? cls[c].cost * cls[c].tiles : 0.0);
+  }
+  const int64_t units = unit_at[nc];
+  const double total = cost_at[nc];
+  auto cost_of = [&](int64_t u) {  // cost of units [0, u)
+    int c = 0;
+    while (c < nc - 1 && unit_at[c + 1] <= u) ++c;
+    const int64_t n = unit_at[c + 1] - unit_at[c];
+    return n ? cost_at[c] + (cost_at[c + 1] - cost_at[c]) * (double)(u - unit_at[c]) / (double)n : cost_at[c];
+  };
+  ranges[0] = 0;
+  int c = 0;
+  for (int w = 1; w < grid; ++w) {
+    const double x = total * w / grid;
+    while (c < nc - 1 && cost_at[c + 1] <= x) ++c;
+    const int64_t n = unit_at[c + 1] - unit_at[c];
+    const double span = cost_at[c + 1] - cost_at[c];
+    int64_t u = unit_at[c] + (n && span > 0.0 ? (int64_t)std::llround((x - cost_at[c]) / span * (double)n) : 0);
+    // strictly increasing, leaving one unit for every later workgroup
+    u = std::max<int64_t>(u, (int64_t)ranges[w - 1] + 1);
+    u = std::min<int64_t>(u, units - (grid - w));
+    ranges[w] = (int32_t)u;
+  }
+  ranges[grid] = (int32_t)units;
+  double worst = 0.0, prev = 0.0;
+  for (int w = 1; w <= grid; ++w) {
+    const double at = cost_of(ranges[w]);
+    worst = std::max(worst, at - prev);
+    prev = at;
+  }
+  return worst;
+}
+
 int build_classes(const int32_t* ps, int G, int cfg, WorkClass* out) {
   const TileConfig& tc = kConfigs[cfg];
   const int mb = tc.wm / 32;
@@ -1021,16 +1079,22 @@ Plan plan_for(const int32_t* ps, int G, int cus, int cfg, int split) {
     p.cost = mx;
     p.ws_bytes = 0;
   } else {
-    p.grid = (int)(units < cus ? units : cus);
-    const double per = p.grid > 0 ? (double)units / p.grid : 0.0;
-    // a workgroup's range touches about per/stages + 1 tiles, two of them split
-    double avg_stages = 0.0;
-    for (int g = 0; g < G; ++g) avg_stages += (double)group_tiles(ps, g, cfg) * group_stages(ps, g);
-    avg_stages = tiles > 0 ? avg_stages / tiles : 1.0;
-    const double segments = per / (avg_stages > 0 ? avg_stages : 1.0) + 1.0;
-    const double fixup = 2.0;          // partial write, in stages
-    const double reduce_kernel = 12.0;  // the second kernel and the partial traffic (measured)
-    p.cost = unit * (std::ceil(per) + tile_overhead * segments + fixup) + reduce_kernel;
+    const int cap = cus < kMaxSplitGrid ? cus : kMaxSplitGrid;
+    p.grid = (int)(units < cap ? units : cap);
+    WorkClass cls[kMaxClasses];
+    const int nc = build_classes(ps, G, cfg, cls);
+    static thread_local int32_t ranges[kMaxSplitGrid + 1];
+    const double per = split_ranges(cls, nc, p.grid, ranges);
+    // Each workgroup stores up to two fp32 partial tiles, and the reduction
+    // kernel reads them back and writes C: both scale with the tile area
+    // (measured: ~25 us for 255 split 256x256 tiles on 256 CUs, ~15 us for
+    // 128x256), on top of the second launch's fixed latency (~12 us on tiny
+    // problems), in 128x128-stage units of about 0.8 us.
+    const TileConfig& tc = kConfigs[cfg];
+    const double area = (double)tc.bm * tc.bn / 65536.0;
+    const double partials = 6.0 * area;   // the main kernel's partial stores
+    const double reduce_kernel = 15.0 + 30.0 * area * (p.grid - 1) / 255.0;
+    p.cost = unit * per + partials + reduce_kernel;
     p.ws_bytes = workspace_bytes_for(cfg, p.grid);
   }
   return p;
@@ -1137,7 +1201,10 @@ int launch(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, vo
   args.num_classes = nc > 0 ? nc : 1;
   args.split = plan.split;
   args.grid = plan.grid;
-  if (plan.split) args.partials = reinterpret_cast<float*>(workspace);
+  if (plan.split) {
+    args.partials = reinterpret_cast<float*>(workspace);
+    split_ranges(cls, nc, plan.grid, args.wg_unit);
+  }
   if (tiles == 0 || plan.grid == 0) return NVFP4_OK;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(tc.kernel, dim3(plan.grid), dim3(kThreads), 0, st, args);
