@@ -140,6 +140,17 @@ def test_heuristic_streamk_with_library_workspace():
     check(shapes, synth.make_custom(shapes, seed=12), label="long-K heuristic stream-K")
 
 
+@pytest.mark.parametrize("split", [None, 0])
+def test_max_k(split):
+    """The largest K the library accepts (2^22): fp32 accumulation over 4M
+    products; with the heuristic every workgroup contributes a range of stages
+    to the one tile (stream-K), forced whole tiles run all 32768 stages in one
+    workgroup."""
+    shapes = [(33, 24, 1 << 22, 1)]
+    assert mm.nvfp4_grouped_gemm_validate(shapes, [(16, 16, 16)], [(16, 16)]) == mm.NVFP4_OK
+    check(shapes, synth.make_custom(shapes, seed=4242), split_mode=split, label="k = 2^22")
+
+
 def test_streamk_is_deterministic_and_workspace_rules():
     shapes, groups = synth.make_workload(1)
     announce("stream-K determinism workload 1")
