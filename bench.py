@@ -52,6 +52,10 @@ def percentile(v, p):
     return float(np.percentile(np.asarray(v), p))
 
 
+def fmt_us(v):
+    return "n/a" if v is None else f"{v:.1f}"
+
+
 def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None):
     import torch
 
@@ -73,16 +77,18 @@ def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None
                 cp.append(e)
             sets.append(cp)
     stream = torch.cuda.current_stream()
-    ptrs = [dev.pointer_tables(s) for s in sets]
+    # argument tables marshalled once, so the timed loop measures the library
+    (ps,) = mm.prepare(problem_sizes=shapes)
+    ptrs = [mm.prepare(ptrs_abc=a, ptrs_sfa_sfb=f) for a, f in (dev.pointer_tables(s) for s in sets)]
     ws = dev.workspace_for(shapes) if split_mode is not None else None
 
-    def call(i):
+    def call(i, st=stream):
         abc, sf = ptrs[i % len(ptrs)]
         if split_mode is None:
-            mm.nvfp4_grouped_gemm_config(shapes, abc, sf, len(shapes), stream, tile_config)
+            mm.nvfp4_grouped_gemm_config(ps, abc, sf, len(shapes), st, tile_config)
         else:
-            mm.nvfp4_grouped_gemm_ex(shapes, abc, sf, len(shapes), ws.data_ptr(), ws.numel(), tile_config,
-                                     split_mode, stream)
+            mm.nvfp4_grouped_gemm_ex(ps, abc, sf, len(shapes), ws.data_ptr(), ws.numel(), tile_config,
+                                     split_mode, st)
 
     for i in range(warmup):
         call(i)
@@ -101,12 +107,37 @@ def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None
     geo = mm.nvfp4_launch_geometry(shapes, torch.cuda.get_device_properties(0).multi_processor_count, tile_config,
                                    -1 if split_mode is None else split_mode)
     avg_s = total_ms / steps / 1e3
+    # The same calls replayed from a captured HIP graph: GPU time per call
+    # without host launch overhead (what matters for the microsecond-sized
+    # workloads). Whole-tile plans only (a stream-K plan's library workspace
+    # would be allocated during capture).
+    graph_us = None
+    if split_mode is None and geo["split"] == 0:
+        reps = min(steps, 50)
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            call(0, side)  # warm the side stream outside capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for i in range(reps):
+                call(i, side)
+        g.replay()
+        torch.cuda.synchronize()
+        ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ga.record(stream)
+        g.replay()
+        gb.record(stream)
+        torch.cuda.synchronize()
+        graph_us = ga.elapsed_time(gb) / reps * 1e3
+        del g
     return dict(
         workload=synth.WORKLOADS[idx]["name"], shapes=[list(s) for s in shapes], flops=flops, bytes=nbytes,
         total_ms=total_ms, wall_s=wall, ms_per_call=total_ms / steps,
         us_median=percentile(per, 50) * 1e3, us_p10=percentile(per, 10) * 1e3, us_p90=percentile(per, 90) * 1e3,
         tflops=flops / avg_s / 1e12, gbs=nbytes / avg_s / 1e9, sets=len(sets), tile_config=geo["config"],
-        tiles=geo["total_tiles"], grid=geo["grid"], split=geo["split"],
+        tiles=geo["total_tiles"], grid=geo["grid"], split=geo["split"], graph_us_per_call=graph_us,
     )
 
 
@@ -208,7 +239,7 @@ def main():
     head = time_workload(args.workload, args.steps, args.warmup, args.tile_config, cold=True)
     hot = time_workload(args.workload, args.steps, args.warmup, args.tile_config, cold=False)
     log(f"[bench] cold {head['tflops']:.1f} TFLOP/s {head['us_median']:.1f} us/call; "
-        f"hot {hot['tflops']:.1f} TFLOP/s")
+        f"hot {hot['tflops']:.1f} TFLOP/s; graph replay {fmt_us(head['graph_us_per_call'])} us/call")
     details = {"headline": head, "hot": hot}
     if args.all:
         allres = []
@@ -220,7 +251,8 @@ def main():
                 log(f"[bench] workload {i} {r['workload']} split={'auto' if sm is None else sm}: "
                     f"{r['tflops']:.1f} TFLOP/s, {r['us_median']:.1f} us/call "
                     f"(p10 {r['us_p10']:.1f}, p90 {r['us_p90']:.1f}), {r['gbs']:.0f} GB/s, cfg {r['tile_config']}, "
-                    f"split {r['split']}, {r['tiles']} tiles, grid {r['grid']}")
+                    f"split {r['split']}, {r['tiles']} tiles, grid {r['grid']}, "
+                    f"graph replay {fmt_us(r['graph_us_per_call'])} us/call")
         details["all"] = allres
 
     if args.sweep:
@@ -267,7 +299,9 @@ def main():
             "cache": f"cold: {head['sets']} rotating input/output sets",
         },
         "us_per_call": {"median": round(head["us_median"], 2), "p10": round(head["us_p10"], 2),
-                        "p90": round(head["us_p90"], 2)},
+                        "p90": round(head["us_p90"], 2),
+                        "graph_replay": None if head["graph_us_per_call"] is None
+                        else round(head["graph_us_per_call"], 2)},
         "hot": {"value": round(hot["tflops"], 2), "us_median": round(hot["us_median"], 2)},
         "algorithmic_gbs": round(head["gbs"], 1),
         "roofline": {

@@ -67,11 +67,15 @@ def load_library() -> ctypes.CDLL:
 
 
 def _sizes(problem_sizes):
+    if isinstance(problem_sizes, ctypes.Array) and problem_sizes._type_ is ctypes.c_int32:
+        return problem_sizes, len(problem_sizes) // 4  # already marshalled (see prepare)
     flat = [int(v) for row in problem_sizes for v in row]
     return (ctypes.c_int32 * max(len(flat), 1))(*flat), len(flat) // 4
 
 
 def _u64(rows, width):
+    if isinstance(rows, ctypes.Array) and rows._type_ is ctypes.c_uint64:
+        return rows
     flat = [int(v) for row in rows for v in row]
     if len(flat) % width:
         raise ValueError(f"pointer table rows must have {width} entries")
@@ -81,9 +85,27 @@ def _u64(rows, width):
 def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         return ctypes.c_void_p(0)
+    if isinstance(stream, ctypes.c_void_p):
+        return stream
     if hasattr(stream, "cuda_stream"):
         return ctypes.c_void_p(stream.cuda_stream)
     return ctypes.c_void_p(int(stream))
+
+
+def prepare(problem_sizes=None, ptrs_abc=None, ptrs_sfa_sfb=None, stream=None):
+    """Marshal arguments once: returns the ctypes arrays (and stream handle) that
+    every entry point accepts as they are, for callers that issue the same
+    call many times (a timed loop, a captured graph)."""
+    out = []
+    if problem_sizes is not None:
+        out.append(_sizes(problem_sizes)[0])
+    if ptrs_abc is not None:
+        out.append(_u64(ptrs_abc, 3))
+    if ptrs_sfa_sfb is not None:
+        out.append(_u64(ptrs_sfa_sfb, 2))
+    if stream is not None:
+        out.append(_stream(stream))
+    return tuple(out)
 
 
 def nvfp4_grouped_gemm(problem_sizes, ptrs_abc, ptrs_sfa_sfb, num_groups=None, stream=None) -> None:

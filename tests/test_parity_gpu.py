@@ -205,6 +205,37 @@ def test_repeat_is_bitwise_deterministic_and_streams():
         assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
 
 
+@pytest.mark.parametrize("idx", [1, 3])
+def test_graph_replay_matches_eager(idx):
+    """A call captured in a HIP graph (whole-tile plan: no library allocation)
+    and replayed several times, with eager work and synchronisation between
+    the replays, writes exactly what the eager call writes."""
+    shapes, groups = synth.make_workload(idx)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert mm.nvfp4_launch_geometry(shapes, cus)["split"] == 0
+    announce(f"graph replay workload {idx}")
+    d = dev.upload(shapes, groups)
+    dev.run(shapes, d)
+    torch.cuda.synchronize()
+    eager = [c.copy() for c in dev.c_as_numpy(shapes, d)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dev.run(shapes, d, stream=side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        dev.run(shapes, d, stream=side)
+    for rep in range(3):
+        for dd in d:
+            dd["c"].fill_(-1)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(eager, dev.c_as_numpy(shapes, d)):
+            assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), f"replay {rep} differs"
+
+
 def test_empty_call_launches_nothing():
     announce("all-empty groups")
     shapes = [(0, 64, 64, 1), (64, 0, 64, 1)]
