@@ -135,13 +135,6 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t num_bytes) 
   return i32x4{(int32_t)(uint32_t)b, (int32_t)((uint32_t)(b >> 32) & 0xFFFFu), n, kBufferWord3};
 }
 
-// The same resource as the builtin buffer-access type (for compiler-issued
-// buffer loads and stores).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_buffer(const void* base, int64_t num_bytes) {
-  const int n = num_bytes <= 0 ? 0 : (num_bytes >= 0x7fffffff ? 0x7fffffff : (int)num_bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kBufferWord3);
-}
-
 // 16 bytes per lane from global (buffer, bounds-checked) straight into LDS at
 // lds_block + 16 * lane (M0 holds the wave's LDS base). Issued as inline asm so
 // the compiler does not treat it as an LDS write it must wait for: the kernel
@@ -305,11 +298,10 @@ struct GemmKernel {
   // 506336 numbers them group by group; here a group may be two classes, and
   // heavier classes come first). A unit is one 128-K stage of one tile; units
   // are numbered tile by tile.
-  __device__ __forceinline__ int group_of_tile(int tile) const {
+  __device__ __forceinline__ int class_of_tile(int tile) const {
     return search_prefix(args.tile_prefix, args.num_classes, tile);
   }
   __device__ __forceinline__ int total_tiles() const { return args.tile_prefix[args.num_classes]; }
-  __device__ __forceinline__ int64_t total_units() const { return args.unit_prefix[args.num_classes]; }
   __device__ __forceinline__ int64_t unit_begin(int wg) const { return args.wg_unit[wg]; }
   // the workgroup whose unit range holds unit u
   __device__ __forceinline__ int owner_of_unit(int64_t u) const {
@@ -319,10 +311,6 @@ struct GemmKernel {
       if (args.wg_unit[mid] <= u) lo = mid; else hi = mid - 1;
     }
     return lo;
-  }
-  __device__ __forceinline__ int64_t first_unit_of_tile(int tile) const {
-    const int g = group_of_tile(tile);
-    return args.unit_prefix[g] + (int64_t)(tile - args.tile_prefix[g]) * args.cls[g].nk;
   }
   __device__ __forceinline__ int tile_of_unit(int64_t u, int* stage) const {
     const int g = search_prefix(args.unit_prefix, args.num_classes, u);
@@ -338,7 +326,7 @@ struct GemmKernel {
     if (!s.valid) return;
     int stage;
     s.tile = tile_of_unit(u, &stage);
-    const int nk = args.cls[group_of_tile(s.tile)].nk;
+    const int nk = args.cls[class_of_tile(s.tile)].nk;
     s.s0 = stage;
     s.s1 = (int)min((int64_t)nk, stage + (u_end - u));
   }
@@ -351,7 +339,7 @@ struct GemmKernel {
       s.tile = vwg;
       s.valid = s.tile < total_tiles();
       s.s0 = 0;
-      s.s1 = s.valid ? args.cls[group_of_tile(s.tile)].nk : 0;
+      s.s1 = s.valid ? args.cls[class_of_tile(s.tile)].nk : 0;
     }
   }
 
@@ -367,12 +355,12 @@ struct GemmKernel {
       s.tile = r * args.grid + ((r & 1) ? args.grid - 1 - vwg : vwg);
       s.valid = s.tile < total_tiles();
       s.s0 = 0;
-      s.s1 = s.valid ? args.cls[group_of_tile(s.tile)].nk : 0;
+      s.s1 = s.valid ? args.cls[class_of_tile(s.tile)].nk : 0;
     }
   }
 
   __device__ __forceinline__ TileCtx setup(int tile) const {
-    const int gi = group_of_tile(tile);
+    const int gi = class_of_tile(tile);
     const ClassArgs& G = args.cls[gi];
     const int M = G.m, N = G.n, K = G.k;
     const int tiles_m = G.tiles_m;
@@ -816,7 +804,7 @@ __global__ __launch_bounds__(kThreads) void nvfp4_streamk_reduce_kernel(KernelAr
   const int tile = k.tile_of_unit(ub, &stage);
   if (stage == 0) return;  // the boundary falls between tiles: nothing split here
   const int64_t u_first = ub - stage;
-  const int nk = args.cls[k.group_of_tile(tile)].nk;
+  const int nk = args.cls[k.class_of_tile(tile)].nk;
   const int c_first = k.owner_of_unit(u_first);
   const int c_last = k.owner_of_unit(u_first + nk - 1);
   if (boundary != c_first + 1) return;  // another boundary of this tile does the work
@@ -929,8 +917,6 @@ int64_t group_tiles(const int32_t* ps, int g, int cfg) {
 }
 
 int group_stages(const int32_t* ps, int g) { return (int)ceil_div64(ps[4 * g + 2], kBK); }
-
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Largest number of 32-row blocks a wave computes in a tile with `rows` rows
 // below m (row blocks alternate between the two wave rows).
