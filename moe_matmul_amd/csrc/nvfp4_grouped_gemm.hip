@@ -670,29 +670,50 @@ struct GemmKernel {
   }
 
   // ---------------- output ----------------
-  // fp32 -> fp16 (RNE), 8-byte stores masked to m and n.
+  // fp32 -> fp16 (RNE), 16-byte stores masked to m and n. A lane holds runs
+  // of 4 consecutive columns of its row (e * 8 + h * 4 .. +3 of each 32-column
+  // block); swapping runs between the two lane halves (v_permlane32_swap) gives
+  // each lane 8 consecutive columns, so a store instruction writes 32
+  // contiguous bytes per row instead of two 16-byte pieces.
+  __device__ __forceinline__ static uint32_t pack_f16(float lo, float hi) {
+    const f16x2 v = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+
   __device__ __forceinline__ void epilogue(const f32x16 (&acc)[MB][NB], const TileCtx& t) const {
+    // Tiles wholly inside m and n (all but the edges) store without masks,
+    // i.e. without an exec-mask branch around every store.
+    if (t.row0 + BM <= t.M && t.col0 + BN <= t.N) epilogue_impl<false>(acc, t);
+    else epilogue_impl<true>(acc, t);
+  }
+
+  template <bool MASKED>
+  __device__ __forceinline__ void epilogue_impl(const f32x16 (&acc)[MB][NB], const TileCtx& t) const {
     const int col0 = t.col0 + wn * WN;
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
       const int row = t.row0 + row_block(wm, i) * 32 + lr;
-      if (row < t.M) {
-        uint16_t* crow = t.c + (size_t)row * t.N;
+      uint16_t* crow = t.c + (size_t)row * t.N;
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
+      for (int j = 0; j < NB; ++j) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int col = col0 + j * 32 + e * 8 + h * 4;
-            if (col < t.N) {
-              const f16x4 v = {(_Float16)acc[i][j][e * 4 + 0], (_Float16)acc[i][j][e * 4 + 1],
-                               (_Float16)acc[i][j][e * 4 + 2], (_Float16)acc[i][j][e * 4 + 3]};
-              *reinterpret_cast<f16x4*>(crow + col) = v;
-            }
+        for (int p = 0; p < 2; ++p) {
+          // runs 2p (kept by lanes h = 0) and 2p + 1 (kept by lanes h = 1)
+          const f32x16& a = acc[i][j];
+          const auto s0 = __builtin_amdgcn_permlane32_swap(pack_f16(a[8 * p + 0], a[8 * p + 1]),
+                                                           pack_f16(a[8 * p + 4], a[8 * p + 5]), false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(pack_f16(a[8 * p + 2], a[8 * p + 3]),
+                                                           pack_f16(a[8 * p + 6], a[8 * p + 7]), false, false);
+          const int col = col0 + j * 32 + (2 * p + h) * 8;
+          if (!MASKED || (row < t.M && col < t.N)) {  // n % 8 == 0: an 8-column chunk is all in or all out
+            const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+            *reinterpret_cast<u32x4*>(crow + col) = v;
           }
         }
       }
     }
   }
+
 
   // Stream-K partials. Workgroup wg owns two fp32 tile-sized slots: slot 0 for
   // its first segment, slot 1 for its last. Each lane's 16 floats of block
