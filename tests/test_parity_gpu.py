@@ -140,6 +140,19 @@ def test_heuristic_streamk_with_library_workspace():
     check(shapes, synth.make_custom(shapes, seed=12), label="long-K heuristic stream-K")
 
 
+def test_streamk_plans_share_library_workspace():
+    """Stream-K calls with different tile configurations (so different grids
+    and slot sizes) in a row on one stream share the library's workspace: each
+    must find its arrival counters at zero, not an earlier call's partials."""
+    shapes = [(256, 256, 16384, 1), (40, 136, 64, 1)]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    groups = synth.make_custom(shapes, seed=21)
+    ref = O.grouped_gemm(shapes, poison_padding(shapes, groups))
+    for cfg in (0, 3, 1, 0):
+        assert mm.nvfp4_launch_geometry(shapes, cus, cfg)["split"] == 1
+        check(shapes, groups, tile_config=cfg, ref=ref, label=f"stream-K cfg {cfg} after others")
+
+
 @pytest.mark.parametrize("split", [None, 0])
 def test_max_k(split):
     """The largest K the library accepts (2^22): fp32 accumulation over 4M
@@ -205,27 +218,27 @@ def test_repeat_is_bitwise_deterministic_and_streams():
         assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
 
 
-@pytest.mark.parametrize("idx", [1, 3])
-def test_graph_replay_matches_eager(idx):
-    """A call captured in a HIP graph (whole-tile plan: no library allocation)
-    and replayed several times, with eager work and synchronisation between
-    the replays, writes exactly what the eager call writes."""
+@pytest.mark.parametrize("idx,split", [(1, 0), (3, 0), (1, 1), (2, 1)])
+def test_graph_replay_matches_eager(idx, split):
+    """A call captured in a HIP graph and replayed several times, with eager
+    work and synchronisation between the replays, writes exactly what the
+    eager call writes. Whole tiles, and stream-K with a caller workspace (its
+    arrival counters must be back at zero after every replay)."""
     shapes, groups = synth.make_workload(idx)
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
-    assert mm.nvfp4_launch_geometry(shapes, cus)["split"] == 0
-    announce(f"graph replay workload {idx}")
+    announce(f"graph replay workload {idx} split {split}")
     d = dev.upload(shapes, groups)
-    dev.run(shapes, d)
+    ws = dev.workspace_for(shapes) if split else None
+    dev.run(shapes, d, split_mode=split, workspace=ws)
     torch.cuda.synchronize()
     eager = [c.copy() for c in dev.c_as_numpy(shapes, d)]
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        dev.run(shapes, d, stream=side)
+        dev.run(shapes, d, stream=side, split_mode=split, workspace=ws)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=side):
-        dev.run(shapes, d, stream=side)
+        dev.run(shapes, d, stream=side, split_mode=split, workspace=ws)
     for rep in range(3):
         for dd in d:
             dd["c"].fill_(-1)  # eager work between replays
