@@ -36,7 +36,8 @@
 //    takes K elements [32h, 32h+32) in four steps of 8. A and B use the same
 //    permutation, so the sum is unchanged; each step of 8 lies inside one
 //    16-block, so one scale covers it.
-//  * Epilogue: fp32 -> fp16 (RNE) fused, 8-byte stores masked to m and n.
+//  * Epilogue: fp32 -> fp16 (RNE) fused; a lane-half swap gives each lane 8
+//    consecutive columns, stored as 16 bytes, masked to m and n.
 //    Tiles split by stream-K store fp32 partials; a second kernel adds them in
 //    a fixed order and writes fp16.
 
