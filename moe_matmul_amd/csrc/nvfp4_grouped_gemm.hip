@@ -690,11 +690,18 @@ struct GemmKernel {
 
   template <bool MASKED>
   __device__ __forceinline__ void epilogue_impl(const f32x16 (&acc)[MB][NB], const TileCtx& t) const {
+    // The lane's row and column offsets are formed here, per tile, from a copy
+    // the compiler cannot see through: left to itself it hoists one offset per
+    // block out of the tile loop and spills them, and each reload between
+    // stores then waits for every store before it.
+    int lro = lr, h8 = h * 8;
+    asm volatile("" : "+v"(lro), "+v"(h8));
     const int col0 = t.col0 + wn * WN;
+    uint16_t* clane = t.c + (size_t)(t.row0 + lro) * t.N + col0 + h8;
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
-      const int row = t.row0 + row_block(wm, i) * 32 + lr;
-      uint16_t* crow = t.c + (size_t)row * t.N;
+      const int rb = row_block(wm, i) * 32;
+      uint16_t* crow = clane + (size_t)rb * t.N;
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
 #pragma unroll
@@ -705,10 +712,11 @@ struct GemmKernel {
                                                            pack_f16(a[8 * p + 4], a[8 * p + 5]), false, false);
           const auto s1 = __builtin_amdgcn_permlane32_swap(pack_f16(a[8 * p + 2], a[8 * p + 3]),
                                                            pack_f16(a[8 * p + 6], a[8 * p + 7]), false, false);
-          const int col = col0 + j * 32 + (2 * p + h) * 8;
-          if (!MASKED || (row < t.M && col < t.N)) {  // n % 8 == 0: an 8-column chunk is all in or all out
+          const int cu = j * 32 + 2 * p * 8;  // uniform part of the column
+          // n % 8 == 0: an 8-column chunk is all in or all out
+          if (!MASKED || (lro < t.M - t.row0 - rb && h8 < t.N - col0 - cu)) {
             const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
-            *reinterpret_cast<u32x4*>(crow + col) = v;
+            *reinterpret_cast<u32x4*>(crow + cu) = v;
           }
         }
       }
