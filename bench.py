@@ -56,14 +56,19 @@ def fmt_us(v):
     return "n/a" if v is None else f"{v:.1f}"
 
 
-def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None):
+def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None, device_tables=False,
+                  super_batch=False):
+    """Times the grouped GEMM on workload ``idx``. ``device_tables``: through
+    nvfp4_grouped_gemm_device (group tables in device memory); ``super_batch``:
+    the groups of 15 calls of the workload in one launch (device tables)."""
     import torch
 
     import moe_matmul_amd as mm
     from moe_matmul_amd import device as dev
     from moe_matmul_amd import synth
 
-    shapes, groups = synth.make_workload(idx)
+    device_tables = device_tables or super_batch
+    shapes, groups = synth.make_super_batch(idx) if super_batch else synth.make_workload(idx)
     base = dev.upload(shapes, groups)
     flops, nbytes = algorithmic(shapes)
     sets = [base]
@@ -81,8 +86,14 @@ def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None
     (ps,) = mm.prepare(problem_sizes=shapes)
     ptrs = [mm.prepare(ptrs_abc=a, ptrs_sfa_sfb=f) for a, f in (dev.pointer_tables(s) for s in sets)]
     ws = dev.workspace_for(shapes) if split_mode is not None else None
+    tables = [dev.device_tables(shapes, s) for s in sets] if device_tables else None
 
     def call(i, st=stream):
+        if device_tables:
+            t = tables[i % len(tables)]
+            mm.nvfp4_grouped_gemm_device(t[0].data_ptr(), t[1].data_ptr(), t[2].data_ptr(), len(shapes), tile_config,
+                                         0, st)
+            return
         abc, sf = ptrs[i % len(ptrs)]
         if split_mode is None:
             mm.nvfp4_grouped_gemm_config(ps, abc, sf, len(shapes), st, tile_config)
@@ -115,8 +126,14 @@ def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None
         evs[i + 1].record(stream)
     torch.cuda.synchronize()
     per = [evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]  # ms
-    geo = mm.nvfp4_launch_geometry(shapes, torch.cuda.get_device_properties(0).multi_processor_count, tile_config,
-                                   -1 if split_mode is None else split_mode)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if device_tables:
+        cfg = 2 if tile_config < 0 else tile_config
+        p0 = [0x1000] * 5
+        geo = dict(config=cfg, split=0, grid=cus,
+                   total_tiles=sum(mm.nvfp4_device_group_tiles(s, p0, cfg) for s in shapes))
+    else:
+        geo = mm.nvfp4_launch_geometry(shapes, cus, tile_config, -1 if split_mode is None else split_mode)
     avg_s = total_ms / steps / 1e3
     # The same calls replayed from a captured HIP graph: GPU time per call
     # without host launch overhead (what matters for the microsecond-sized
@@ -143,8 +160,11 @@ def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None
         torch.cuda.synchronize()
         graph_us = ga.elapsed_time(gb) / reps * 1e3
         del g
+    name = synth.WORKLOADS[idx]["name"]
+    if super_batch:
+        name = f"superbatch{synth.SUPER_BATCH_COPIES}x_{name}"
     return dict(
-        workload=synth.WORKLOADS[idx]["name"], shapes=[list(s) for s in shapes], flops=flops, bytes=nbytes,
+        workload=name, device_tables=device_tables, shapes=[list(s) for s in shapes], flops=flops, bytes=nbytes,
         total_ms=total_ms, wall_s=wall, ms_per_call=total_ms / steps,
         us_median=percentile(per, 50) * 1e3, us_p10=percentile(per, 10) * 1e3, us_p90=percentile(per, 90) * 1e3,
         tflops=flops / avg_s / 1e12, gbs=nbytes / avg_s / 1e9, sets=len(sets), tile_config=geo["config"],
@@ -220,6 +240,8 @@ def main():
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--tile-config", type=int, default=-1)
     ap.add_argument("--all", action="store_true", help="also time every workload (to stderr / --out)")
+    ap.add_argument("--super-batch", action="store_true",
+                    help="also time 15 calls of workload 2 merged into one 120-group launch (device tables)")
     ap.add_argument("--sweep", action="store_true",
                     help="time every workload under every tile configuration and split mode (to stderr / --out)")
     ap.add_argument("--out", default=None, help="write the per-workload details as JSON here")
@@ -238,6 +260,7 @@ def main():
 
     import torch
     import moe_matmul_amd as mm
+    from moe_matmul_amd import synth
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -265,7 +288,23 @@ def main():
                     f"(p10 {r['us_p10']:.1f}, p90 {r['us_p90']:.1f}), {r['gbs']:.0f} GB/s, cfg {r['tile_config']}, "
                     f"split {r['split']}, {r['tiles']} tiles, grid {r['grid']}, "
                     f"graph replay {fmt_us(r['graph_us_per_call'])} us/call")
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        for i in range(5):
+            # the tile configuration the by-value entry point's heuristic picks
+            cfg = mm.nvfp4_select_tile_config(synth.workload_shapes(i), cus)
+            r = time_workload(i, max(20, args.steps // 2), 5, cfg, cold=True, device_tables=True)
+            allres.append(r)
+            log(f"[bench] workload {i} {r['workload']} device tables: {r['tflops']:.1f} TFLOP/s, "
+                f"{r['ms_per_call'] * 1e3:.1f} us/call, median {r['us_median']:.1f}, cfg {r['tile_config']}, "
+                f"{r['tiles']} tiles, graph replay {fmt_us(r['graph_us_per_call'])} us/call")
         details["all"] = allres
+    if args.all or args.super_batch:
+        sb = time_workload(2, max(10, args.steps // 10), 3, args.tile_config, cold=True, super_batch=True)
+        log(f"[bench] super-batch {sb['workload']} ({len(sb['shapes'])} groups, device tables): "
+            f"{sb['tflops']:.1f} TFLOP/s, {sb['ms_per_call'] * 1e3:.1f} us/call, median {sb['us_median']:.1f}, "
+            f"cfg {sb['tile_config']}, {sb['tiles']} tiles, "
+            f"{100 * sb['tflops'] / PEAK_F16_TFLOPS:.1f}% of the f16 MFMA peak")
+        details["super_batch"] = sb
 
     if args.sweep:
         sweep = []

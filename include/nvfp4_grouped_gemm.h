@@ -105,6 +105,52 @@ int nvfp4_grouped_gemm_ex(const int32_t* problem_sizes, const uint64_t* ptrs_abc
                           size_t workspace_bytes, int tile_config, int split_mode, void* stream);
 
 /*
+ * nvfp4_grouped_gemm_device - the same grouped GEMM with the group tables in
+ * device memory, for up to NVFP4_MAX_DEVICE_GROUPS groups. This is the
+ * super-batch of submission 506336 (kernelindex.com "kernelbot nvfp4 group
+ * gemm", the super-batch build and its compiled 120-group kernel: the groups
+ * of 15 benchmark calls merged into one launch, with the problem sizes and
+ * tensor addresses read from device pointer tables and each tile's group
+ * found by binary search over the tile prefix). The host reads no table, so
+ * a captured HIP graph of this call follows whatever the tables hold when it
+ * is replayed.
+ *
+ *   d_problem_sizes  device int32 [num_groups][4] = (m, n, k, l), 16-byte aligned.
+ *   d_ptrs_abc       device uint64 [num_groups][3] = addresses of A, B, C, 16-byte aligned.
+ *   d_ptrs_sfa_sfb   device uint64 [num_groups][2] = addresses of SFA, SFB, 16-byte aligned.
+ *   num_groups       1 .. NVFP4_MAX_DEVICE_GROUPS.
+ *   tile_config      0 .. nvfp4_num_tile_configs()-1, or -1 for 256x128 tiles.
+ *   d_status         device int32, 4-byte aligned, or NULL: the kernel stores
+ *                    there the number of groups it rejected (0: none).
+ *   stream           a hipStream_t (NULL = the default stream).
+ *
+ * Checked on the host (nothing is launched on failure): num_groups, the table
+ * pointers (non-null, aligned), tile_config. Checked by the kernel, per group,
+ * with the same rules as nvfp4_grouped_gemm plus at most 2^20 tiles of
+ * 128x128 per group: a group that fails is rejected - it gets no tiles, its C
+ * is left untouched - and counted in *d_status. Whole tiles only, over one
+ * workgroup per compute unit, the full tile rows of all groups first, then
+ * the groups' last tile rows by how full they are (the kernel sorts by row
+ * count only: groups of different k keep their table order within a class);
+ * the library allocates nothing.
+ * The tables must stay unchanged until the kernel has finished.
+ * Returns NVFP4_OK once enqueued, NVFP4_ERR_HIP if the launch failed.
+ */
+#define NVFP4_MAX_DEVICE_GROUPS 512
+int nvfp4_grouped_gemm_device(const int32_t* d_problem_sizes, const uint64_t* d_ptrs_abc,
+                              const uint64_t* d_ptrs_sfa_sfb, int num_groups, int tile_config,
+                              int32_t* d_status, void* stream);
+
+/*
+ * nvfp4_device_group_tiles - the per-group check of nvfp4_grouped_gemm_device,
+ * on the host (no HIP call): `size` = (m, n, k, l), `ptrs` = addresses of
+ * (A, B, C, SFA, SFB). Returns the tiles the kernel gives the group with
+ * `tile_config` (-1: the default), or -1 if the kernel rejects the group (or
+ * an argument is NULL or tile_config unknown).
+ */
+int64_t nvfp4_device_group_tiles(const int32_t* size, const uint64_t* ptrs, int tile_config);
+
+/*
  * nvfp4_workspace_bytes - workspace that covers every plan the library may
  * choose for these sizes on `num_cus` compute units (host only, no HIP call);
  * 0 for invalid sizes.

@@ -18,6 +18,7 @@ NVFP4_ERR_HIP = -3
 NVFP4_ERR_CONFIG = -4
 NVFP4_ERR_WORKSPACE = -5
 NVFP4_MAX_GROUPS = 8
+NVFP4_MAX_DEVICE_GROUPS = 512
 
 _lib = None
 
@@ -53,6 +54,9 @@ def load_library() -> ctypes.CDLL:
                                                  i64p, ip, ip, ctypes.POINTER(ctypes.c_size_t)]),
         "nvfp4_grouped_gemm_ex": (ctypes.c_int, [i32p, u64p, u64p, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
                                                  ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
+        "nvfp4_grouped_gemm_device": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                                     ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]),
+        "nvfp4_device_group_tiles": (ctypes.c_int64, [i32p, u64p, ctypes.c_int]),
         "nvfp4_workspace_bytes": (ctypes.c_size_t, [i32p, ctypes.c_int, ctypes.c_int]),
         "nvfp4_sf_bytes": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int, ctypes.c_int]),
         "nvfp4_last_hip_error": (ctypes.c_int, []),
@@ -171,6 +175,27 @@ def nvfp4_grouped_gemm_ex(problem_sizes, ptrs_abc, ptrs_sfa_sfb, num_groups=None
                                    int(workspace_bytes), int(tile_config), int(split_mode), _stream(stream))
     if rc != NVFP4_OK:
         raise Nvfp4Error(rc, "nvfp4_grouped_gemm_ex")
+
+
+def nvfp4_grouped_gemm_device(d_problem_sizes, d_ptrs_abc, d_ptrs_sfa_sfb, num_groups, tile_config=-1,
+                              d_status=0, stream=None) -> None:
+    """Grouped GEMM over group tables in device memory: the first three
+    arguments are device addresses of int32 [G][4] (m, n, k, l), uint64 [G][3]
+    (A, B, C) and uint64 [G][2] (SFA, SFB); ``d_status`` is the device address
+    of an int32 that receives the number of rejected groups (0 = none)."""
+    rc = load_library().nvfp4_grouped_gemm_device(
+        ctypes.c_void_p(int(d_problem_sizes)), ctypes.c_void_p(int(d_ptrs_abc)), ctypes.c_void_p(int(d_ptrs_sfa_sfb)),
+        int(num_groups), int(tile_config), ctypes.c_void_p(int(d_status)), _stream(stream))
+    if rc != NVFP4_OK:
+        raise Nvfp4Error(rc, "nvfp4_grouped_gemm_device")
+
+
+def nvfp4_device_group_tiles(size, ptrs, tile_config=-1) -> int:
+    """Host copy of the device-table kernel's per-group check: tiles of the
+    group (m, n, k, l) with addresses (A, B, C, SFA, SFB), or -1 if rejected."""
+    sz = (ctypes.c_int32 * 4)(*[int(v) for v in size])
+    p = (ctypes.c_uint64 * 5)(*[int(v) for v in ptrs])
+    return int(load_library().nvfp4_device_group_tiles(sz, p, int(tile_config)))
 
 
 def nvfp4_workspace_bytes(problem_sizes, num_cus: int, num_groups=None) -> int:

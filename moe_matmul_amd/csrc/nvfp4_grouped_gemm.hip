@@ -204,7 +204,116 @@ __device__ __forceinline__ int search_prefix(const int32_t* prefix, int count, i
   return lo;
 }
 
-template <int BM, int BN, int WM, int WN, int NS>
+// Where a kernel finds its work: the by-value argument block (up to eight
+// groups, split into cost-ordered classes by the host; whole tiles or
+// stream-K) ...
+struct KernargSrc {
+  static constexpr bool kCanSplit = true;
+  const KernelArgs& args;
+  __device__ __forceinline__ int grid() const { return args.grid; }
+  __device__ __forceinline__ bool split() const { return args.split != 0; }
+  __device__ __forceinline__ int total_tiles() const { return args.tile_prefix[args.num_classes]; }
+  __device__ __forceinline__ int class_of_tile(int tile) const {
+    return search_prefix(args.tile_prefix, args.num_classes, tile);
+  }
+  __device__ __forceinline__ int tile_prefix(int c) const { return args.tile_prefix[c]; }
+  __device__ __forceinline__ const ClassArgs& cls(int c) const { return args.cls[c]; }
+  __device__ __forceinline__ int nk(int c) const { return args.cls[c].nk; }
+};
+
+// ... or group tables in device memory. There the kernel makes the classes
+// itself, heaviest first as far as the row count goes: with R = BM / 64
+// (32-row blocks per wave in a full tile row), class b * G + g holds the tile
+// rows of group g in which a wave computes R - b blocks - the full rows for
+// b = 0, the last row for the b its row count gives (none if that row is
+// full). Tiles are numbered class by class: the full rows of all groups, then
+// the last rows, the least light first. Whole tiles only. The tile prefix over
+// the classes is built in LDS (build_device_prefix).
+constexpr int kMaxDeviceGroups = NVFP4_MAX_DEVICE_GROUPS;
+constexpr int kMaxRowClasses = 4;  // R for the 256-row tiles
+constexpr int kMaxDeviceClasses = kMaxRowClasses * kMaxDeviceGroups;
+static_assert(kMaxDeviceClasses == 32 * 64, "two-level ballot search over 64 lanes");
+
+struct DeviceGroupArgs {
+  const int32_t* sizes;  // [G][4] (m, n, k, l)
+  const uint64_t* abc;   // [G][3] addresses of A, B, C
+  const uint64_t* sf;    // [G][2] addresses of SFA, SFB
+  int32_t* status;       // nullptr, or: number of rejected groups
+  int32_t num_groups;
+  int32_t grid;
+};
+
+// The tables do not change while the kernel runs: reading them through the
+// constant address space lets the wave-uniform reads be scalar loads.
+template <class T>
+__device__ __forceinline__ T load_const(const T* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) T*)p)[i];
+}
+
+// Class of the last tile row of a group with m > 0 rows: BM / 64 minus the
+// 32-row blocks a wave computes there (0: a full row).
+template <int BM>
+__host__ __device__ inline int last_row_class(int64_t m) {
+  const int64_t rows = m - ((m + BM - 1) / BM - 1) * BM;  // 1 .. BM
+  const int64_t amb = ((rows + 31) / 32 + 1) / 2;
+  return BM / 64 - (int)amb;
+}
+
+template <int BM, int BN>
+struct DeviceSrc {
+  static constexpr bool kCanSplit = false;
+  static constexpr int R = BM / 64;
+  static_assert(R >= 1 && R <= kMaxRowClasses, "row classes");
+  const DeviceGroupArgs& args;
+  const int32_t* prefix;  // LDS: first tile of class c for c = 0 .. R G (prefix[R G] = all tiles)
+  __device__ __forceinline__ int grid() const { return args.grid; }
+  __device__ __forceinline__ bool split() const { return false; }
+  __device__ __forceinline__ int total_tiles() const {
+    return __builtin_amdgcn_readfirstlane(prefix[R * args.num_groups]);
+  }
+  __device__ __forceinline__ int tile_prefix(int c) const { return __builtin_amdgcn_readfirstlane(prefix[c]); }
+  // Last class whose first tile is <= tile (the prefix does not decrease, so
+  // the entries at or below `tile` are a leading run): one ballot over every
+  // 32nd entry, one over the 32 entries of the block it finds. Called with
+  // all 64 lanes of the wave active.
+  __device__ __forceinline__ int class_of_tile(int tile) const {
+    const int nc = R * args.num_groups;
+    const int lane = (int)(threadIdx.x & 63);
+    const int i0 = lane * 32;
+    const bool c0 = i0 < nc && prefix[i0] <= tile;
+    const int blk = __popcll(__ballot(c0)) - 1;
+    const int i1 = blk * 32 + (lane & 31);
+    const bool c1 = lane < 32 && i1 < nc && prefix[i1] <= tile;
+    return blk * 32 + __popcll(__ballot(c1)) - 1;
+  }
+  __device__ __forceinline__ ClassArgs cls(int c) const {
+    const int G = args.num_groups;
+    const int b = c / G, g = c - b * G;
+    ClassArgs r;
+    r.m = load_const(args.sizes, 4 * g + 0);
+    r.n = load_const(args.sizes, 4 * g + 1);
+    r.k = load_const(args.sizes, 4 * g + 2);
+    r.l = load_const(args.sizes, 4 * g + 3);
+    r.a = reinterpret_cast<const uint8_t*>(load_const(args.abc, 3 * g + 0));
+    r.b = reinterpret_cast<const uint8_t*>(load_const(args.abc, 3 * g + 1));
+    r.c = reinterpret_cast<uint16_t*>(load_const(args.abc, 3 * g + 2));
+    r.sfa = reinterpret_cast<const uint8_t*>(load_const(args.sf, 2 * g + 0));
+    r.sfb = reinterpret_cast<const uint8_t*>(load_const(args.sf, 2 * g + 1));
+    const int tiles_m = (r.m + BM - 1) / BM;
+    const int full = tiles_m - (last_row_class<BM>(r.m) > 0 ? 1 : 0);
+    r.tiles_m = b == 0 ? full : tiles_m - full;  // a class with tiles is never empty here
+    r.tm0 = b == 0 ? 0 : full;
+    r.tiles_n = (r.n + BN - 1) / BN;
+    r.nk = (r.k + kBK - 1) / kBK;
+    return r;
+  }
+  __device__ __forceinline__ int nk(int c) const {
+    const int g = c % args.num_groups;
+    return (load_const(args.sizes, 4 * g + 2) + kBK - 1) / kBK;
+  }
+};
+
+template <int BM, int BN, int WM, int WN, int NS, class Src>
 struct GemmKernel {
   static constexpr int MB = WM / 32;
   static constexpr int NB = WN / 32;
@@ -246,7 +355,7 @@ struct GemmKernel {
     f16x8 b[NB];
   };
 
-  const KernelArgs& args;
+  const Src src;
   uint8_t* smem;
   int wave, wm, wn, h, lr, lane;
   int vwg;  // this workgroup's virtual index
@@ -271,11 +380,11 @@ struct GemmKernel {
   // L2). The virtual index gives each XCD a contiguous run of indices, hence of
   // tiles (or units), which the raster below turns into compact 2-D blocks.
   __device__ __forceinline__ int virtual_wg(int b) const {
-    const int P = args.grid, q = P / kXcds, r = P % kXcds, x = b % kXcds;
+    const int P = src.grid(), q = P / kXcds, r = P % kXcds, x = b % kXcds;
     return x * q + (x < r ? x : r) + b / kXcds;
   }
 
-  __device__ GemmKernel(const KernelArgs& a, uint8_t* sm) : args(a), smem(sm) {
+  __device__ GemmKernel(const Src& s, uint8_t* sm) : src(s), smem(sm) {
     const int tid = threadIdx.x;
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -283,7 +392,7 @@ struct GemmKernel {
     wn = wave % WAVES_N;
     h = lane >> 5;
     lr = lane & 31;
-    vwg = blockIdx.x < (unsigned)a.grid ? virtual_wg(blockIdx.x) : 0;
+    vwg = blockIdx.x < (unsigned)s.grid() ? virtual_wg(blockIdx.x) : 0;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       a_base[kk] = lds_off(row_block(wm, 0) * 32 + lr, kk * 2 + h);
@@ -299,21 +408,21 @@ struct GemmKernel {
   // 506336 numbers them group by group; here a group may be two classes, and
   // heavier classes come first). A unit is one 128-K stage of one tile; units
   // are numbered tile by tile.
-  __device__ __forceinline__ int class_of_tile(int tile) const {
-    return search_prefix(args.tile_prefix, args.num_classes, tile);
-  }
-  __device__ __forceinline__ int total_tiles() const { return args.tile_prefix[args.num_classes]; }
-  __device__ __forceinline__ int64_t unit_begin(int wg) const { return args.wg_unit[wg]; }
+  __device__ __forceinline__ int class_of_tile(int tile) const { return src.class_of_tile(tile); }
+  __device__ __forceinline__ int total_tiles() const { return src.total_tiles(); }
+  // stream-K only (the by-value argument block)
+  __device__ __forceinline__ int64_t unit_begin(int wg) const { return src.args.wg_unit[wg]; }
   // the workgroup whose unit range holds unit u
   __device__ __forceinline__ int owner_of_unit(int64_t u) const {
-    int lo = 0, hi = args.grid - 1;  // last workgroup whose range starts at or before u
+    int lo = 0, hi = src.args.grid - 1;  // last workgroup whose range starts at or before u
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (args.wg_unit[mid] <= u) lo = mid; else hi = mid - 1;
+      if (src.args.wg_unit[mid] <= u) lo = mid; else hi = mid - 1;
     }
     return lo;
   }
   __device__ __forceinline__ int tile_of_unit(int64_t u, int* stage) const {
+    const KernelArgs& args = src.args;
     const int g = search_prefix(args.unit_prefix, args.num_classes, u);
     const int nk = args.cls[g].nk;
     const int local = (int)(u - args.unit_prefix[g]);
@@ -327,46 +436,53 @@ struct GemmKernel {
     if (!s.valid) return;
     int stage;
     s.tile = tile_of_unit(u, &stage);
-    const int nk = args.cls[class_of_tile(s.tile)].nk;
+    const int nk = src.nk(class_of_tile(s.tile));
     s.s0 = stage;
     s.s1 = (int)min((int64_t)nk, stage + (u_end - u));
   }
 
   __device__ __forceinline__ void first_segment(Segment& s) const {
-    if (args.split) {
-      locate(s, unit_begin(vwg), unit_begin(vwg + 1));
-    } else {
-      s.u = 0;
-      s.tile = vwg;
-      s.valid = s.tile < total_tiles();
-      s.s0 = 0;
-      s.s1 = s.valid ? args.cls[class_of_tile(s.tile)].nk : 0;
+    if constexpr (Src::kCanSplit) {
+      if (src.split()) {
+        locate(s, unit_begin(vwg), unit_begin(vwg + 1));
+        return;
+      }
     }
+    s.u = 0;
+    s.tile = vwg;
+    s.valid = s.tile < total_tiles();
+    s.s0 = 0;
+    s.s1 = s.valid ? src.nk(class_of_tile(s.tile)) : 0;
   }
 
   __device__ __forceinline__ void next_segment(Segment& s) const {
-    if (args.split) {
-      locate(s, s.u + (s.s1 - s.s0), unit_begin(vwg + 1));
-    } else {
+    if constexpr (Src::kCanSplit) {
+      if (src.split()) {
+        locate(s, s.u + (s.s1 - s.s0), unit_begin(vwg + 1));
+        return;
+      }
+    }
+    {
       // Round r hands tiles [r grid, (r + 1) grid) out forwards when r is
       // even and backwards when r is odd: tiles come heaviest first, so the
       // workgroups that drew the lightest tiles of one round draw the
       // heaviest of the next.
       const int r = (int)++s.u;
-      s.tile = r * args.grid + ((r & 1) ? args.grid - 1 - vwg : vwg);
+      const int P = src.grid();
+      s.tile = r * P + ((r & 1) ? P - 1 - vwg : vwg);
       s.valid = s.tile < total_tiles();
       s.s0 = 0;
-      s.s1 = s.valid ? args.cls[class_of_tile(s.tile)].nk : 0;
+      s.s1 = s.valid ? src.nk(class_of_tile(s.tile)) : 0;
     }
   }
 
   __device__ __forceinline__ TileCtx setup(int tile) const {
     const int gi = class_of_tile(tile);
-    const ClassArgs& G = args.cls[gi];
+    const ClassArgs& G = src.cls(gi);
     const int M = G.m, N = G.n, K = G.k;
     const int tiles_m = G.tiles_m;
     const int per_l = tiles_m * G.tiles_n;
-    const int rest = tile - args.tile_prefix[gi];
+    const int rest = tile - src.tile_prefix(gi);
     const int li = rest / per_l;
     const int r2 = rest - li * per_l;
     // Raster inside the group: super-columns of kRasterWidth n-tiles, taken
@@ -735,7 +851,7 @@ struct GemmKernel {
   // This workgroup computed stages [s0, s1) of a tile, not all of it: store the
   // fp32 partial sum; the reduction kernel adds the partials up.
   __device__ __forceinline__ void write_partial(const f32x16 (&acc)[MB][NB], bool first_seg) const {
-    uint8_t* slot = reinterpret_cast<uint8_t*>(args.partials) +
+    uint8_t* slot = reinterpret_cast<uint8_t*>(src.args.partials) +
                     ((size_t)vwg * 2 + (first_seg ? 0 : 1)) * TILE_FLOATS * 4;
 #pragma unroll
     for (int i = 0; i < MB; ++i)
@@ -755,6 +871,7 @@ struct GemmKernel {
     for (int i = 0; i < MB; ++i)
 #pragma unroll
       for (int j = 0; j < NB; ++j) zero[i][j] = f32x16{};
+    const KernelArgs& args = src.args;
     for (int gi = 0; gi < args.num_classes; ++gi) {
       if (args.cls[gi].nk != 0) continue;
       for (int tile = args.tile_prefix[gi] + vwg; tile < args.tile_prefix[gi + 1]; tile += args.grid)
@@ -779,13 +896,19 @@ struct GemmKernel {
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
       if (n > 0) mainloop_rows(acc, t, n, g0, ld);
-      if (seg.s0 == 0 && seg.s1 == t.nk) epilogue(acc, t);
-      else write_partial(acc, first_seg);
+      if constexpr (Src::kCanSplit) {
+        if (seg.s0 == 0 && seg.s1 == t.nk) epilogue(acc, t);
+        else write_partial(acc, first_seg);
+      } else {
+        epilogue(acc, t);  // whole tiles only
+      }
       g0 += n;
       first_seg = false;
       next_segment(seg);
     }
-    if (args.split) zero_k_tiles();
+    if constexpr (Src::kCanSplit) {
+      if (src.split()) zero_k_tiles();
+    }
     wait_vmem_all();  // no direct load may still be writing LDS when the workgroup ends
   }
 };
@@ -803,9 +926,136 @@ __device__ __forceinline__ const KernelArgs& kernel_args() {
 // swizzled by lds_off, the scale atoms are stored as in global memory.
 template <int BM, int BN, int WM, int WN, int NS>
 __global__ __launch_bounds__(kThreads, 1) void nvfp4_grouped_gemm_kernel(KernelArgs) {
-  using K = GemmKernel<BM, BN, WM, WN, NS>;
+  using K = GemmKernel<BM, BN, WM, WN, NS, KernargSrc>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[K::LDS_BYTES];
-  const K k(kernel_args(), smem);
+  const K k(KernargSrc{kernel_args()}, smem);
+  k.run();
+}
+
+// Tiles of one group of the device tables with BM x BN tiles, or -1 if the
+// group breaks a rule of the host-side validation (or has more than 2^20 tiles
+// of 128x128, which keeps the tile count of all groups within 2^30).
+__host__ __device__ inline bool bad_ptr(uint64_t p) { return p == 0 || (p & 15) != 0; }
+
+template <int BM, int BN>
+__host__ __device__ int64_t device_group_tiles(const int32_t* sz, const uint64_t* ptr) {
+  const int64_t m = sz[0], n = sz[1], k = sz[2], l = sz[3];
+  if (m < 0 || n < 0 || k < 0 || l < 1 || k % 64 != 0 || n % 8 != 0) return -1;
+  const int64_t lim = (int64_t(1) << 31) - 1;
+  if (k > (int64_t(1) << 22) || m > (int64_t(1) << 30) || n > (int64_t(1) << 30)) return -1;
+  if (m * (k / 2) > lim / l || n * (k / 2) > lim / l) return -1;
+  if ((m + 127) / 128 * 128 * (k / 16) > lim / l || (n + 127) / 128 * 128 * (k / 16) > lim / l) return -1;
+  if (m * n > (int64_t(1) << 40) / l) return -1;
+  if (m == 0 || n == 0) return 0;
+  if (bad_ptr(ptr[2])) return -1;  // C
+  if (k > 0 && (bad_ptr(ptr[0]) || bad_ptr(ptr[1]) || bad_ptr(ptr[3]) || bad_ptr(ptr[4]))) return -1;
+  if ((m + 127) / 128 * ((n + 127) / 128) * l > (int64_t(1) << 20)) return -1;
+  return (m + BM - 1) / BM * ((n + BN - 1) / BN) * l;
+}
+
+// prefix[c] = first tile of class c (see DeviceSrc), prefix[R G] = all tiles;
+// rejected groups own no tiles. Each thread takes G / 256 consecutive groups;
+// wave scans and the four wave totals give the offsets. Workgroup 0 stores the
+// number of rejected groups. Ends with a barrier.
+template <int BM, int BN>
+__device__ void build_device_prefix(const DeviceGroupArgs& a, int32_t* prefix, int32_t* wave_sums) {
+  constexpr int PER = kMaxDeviceGroups / kThreads;
+  constexpr int WAVES = kThreads / 64;
+  constexpr int R = BM / 64;
+  constexpr int V = R + 1;  // tiles per row class, then rejected groups
+  const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = a.num_groups;
+  // every table read first (one round trip), then the checks
+  int32_t sz[PER][4];
+  uint64_t ptr[PER][5];
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int g = min(tid * PER + q, G - 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sz[q][i] = a.sizes[4 * g + i];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) ptr[q][i] = a.abc[3 * g + i];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) ptr[q][3 + i] = a.sf[2 * g + i];
+  }
+  int32_t full[PER], last[PER], last_cls[PER];
+  int32_t v[V] = {};
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int g = tid * PER + q;
+    const int64_t x = g < G ? device_group_tiles<BM, BN>(sz[q], ptr[q]) : 0;
+    last_cls[q] = x > 0 ? last_row_class<BM>(sz[q][0]) : 0;
+    const int64_t row = x > 0 ? (int64_t)((sz[q][1] + BN - 1) / BN) * sz[q][3] : 0;  // tiles of one tile row
+    last[q] = last_cls[q] > 0 ? (int32_t)row : 0;
+    full[q] = x > 0 ? (int32_t)(x - last[q]) : 0;
+    v[0] += full[q];
+#pragma unroll
+    for (int b = 1; b < R; ++b) v[b] += last_cls[q] == b ? last[q] : 0;
+    v[R] += x < 0 ? 1 : 0;
+  }
+  int incl[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) incl[j] = v[j];
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int y = __shfl_up(incl[j], d);
+      if (lane >= d) incl[j] += y;
+    }
+  }
+  if (lane == 63) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) wave_sums[j * WAVES + wave] = incl[j];
+  }
+  __syncthreads();
+  int before[V] = {}, total[V] = {};
+#pragma unroll
+  for (int w = 0; w < WAVES; ++w)
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int x = wave_sums[j * WAVES + w];
+      before[j] += w < wave ? x : 0;
+      total[j] += x;
+    }
+  // run[b]: first tile of this thread's first group in class b
+  int run[R];
+  int base = 0;
+#pragma unroll
+  for (int b = 0; b < R; ++b) {
+    run[b] = base + before[b] + incl[b] - v[b];
+    base += total[b];
+  }
+#pragma unroll
+  for (int q = 0; q < PER; ++q) {
+    const int g = tid * PER + q;
+#pragma unroll
+    for (int b = 0; b < R; ++b) {
+      if (g < G) prefix[b * G + g] = run[b];
+      run[b] += b == 0 ? full[q] : (last_cls[q] == b ? last[q] : 0);
+    }
+  }
+  if (tid == 0) prefix[R * G] = base;
+  // (a wave-uniform test outside the one-thread branch: a test on the
+  // workgroup id inside it would make the id look lane-dependent below)
+  if (blockIdx.x == 0 && a.status != nullptr) {
+    if (tid == 0) *a.status = total[R];
+  }
+  __syncthreads();
+}
+
+template <int BM, int BN, int WM, int WN, int NS>
+__global__ __launch_bounds__(kThreads, 1) void nvfp4_grouped_gemm_device_kernel(DeviceGroupArgs) {
+  using Src = DeviceSrc<BM, BN>;
+  using K = GemmKernel<BM, BN, WM, WN, NS, Src>;
+  static_assert(K::LDS_BYTES + 4 * (kMaxDeviceClasses + 1 + (kMaxRowClasses + 1) * kThreads / 64) <= 160 * 1024,
+                "LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[K::LDS_BYTES];
+  __shared__ int32_t prefix[kMaxDeviceClasses + 1];
+  __shared__ int32_t wave_sums[(kMaxRowClasses + 1) * kThreads / 64];
+  const DeviceGroupArgs& args = *(const DeviceGroupArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  build_device_prefix<BM, BN>(args, prefix, wave_sums);
+  const K k(Src{args, prefix}, smem);
   k.run();
 }
 
@@ -821,12 +1071,12 @@ constexpr int kReduceChunkWords = kThreads * kReduceWordsPerThread;
 
 template <int BM, int BN, int WM, int WN, int NS>
 __global__ __launch_bounds__(kThreads) void nvfp4_streamk_reduce_kernel(KernelArgs) {
-  using K = GemmKernel<BM, BN, WM, WN, NS>;
+  using K = GemmKernel<BM, BN, WM, WN, NS, KernargSrc>;
   constexpr int WORDS = K::TILE_FLOATS / 4;
   constexpr int CHUNKS = WORDS / kReduceChunkWords;
   static_assert(WORDS % kReduceChunkWords == 0, "chunking");
   const KernelArgs& args = kernel_args();
-  const K k(args, nullptr);
+  const K k(KernargSrc{args}, nullptr);
   const int boundary = 1 + (int)(blockIdx.x / CHUNKS);  // workgroup whose range starts inside the tile
   const int chunk = (int)(blockIdx.x % CHUNKS);
   const int64_t ub = k.unit_begin(boundary);
@@ -891,13 +1141,16 @@ struct TileConfig {
   int bm, bn, wm, wn;
   void (*kernel)(KernelArgs);
   void (*reduce)(KernelArgs);
+  void (*device_kernel)(DeviceGroupArgs);
+  int64_t (*device_tiles)(const int32_t*, const uint64_t*);  // the device kernel's per-group check
 };
 
 constexpr int kStages = 4;  // LDS pipeline depth (4 x 36 KiB for 256x256 tiles)
 
 #define NVFP4_TILE_CONFIG(bm, bn, wm, wn)                                                       \
   { bm, bn, wm, wn, nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, kStages>,                     \
-    nvfp4_streamk_reduce_kernel<bm, bn, wm, wn, kStages> }
+    nvfp4_streamk_reduce_kernel<bm, bn, wm, wn, kStages>, nvfp4_grouped_gemm_device_kernel<bm, bn, wm, wn, kStages>, \
+    device_group_tiles<bm, bn> }
 const TileConfig kConfigs[] = {
     NVFP4_TILE_CONFIG(256, 256, 128, 128),
     NVFP4_TILE_CONFIG(128, 256, 64, 128),
@@ -906,6 +1159,7 @@ const TileConfig kConfigs[] = {
 };
 #undef NVFP4_TILE_CONFIG
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
+constexpr int kDefaultDeviceConfig = 2;  // 256x128 tiles for the device-table entry point
 
 thread_local int t_last_hip_error = 0;
 
@@ -1053,8 +1307,8 @@ size_t workspace_bytes_for(int cfg, int grid) {
 
 // Cost model, in units of one 128x128 tile-stage of MFMA work. Smaller wave
 // tiles dequantise more per MFMA; a tile costs a fixed prologue/epilogue on top
-// of its stages; a stream-K fixup costs a partial write plus, for the last
-// arriver, the reads of the other partials.
+// of its stages; a stream-K plan adds its partial stores and the reduction
+// kernel (plan_for).
 double tile_unit(int cfg) {
   const TileConfig& tc = kConfigs[cfg];
   const double size = (double)tc.bm * tc.bn / (128.0 * 128.0);
@@ -1243,10 +1497,11 @@ int sizes_ok(const int32_t* ps, int G) {
     if (k % 64 != 0 || n % 8 != 0) return NVFP4_ERR_INVALID;
     // The kernel addresses A, B and the scale tensors with 32-bit buffer
     // offsets: each must stay below 2^31 bytes, and k below 2^22.
+    // (x > lim / l stands for x * l > lim without overflowing)
     const int64_t lim = (int64_t(1) << 31) - 1;
-    if (k > (int64_t(1) << 22) || m * (k / 2) * l > lim || n * (k / 2) * l > lim ||
-        ceil_div64(m, 128) * 128 * (k / 16) * l > lim || ceil_div64(n, 128) * 128 * (k / 16) * l > lim ||
-        m > (int64_t(1) << 30) || n > (int64_t(1) << 30) || m * n * l > (int64_t(1) << 40))
+    if (k > (int64_t(1) << 22) || m > (int64_t(1) << 30) || n > (int64_t(1) << 30)) return NVFP4_ERR_INVALID;
+    if (m * (k / 2) > lim / l || n * (k / 2) > lim / l || ceil_div64(m, 128) * 128 * (k / 16) > lim / l ||
+        ceil_div64(n, 128) * 128 * (k / 16) > lim / l || m * n > (int64_t(1) << 40) / l)
       return NVFP4_ERR_INVALID;
     if (m == 0 || n == 0) continue;
     // tile and unit counts (of the smallest tile) stay within int32
@@ -1301,6 +1556,31 @@ int nvfp4_grouped_gemm_validate(const int32_t* ps, const uint64_t* abc, const ui
     }
   }
   return NVFP4_OK;
+}
+
+int nvfp4_grouped_gemm_device(const int32_t* d_ps, const uint64_t* d_abc, const uint64_t* d_sf, int G,
+                              int tile_config, int32_t* d_status, void* stream) {
+  if (G < 1 || G > kMaxDeviceGroups || d_ps == nullptr || d_abc == nullptr || d_sf == nullptr)
+    return NVFP4_ERR_INVALID;
+  if (!aligned16(reinterpret_cast<uint64_t>(d_ps)) || !aligned16(reinterpret_cast<uint64_t>(d_abc)) ||
+      !aligned16(reinterpret_cast<uint64_t>(d_sf)) || (reinterpret_cast<uint64_t>(d_status) & 3u) != 0)
+    return NVFP4_ERR_MISALIGNED;
+  if (tile_config < -1 || tile_config >= kNumConfigs) return NVFP4_ERR_CONFIG;
+  const int cfg = tile_config < 0 ? kDefaultDeviceConfig : tile_config;
+  int cus = 0;
+  const int crc = device_cu_count(&cus);
+  if (crc != NVFP4_OK) return crc;
+  const DeviceGroupArgs args{d_ps, d_abc, d_sf, d_status, G, cus};
+  hipLaunchKernelGGL(kConfigs[cfg].device_kernel, dim3(cus), dim3(kThreads), 0,
+                     reinterpret_cast<hipStream_t>(stream), args);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) { t_last_hip_error = (int)e; return NVFP4_ERR_HIP; }
+  return NVFP4_OK;
+}
+
+int64_t nvfp4_device_group_tiles(const int32_t* size, const uint64_t* ptrs, int tile_config) {
+  if (size == nullptr || ptrs == nullptr || tile_config < -1 || tile_config >= kNumConfigs) return -1;
+  return kConfigs[tile_config < 0 ? kDefaultDeviceConfig : tile_config].device_tiles(size, ptrs);
 }
 
 int nvfp4_num_tile_configs(void) { return kNumConfigs; }

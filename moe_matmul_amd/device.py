@@ -5,7 +5,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from ._binding import nvfp4_grouped_gemm_config, nvfp4_grouped_gemm_ex
+from ._binding import nvfp4_grouped_gemm_config, nvfp4_grouped_gemm_device, nvfp4_grouped_gemm_ex
 
 FP16_NAN_BITS = 0xFFFF
 
@@ -57,6 +57,25 @@ def run(shapes, dev_groups, stream=None, tile_config=-1, split_mode=None, worksp
         ws_bytes = 0 if workspace is None else workspace.numel()
         nvfp4_grouped_gemm_ex(shapes, abc, sf, len(shapes), ws_ptr, ws_bytes, tile_config,
                               -1 if split_mode is None else split_mode, stream)
+
+
+def device_tables(shapes, dev_groups, device="cuda"):
+    """The group tables of nvfp4_grouped_gemm_device as device tensors:
+    int32 [G][4] sizes, int64 [G][3] (A, B, C) and [G][2] (SFA, SFB) addresses."""
+    abc, sf = pointer_tables(dev_groups)
+    sizes = torch.tensor([list(s) for s in shapes], dtype=torch.int32).reshape(-1, 4)
+    as_i64 = lambda rows, w: torch.tensor(np.array(rows, dtype=np.uint64).reshape(-1, w).view(np.int64))
+    return sizes.to(device), as_i64(abc, 3).to(device), as_i64(sf, 2).to(device)
+
+
+def run_device(tables, num_groups, tile_config=-1, status=None, stream=None):
+    """Enqueue nvfp4_grouped_gemm_device over ``tables`` (see device_tables);
+    ``status`` is an int32 device tensor or None."""
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    sizes, abc, sf = tables
+    nvfp4_grouped_gemm_device(sizes.data_ptr(), abc.data_ptr(), sf.data_ptr(), num_groups, tile_config,
+                              0 if status is None else status.data_ptr(), stream)
 
 
 def workspace_for(shapes, device="cuda"):

@@ -90,3 +90,20 @@ def make_custom(shapes, seed: int, scale_codes: np.ndarray | None = None) -> lis
         sfb = pool[rng.integers(0, len(pool), size=sf_buffer_bytes(n, k, l))]
         out.append(dict(a=a, b=b, sfa=sfa, sfb=sfb))
     return out
+
+
+# The super-batch of the pages: the groups of 15 benchmark calls (each with up
+# to 8 groups, each call with its own data) merged into one launch.
+SUPER_BATCH_COPIES = 15
+
+
+def make_super_batch(index: int, copies: int = SUPER_BATCH_COPIES):
+    """``copies`` calls of workload ``index`` as one grouped problem: the same
+    per-group shapes repeated, each copy's bytes drawn from its own seed."""
+    shapes = workload_shapes(index)
+    all_shapes, groups = [], []
+    for c in range(copies):
+        rng = np.random.default_rng(1000 + index + 7919 * (c + 1))
+        all_shapes += shapes
+        groups += [draw_group(rng, *s) for s in shapes]
+    return all_shapes, groups

@@ -163,3 +163,72 @@ def test_ex_entry_point_checks_before_any_hip_call():
 def test_error_strings():
     for code in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(mm.nvfp4_error_string(code), str)
+
+
+@pytest.mark.parametrize("shapes", [
+    [(1 << 30, 1 << 10, 64, 1 << 30)],      # m*(k/2)*l would overflow int64
+    [(1 << 20, 1 << 20, 64, 1 << 25)],      # m*n*l would overflow int64
+    [(64, 64, 1 << 22, (1 << 31) - 1)],     # huge l
+])
+def test_validate_rejects_overflowing_products(shapes):
+    abc, sf = _ptrs(len(shapes))
+    assert mm.nvfp4_grouped_gemm_validate(shapes, abc, sf) == mm.NVFP4_ERR_INVALID
+
+
+def _group_ptrs(base=0x100000):
+    return [base, base + 0x1000, base + 0x2000, base + 0x3000, base + 0x4000]  # A, B, C, SFA, SFB
+
+
+def test_device_group_check_matches_host_rules():
+    """The per-group check the device-table kernel runs (host copy): the tiles
+    it gives a valid group, and -1 for every size or pointer rule the host
+    validation enforces."""
+    p = _group_ptrs()
+    for cfg in range(mm.nvfp4_num_tile_configs()):
+        info = mm.nvfp4_tile_config_info(cfg)
+        for (m, n, k, l) in [(300, 4096, 7168, 1), (1, 8, 64, 1), (129, 136, 0, 2), (0, 64, 64, 1), (64, 0, 64, 1)]:
+            want = 0 if m == 0 or n == 0 else -(-m // info["bm"]) * -(-n // info["bn"]) * l
+            assert mm.nvfp4_device_group_tiles((m, n, k, l), p, cfg) == want
+    default = mm.nvfp4_tile_config_info(2)
+    assert mm.nvfp4_device_group_tiles((300, 512, 64, 1), p) == -(-300 // default["bm"]) * -(-512 // default["bn"])
+    bad_sizes = [(128, 128, 96, 1), (128, 100, 128, 1), (-1, 128, 128, 1), (128, -8, 128, 1), (128, 128, -64, 1),
+                 (128, 128, 128, 0), (128, 128, 1 << 23, 1), (1 << 20, 128, 4096, 1), (64, 64, 1 << 22, (1 << 31) - 1),
+                 (1 << 20, 1 << 20, 64, 1 << 25), ((1 << 30) + 1, 8, 64, 1),
+                 ((1 << 17) + 128, 1 << 17, 64, 1)]  # more than 2^20 tiles of 128x128
+    for sz in bad_sizes:
+        abc = [(p[0], p[1], p[2])]
+        host = mm.nvfp4_grouped_gemm_validate([sz], abc, [(p[3], p[4])])
+        assert mm.nvfp4_device_group_tiles(sz, p) == -1, sz
+        if sz != ((1 << 17) + 128, 1 << 17, 64, 1):
+            assert host == mm.NVFP4_ERR_INVALID, sz
+    assert mm.nvfp4_device_group_tiles((1 << 17, 1 << 17, 64, 1), p) > 0  # exactly 2^20 tiles of 128x128
+    for i in range(5):  # null or misaligned A, B, C, SFA, SFB
+        for v in (0, p[i] + 8):
+            q = list(p)
+            q[i] = v
+            assert mm.nvfp4_device_group_tiles((64, 64, 64, 1), q) == -1
+            # k = 0 needs only C; empty groups need nothing
+            assert mm.nvfp4_device_group_tiles((64, 64, 0, 1), q) == (-1 if i == 2 else 1)
+            assert mm.nvfp4_device_group_tiles((0, 64, 64, 1), q) == 0
+    assert mm.nvfp4_device_group_tiles((64, 64, 64, 1), p, 99) == -1
+
+
+def test_device_entry_point_checks_before_any_hip_call():
+    lib = mm.load_library()
+    ok = 0x100000
+    cases = [
+        ((ok, ok, ok, 0, -1, 0), mm.NVFP4_ERR_INVALID),                      # no groups
+        ((ok, ok, ok, mm.NVFP4_MAX_DEVICE_GROUPS + 1, -1, 0), mm.NVFP4_ERR_INVALID),
+        ((0, ok, ok, 8, -1, 0), mm.NVFP4_ERR_INVALID),                       # null tables
+        ((ok, 0, ok, 8, -1, 0), mm.NVFP4_ERR_INVALID),
+        ((ok, ok, 0, 8, -1, 0), mm.NVFP4_ERR_INVALID),
+        ((ok + 8, ok, ok, 8, -1, 0), mm.NVFP4_ERR_MISALIGNED),               # tables 16-byte aligned
+        ((ok, ok + 8, ok, 8, -1, 0), mm.NVFP4_ERR_MISALIGNED),
+        ((ok, ok, ok + 8, 8, -1, 0), mm.NVFP4_ERR_MISALIGNED),
+        ((ok, ok, ok, 8, -1, ok + 2), mm.NVFP4_ERR_MISALIGNED),              # status 4-byte aligned
+        ((ok, ok, ok, 8, mm.nvfp4_num_tile_configs(), 0), mm.NVFP4_ERR_CONFIG),
+        ((ok, ok, ok, 8, -2, 0), mm.NVFP4_ERR_CONFIG),
+    ]
+    for (ps, abc, sf, g, cfg, status), code in cases:
+        rc = lib.nvfp4_grouped_gemm_device(ps, abc, sf, g, cfg, status, None)
+        assert rc == code, (ps, abc, sf, g, cfg, status, rc)
