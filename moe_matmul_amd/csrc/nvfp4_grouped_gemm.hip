@@ -130,10 +130,11 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 // Raw buffer resource (4 SGPRs): 48-bit base, stride 0, num_records bytes;
 // offsets at or past num_records read 0.
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, int64_t num_bytes) {
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, int32_t num_bytes) {
+  // 32-bit counts (every operand is validated below 2^31 bytes): scalar
+  // arithmetic, where 64-bit compares would go to the vector unit
   const uint64_t b = reinterpret_cast<uint64_t>(base);
-  const int n = num_bytes <= 0 ? 0 : (num_bytes >= 0x7fffffff ? 0x7fffffff : (int)num_bytes);
-  return i32x4{(int32_t)(uint32_t)b, (int32_t)((uint32_t)(b >> 32) & 0xFFFFu), n, kBufferWord3};
+  return i32x4{(int32_t)(uint32_t)b, (int32_t)((uint32_t)(b >> 32) & 0xFFFFu), max(num_bytes, 0), kBufferWord3};
 }
 
 // 16 bytes per lane from global (buffer, bounds-checked) straight into LDS at
@@ -181,9 +182,9 @@ constexpr int kSchedDSRead = 0x100;
 struct TileCtx {
   const uint8_t* a_tile;   // first byte of the tile's A rows
   const uint8_t* b_tile;
-  int64_t a_rem, b_rem;    // bytes from the tile base to the end of the operand
+  int32_t a_rem, b_rem;    // bytes from the tile base to the end of the operand (< 2^31)
   const uint8_t* sf_row;   // this wave's scale atom row (nullptr: none)
-  int64_t sf_rem;
+  int32_t sf_rem;
   uint16_t* c;             // C of the tile's batch
   int M, N, kbytes, nk, row0, col0;
 };
@@ -508,19 +509,19 @@ struct GemmKernel {
     t.col0 = tn * BN;
     t.a_tile = G.a + ((size_t)li * M + (size_t)tm * BM) * kbytes;
     t.b_tile = G.b + ((size_t)li * N + (size_t)tn * BN) * kbytes;
-    t.a_rem = (int64_t)(M - tm * BM) * kbytes;
-    t.b_rem = (int64_t)(N - tn * BN) * kbytes;
+    t.a_rem = (M - tm * BM) * kbytes;
+    t.b_rem = (N - tn * BN) * kbytes;
     t.c = G.c + (size_t)li * M * N;
     t.sf_row = nullptr;
     t.sf_rem = 0;
     if (wave < BM / 128) {
       const int atom = tm * (BM / 128) + wave;
       t.sf_row = G.sfa + ((size_t)li * Mt + atom) * Kt * kAtomBytes;
-      t.sf_rem = atom < Mt ? (int64_t)Kt * kAtomBytes : 0;
+      t.sf_rem = atom < Mt ? Kt * kAtomBytes : 0;
     } else if (wave < SF_ATOMS) {
       const int atom = tn * (BN / 128) + (wave - BM / 128);
       t.sf_row = G.sfb + ((size_t)li * Nt + atom) * Kt * kAtomBytes;
-      t.sf_rem = atom < Nt ? (int64_t)Kt * kAtomBytes : 0;
+      t.sf_rem = atom < Nt ? Kt * kAtomBytes : 0;
     }
     return t;
   }
@@ -582,11 +583,11 @@ struct GemmKernel {
     // the K offset goes into the resource base, so the range check also
     // zero-fills past the end of the last row
     const bool live = ld.seg.valid;
-    const int64_t kb0 = (int64_t)ld.stage * kRowBytes;
+    const int kb0 = ld.stage * kRowBytes;
     si.ra = uniform(make_rsrc(t.a_tile + kb0, live ? t.a_rem - kb0 : 0));
     si.rb = uniform(make_rsrc(t.b_tile + kb0, live ? t.b_rem - kb0 : 0));
     // two 64-K groups (1 KiB) of this wave's atom row; groups past k read 0
-    const int64_t q0 = (int64_t)ld.stage * 2 * kAtomBytes;
+    const int q0 = ld.stage * 2 * kAtomBytes;
     const bool has_sf = wave < SF_ATOMS;
     si.rs = uniform(make_rsrc(t.sf_row + q0, live && has_sf ? t.sf_rem - q0 : 0));
     si.sdst = has_sf ? si.st + A_BYTES + B_BYTES + wave * 1024 : lds0 + DUMMY_OFF;
