@@ -575,7 +575,7 @@ struct GemmKernel {
     const TileCtx& t = ld.ctx;
     StageIssue si;
     const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(smem);
-    si.st = lds0 + (uint32_t)((ld.issued % NS) * STAGE_BYTES);
+    si.st = lds0 + ((uint32_t)ld.issued % NS) * STAGE_BYTES;
     // Lane -> (row, chunk) of its 16 bytes in a 1 KiB direct load: 16 rows of 64
     // bytes; the physical chunk is lane & 3, the global chunk undoes the swizzle.
     si.voff = (wave * 16 + (lane >> 2)) * t.kbytes + (((lane & 3) ^ swz(lane >> 2)) << 4);
@@ -741,13 +741,13 @@ struct GemmKernel {
     Frags f0, f1;
     wait_vmem_all();  // stage g0 landed (and earlier C or partial stores are done)
     block_sync();
-    read_half<AMB>(r0, g0 % NS, 0);
+    read_half<AMB>(r0, (uint32_t)g0 % NS, 0);
     convert_scales<AMB>(s0, r0);
     dequant<0, AMB>(f0, r0, s0);
     for (int kt = 0; kt < n; ++kt) {
       const int g = g0 + kt;
       // ---- first half (K 0..63 of the stage): raw data in r0 ----
-      read_half<AMB>(r1, g % NS, 1);
+      read_half<AMB>(r1, (uint32_t)g % NS, 1);
       __builtin_amdgcn_sched_group_barrier(kSchedDSRead, AMB + NB + 1 + (AMB + 1) / 2, 0);
       step<1, false, AMB>(acc, f0, f1, r0, s0);
       step<2, false, AMB>(acc, f1, f0, r0, s0);
@@ -760,7 +760,7 @@ struct GemmKernel {
       wait_vmem<(NS - 2) * L>();
       block_sync();
       const StageIssue si = prep_issue(ld);
-      read_half<AMB>(r0, (g + 1) % NS, 0);  // unused after the last stage
+      read_half<AMB>(r0, (uint32_t)(g + 1) % NS, 0);  // unused after the last stage
       __builtin_amdgcn_sched_group_barrier(kSchedDSRead, AMB + NB + 1 + (AMB + 1) / 2, 0);
       step<1, false, AMB, 0, U1>(acc, f0, f1, r1, s1, &si);
       step<2, false, AMB, U1, U2>(acc, f1, f0, r1, s1, &si);
