@@ -76,7 +76,7 @@ extern "C" {
  *
  * Requirements, checked before any HIP call (else NVFP4_ERR_INVALID or
  * NVFP4_ERR_MISALIGNED, and nothing is launched):
- *   m, n, k >= 0, l >= 1; k % 64 == 0; n % 8 == 0; k <= 2^22; the bytes of
+ *   m, n, k >= 0, l >= 1; k % 32 == 0; n % 8 == 0; k <= 2^22; the bytes of
  *   each of A, B, SFA and SFB (all l batches) below 2^31; m*n*l <= 2^40.
  *   For a group with m > 0 and n > 0, C must be
  *   non-null and 16-byte aligned, and when k > 0 also A, B, SFA and SFB.

@@ -187,6 +187,11 @@ struct TileCtx {
   int32_t sf_rem;
   uint16_t* c;             // C of the tile's batch
   int M, N, kbytes, nk, row0, col0;
+  // k % 64 == 32: the last 64-K scale atom is half used; its 16-blocks 2 and
+  // 3 (bytes 2 and 3 of every 4-byte row word) are padding and may hold
+  // anything. kpad_group is the 64-K group of the last stage that holds that
+  // atom (0 or 1), -1 when k % 64 == 0.
+  int kpad_group;
 };
 
 // A run of 128-K stages [s0, s1) of one tile, processed by one workgroup.
@@ -314,7 +319,10 @@ struct DeviceSrc {
   }
 };
 
-template <int BM, int BN, int WM, int WN, int NS, class Src>
+// KPAD: the instantiation that can meet a k % 64 == 32 group (a tile's last
+// stage then needs its scales patched, a check per stage in the mainloop);
+// calls without such groups use the one without.
+template <int BM, int BN, int WM, int WN, int NS, class Src, bool KPAD = false>
 struct GemmKernel {
   static constexpr int MB = WM / 32;
   static constexpr int NB = WN / 32;
@@ -497,7 +505,7 @@ struct GemmKernel {
     const int tm = G.tm0 + in_sc / width;
     const int tn = sc * kRasterWidth + in_sc % width;
     const int kbytes = K >> 1;
-    const int Kt = K >> 6;
+    const int Kt = (K + 63) >> 6;  // scale atoms along K (the last may be half used)
     const int Mt = (M + 127) >> 7;
     const int Nt = (N + 127) >> 7;
     TileCtx t;
@@ -505,6 +513,7 @@ struct GemmKernel {
     t.N = N;
     t.kbytes = kbytes;
     t.nk = G.nk;
+    t.kpad_group = (K & 63) ? (K >> 6) & 1 : -1;
     t.row0 = tm * BM;
     t.col0 = tn * BN;
     t.a_tile = G.a + ((size_t)li * M + (size_t)tm * BM) * kbytes;
@@ -728,18 +737,36 @@ struct GemmKernel {
     __builtin_amdgcn_sched_barrier(0);
   }
 
+  // Zeroes the padding 16-blocks of a half-used last scale atom (bytes 2 and
+  // 3 of each of its 128 row words) in this wave's atom row of the stage in
+  // LDS buffer buf: after this wave's loads of the stage have landed, before
+  // the barrier after which every wave reads it. The A and B bytes past k in
+  // that stage (the next row's codes, or zeros past the end) are finite, so
+  // with zero scales they add exactly nothing.
+  __device__ __forceinline__ void zero_half_atom(uint32_t buf, int group) const {
+    if (wave >= SF_ATOMS) return;
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    u32x2* w = reinterpret_cast<u32x2*>(smem + buf * STAGE_BYTES + A_BYTES + B_BYTES + wave * 1024 +
+                                        group * kAtomBytes) + lane;
+    *w = *w & 0x0000FFFFu;
+  }
+
   // n stages of one segment, whose first stage is global stage g0. Every
   // iteration issues exactly one stage (L loads per wave), so on entry stages
   // up to g0 + NS - 1 are issued, and at the mid-stage wait of stage g the
-  // stages after g + 1 are exactly NS - 2.
+  // stages after g + 1 are exactly NS - 2. With KPAD, global stage kpad_g
+  // (or none, -1) is a tile's last stage with a half-used scale atom in 64-K
+  // group kpad_grp.
   template <int AMB>
-  __device__ __forceinline__ void mainloop(f32x16 (&acc)[MB][NB], int n, int g0, Loader& ld) const {
+  __device__ __forceinline__ void mainloop(f32x16 (&acc)[MB][NB], int n, int g0, Loader& ld, int kpad_g,
+                                           int kpad_grp) const {
     // split of a stage's L loads over the four steps of a half stage
     constexpr int U1 = (L + 3) / 4, U2 = U1 + (L - U1 + 2) / 3, U3 = U2 + (L - U2 + 1) / 2;
     Raw r0, r1;
     Scales s0, s1;
     Frags f0, f1;
     wait_vmem_all();  // stage g0 landed (and earlier C or partial stores are done)
+    if (KPAD && g0 == kpad_g) zero_half_atom((uint32_t)g0 % NS, kpad_grp);
     block_sync();
     read_half<AMB>(r0, (uint32_t)g0 % NS, 0);
     convert_scales<AMB>(s0, r0);
@@ -758,6 +785,7 @@ struct GemmKernel {
       // first half is read; every wave is done with stage g's buffer here, so
       // stage g + NS can take it.
       wait_vmem<(NS - 2) * L>();
+      if (KPAD && g + 1 == kpad_g) zero_half_atom((uint32_t)(g + 1) % NS, kpad_grp);
       block_sync();
       const StageIssue si = prep_issue(ld);
       read_half<AMB>(r0, (uint32_t)(g + 1) % NS, 0);  // unused after the last stage
@@ -773,17 +801,17 @@ struct GemmKernel {
 
   // Dispatch on this wave's active 32-row blocks (rows below m).
   __device__ __forceinline__ void mainloop_rows(f32x16 (&acc)[MB][NB], const TileCtx& t, int n, int g0,
-                                                Loader& ld) const {
+                                                Loader& ld, int kpad_g) const {
     const int rows = t.M - t.row0;
     const int nb = rows <= 0 ? 0 : (rows + 31) >> 5;  // row blocks of the tile below m
     const int amb = nb <= wm ? 0 : min(MB, (nb - wm + 1) >> 1);
     static_assert(MB <= 4, "active-block dispatch covers MB <= 4");
     switch (amb) {
-      case 0: mainloop<0>(acc, n, g0, ld); break;
-      case 1: mainloop<(MB >= 1 ? 1 : MB)>(acc, n, g0, ld); break;
-      case 2: mainloop<(MB >= 2 ? 2 : MB)>(acc, n, g0, ld); break;
-      case 3: mainloop<(MB >= 3 ? 3 : MB)>(acc, n, g0, ld); break;
-      default: mainloop<MB>(acc, n, g0, ld); break;
+      case 0: mainloop<0>(acc, n, g0, ld, kpad_g, t.kpad_group); break;
+      case 1: mainloop<(MB >= 1 ? 1 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group); break;
+      case 2: mainloop<(MB >= 2 ? 2 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group); break;
+      case 3: mainloop<(MB >= 3 ? 3 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group); break;
+      default: mainloop<MB>(acc, n, g0, ld, kpad_g, t.kpad_group); break;
     }
   }
 
@@ -896,7 +924,10 @@ struct GemmKernel {
       for (int i = 0; i < MB; ++i)
 #pragma unroll
         for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
-      if (n > 0) mainloop_rows(acc, t, n, g0, ld);
+      // the tile's last stage, if this segment ends the tile and its last
+      // scale atom is half used
+      const int kpad_g = KPAD && t.kpad_group >= 0 && seg.s1 == t.nk ? g0 + n - 1 : -1;
+      if (n > 0) mainloop_rows(acc, t, n, g0, ld, kpad_g);
       if constexpr (Src::kCanSplit) {
         if (seg.s0 == 0 && seg.s1 == t.nk) epilogue(acc, t);
         else write_partial(acc, first_seg);
@@ -925,9 +956,9 @@ __device__ __forceinline__ const KernelArgs& kernel_args() {
 // Stage layout in LDS (bytes): [A: BM rows x 64][B: BN rows x 64]
 // [scale atoms: (BM + BN) / 128 atom rows x 2 k-groups x 512]; A and B rows are
 // swizzled by lds_off, the scale atoms are stored as in global memory.
-template <int BM, int BN, int WM, int WN, int NS>
+template <int BM, int BN, int WM, int WN, int NS, bool KPAD>
 __global__ __launch_bounds__(kThreads, 1) void nvfp4_grouped_gemm_kernel(KernelArgs) {
-  using K = GemmKernel<BM, BN, WM, WN, NS, KernargSrc>;
+  using K = GemmKernel<BM, BN, WM, WN, NS, KernargSrc, KPAD>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[K::LDS_BYTES];
   const K k(KernargSrc{kernel_args()}, smem);
   k.run();
@@ -941,7 +972,7 @@ __host__ __device__ inline bool bad_ptr(uint64_t p) { return p == 0 || (p & 15) 
 template <int BM, int BN>
 __host__ __device__ int64_t device_group_tiles(const int32_t* sz, const uint64_t* ptr) {
   const int64_t m = sz[0], n = sz[1], k = sz[2], l = sz[3];
-  if (m < 0 || n < 0 || k < 0 || l < 1 || k % 64 != 0 || n % 8 != 0) return -1;
+  if (m < 0 || n < 0 || k < 0 || l < 1 || k % 32 != 0 || n % 8 != 0) return -1;
   const int64_t lim = (int64_t(1) << 31) - 1;
   if (k > (int64_t(1) << 22) || m > (int64_t(1) << 30) || n > (int64_t(1) << 30)) return -1;
   if (m * (k / 2) > lim / l || n * (k / 2) > lim / l) return -1;
@@ -1048,7 +1079,7 @@ __device__ void build_device_prefix(const DeviceGroupArgs& a, int32_t* prefix, i
 template <int BM, int BN, int WM, int WN, int NS>
 __global__ __launch_bounds__(kThreads, 1) void nvfp4_grouped_gemm_device_kernel(DeviceGroupArgs) {
   using Src = DeviceSrc<BM, BN>;
-  using K = GemmKernel<BM, BN, WM, WN, NS, Src>;
+  using K = GemmKernel<BM, BN, WM, WN, NS, Src, true>;  // the tables may hold any k
   static_assert(K::LDS_BYTES + 4 * (kMaxDeviceClasses + 1 + (kMaxRowClasses + 1) * kThreads / 64) <= 160 * 1024,
                 "LDS");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[K::LDS_BYTES];
@@ -1140,7 +1171,8 @@ __global__ __launch_bounds__(kThreads) void nvfp4_streamk_reduce_kernel(KernelAr
 
 struct TileConfig {
   int bm, bn, wm, wn;
-  void (*kernel)(KernelArgs);
+  void (*kernel)(KernelArgs);       // k % 64 == 0 in every group
+  void (*kernel_kpad)(KernelArgs);  // some group with k % 64 == 32
   void (*reduce)(KernelArgs);
   void (*device_kernel)(DeviceGroupArgs);
   int64_t (*device_tiles)(const int32_t*, const uint64_t*);  // the device kernel's per-group check
@@ -1149,7 +1181,8 @@ struct TileConfig {
 constexpr int kStages = 4;  // LDS pipeline depth (4 x 36 KiB for 256x256 tiles)
 
 #define NVFP4_TILE_CONFIG(bm, bn, wm, wn)                                                       \
-  { bm, bn, wm, wn, nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, kStages>,                     \
+  { bm, bn, wm, wn, nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, kStages, false>,              \
+    nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, kStages, true>,                                  \
     nvfp4_streamk_reduce_kernel<bm, bn, wm, wn, kStages>, nvfp4_grouped_gemm_device_kernel<bm, bn, wm, wn, kStages>, \
     device_group_tiles<bm, bn> }
 const TileConfig kConfigs[] = {
@@ -1478,7 +1511,9 @@ int launch(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, vo
   }
   if (tiles == 0 || plan.grid == 0) return NVFP4_OK;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(tc.kernel, dim3(plan.grid), dim3(kThreads), 0, st, args);
+  bool kpad = false;
+  for (int g = 0; g < G; ++g) kpad = kpad || (ps[4 * g + 2] % 64 != 0);
+  hipLaunchKernelGGL(kpad ? tc.kernel_kpad : tc.kernel, dim3(plan.grid), dim3(kThreads), 0, st, args);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && plan.split && plan.grid > 1) {
     const int chunks = tc.bm * tc.bn / 4 / kReduceChunkWords;
@@ -1495,7 +1530,7 @@ int sizes_ok(const int32_t* ps, int G) {
   for (int g = 0; g < G; ++g) {
     const int64_t m = ps[4 * g + 0], n = ps[4 * g + 1], k = ps[4 * g + 2], l = ps[4 * g + 3];
     if (m < 0 || n < 0 || k < 0 || l < 1) return NVFP4_ERR_INVALID;
-    if (k % 64 != 0 || n % 8 != 0) return NVFP4_ERR_INVALID;
+    if (k % 32 != 0 || n % 8 != 0) return NVFP4_ERR_INVALID;
     // The kernel addresses A, B and the scale tensors with 32-bit buffer
     // offsets: each must stay below 2^31 bytes, and k below 2^22.
     // (x > lim / l stands for x * l > lim without overflowing)

@@ -47,7 +47,7 @@ def test_validate_accepts_workloads():
 
 
 @pytest.mark.parametrize("shapes,code", [
-    ([(128, 128, 96, 1)], mm.NVFP4_ERR_INVALID),        # k % 64
+    ([(128, 128, 48, 1)], mm.NVFP4_ERR_INVALID),        # k % 32
     ([(128, 100, 128, 1)], mm.NVFP4_ERR_INVALID),       # n % 8
     ([(-1, 128, 128, 1)], mm.NVFP4_ERR_INVALID),
     ([(128, -8, 128, 1)], mm.NVFP4_ERR_INVALID),
@@ -90,6 +90,17 @@ def test_validate_alignment():
         sf2 = [list(sf[0])]
         sf2[0][col] += 4
         assert mm.nvfp4_grouped_gemm_validate(shapes, abc, sf2) == mm.NVFP4_ERR_MISALIGNED
+
+
+def test_validate_accepts_half_atom_k():
+    """k % 64 == 32 (the last 64-K scale atom half used) is accepted, k % 32 != 0 is not."""
+    abc, sf = _ptrs(1)
+    for k in (32, 96, 160, 7168 + 32):
+        assert mm.nvfp4_grouped_gemm_validate([(64, 64, k, 1)], abc, sf) == mm.NVFP4_OK, k
+        assert mm.nvfp4_device_group_tiles((64, 64, k, 1), _group_ptrs()) == 1, k
+    for k in (16, 48, 80, 112):
+        assert mm.nvfp4_grouped_gemm_validate([(64, 64, k, 1)], abc, sf) == mm.NVFP4_ERR_INVALID, k
+        assert mm.nvfp4_device_group_tiles((64, 64, k, 1), _group_ptrs()) == -1, k
 
 
 def test_validate_edge_semantics():
@@ -191,7 +202,7 @@ def test_device_group_check_matches_host_rules():
             assert mm.nvfp4_device_group_tiles((m, n, k, l), p, cfg) == want
     default = mm.nvfp4_tile_config_info(2)
     assert mm.nvfp4_device_group_tiles((300, 512, 64, 1), p) == -(-300 // default["bm"]) * -(-512 // default["bn"])
-    bad_sizes = [(128, 128, 96, 1), (128, 100, 128, 1), (-1, 128, 128, 1), (128, -8, 128, 1), (128, 128, -64, 1),
+    bad_sizes = [(128, 128, 80, 1), (128, 100, 128, 1), (-1, 128, 128, 1), (128, -8, 128, 1), (128, 128, -64, 1),
                  (128, 128, 128, 0), (128, 128, 1 << 23, 1), (1 << 20, 128, 4096, 1), (64, 64, 1 << 22, (1 << 31) - 1),
                  (1 << 20, 1 << 20, 64, 1 << 25), ((1 << 30) + 1, 8, 64, 1),
                  ((1 << 17) + 128, 1 << 17, 64, 1)]  # more than 2^20 tiles of 128x128

@@ -126,7 +126,7 @@ def test_device_rejects_bad_groups_and_leaves_their_c():
     announce("device tables with rejected groups")
     d = dev.upload(shapes, groups, c_guard=GUARD)
     sizes, abc, sf = dev.device_tables(shapes, d)
-    bad = {1: ("size", (96, 136, 192 + 32, 1)),   # k % 64
+    bad = {1: ("size", (96, 136, 240, 1)),        # k % 32
            2: ("size", (96, 132, 256, 1)),        # n % 8
            3: ("size", (96, 136, 256, 0)),        # l = 0
            5: ("abc", 2),                         # C misaligned by 2 bytes (inside its guard band)

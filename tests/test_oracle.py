@@ -230,7 +230,8 @@ def test_config_scale_codes_span_exponents():
 # Scale layout pins
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("rows,k,l", [(1, 64, 1), (128, 256, 1), (300, 512, 1), (129, 192, 2)])
+@pytest.mark.parametrize("rows,k,l", [(1, 64, 1), (128, 256, 1), (300, 512, 1), (129, 192, 2), (1, 32, 1),
+                                      (129, 96, 2), (300, 160, 1)])
 def test_sf_offset_matches_cute_layout(rows, k, l):
     mt = -(-rows // 128) * 128
     r = np.arange(mt)[:, None]
@@ -413,6 +414,30 @@ def test_negating_a_negates_c():
     c = O.grouped_gemm([(m, n, k, 1)], [g])[0]["c64"][0]
     cn = O.grouped_gemm([(m, n, k, 1)], [gn])[0]["c64"][0]
     assert np.array_equal(c, -cn)
+
+
+@pytest.mark.parametrize("k", [32, 96, 160])
+def test_half_atom_k_is_the_truncated_sum(k):
+    """k % 64 == 32: the result equals the integer oracle's (CuTe-evaluator
+    gather) and the oracle's own result for k + 32 with the extra 32 codes of
+    every row zero (their scales are the bytes of the last atom's unused half,
+    finite codes in these buffers)."""
+    m, n = 37, 24
+    grp = _rand_group(m, n, k, 96 + k)
+    out = O.grouped_gemm([(m, n, k, 1)], [grp])[0]
+    ref = int_oracle(m, n, k, grp["a"], grp["b"], grp["sfa"], grp["sfb"])
+    assert np.array_equal(out["c64"][0] * 2 ** 20, ref.astype(np.float64))
+    k2 = k + 32
+    assert synth.sf_buffer_bytes(m, k2) == synth.sf_buffer_bytes(m, k)  # same atoms, now fully used
+    ext = {}
+    for key, rows in (("a", m), ("b", n)):
+        x = np.zeros((1, rows, k2 // 2), np.uint8)
+        x[0, :, : k // 2] = grp[key][0]
+        ext[key] = x
+    for key in ("sfa", "sfb"):
+        ext[key] = grp[key].copy()
+    longer = O.grouped_gemm([(m, n, k2, 1)], [ext])[0]
+    assert np.array_equal(longer["c64"], out["c64"])
 
 
 def test_groups_are_independent():

@@ -29,17 +29,23 @@ def announce(msg):
 
 
 def poison_padding(shapes, groups):
-    """Copy of ``groups`` with every scale byte of rows >= m (n) set to 0x7F."""
+    """Copy of ``groups`` with every padding scale byte set to 0x7F (E4M3 NaN):
+    rows >= m (n) of the last 128-row atom, and, when k % 64 == 32, the two
+    unused 16-blocks of every row's last 64-K atom."""
     out = []
     for (m, n, k, l), g in zip(shapes, groups):
         g = dict(g)
         for key, rows in (("sfa", m), ("sfb", n)):
             buf = np.array(g[key], dtype=np.uint8, copy=True)
             pad_rows = np.arange(rows, -(-rows // 128) * 128)
-            if pad_rows.size and k:
-                kb = np.arange(k // 16)
-                for li in range(l):
+            all_rows = np.arange(-(-rows // 128) * 128)
+            for li in range(l):
+                if pad_rows.size and k:
+                    kb = np.arange(k // 16)
                     buf[O.sf_offset(pad_rows[:, None], kb[None, :], rows, k, li).reshape(-1)] = 0x7F
+                if k % 64 and all_rows.size:
+                    kb = np.array([k // 16, k // 16 + 1])
+                    buf[O.sf_offset(all_rows[:, None], kb[None, :], rows, k, li).reshape(-1)] = 0x7F
             g[key] = buf
         out.append(g)
     return out
@@ -110,6 +116,21 @@ def test_every_tile_config(cfg, split):
     for name in ("g8_ragged", "empty_groups_in_middle", "k_zero", "batch_l2"):
         shapes = EDGE_CASES[name]
         check(shapes, synth.make_custom(shapes, seed=77), tile_config=cfg, split_mode=split, label=name)
+
+
+@pytest.mark.parametrize("split", [0, 1])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+def test_half_atom_k(cfg, split):
+    """k % 64 == 32: the last 64-K scale atom is half used and its other half
+    (poisoned with NaN codes) must not count; the last stage holds 32 or 96
+    valid K of 128, in the first or the second 64-K group; groups of one call
+    mix k % 128 = 32, 96 and 0, and a long K splits over workgroups."""
+    if cfg >= mm.nvfp4_num_tile_configs():
+        pytest.skip("config not compiled")
+    shapes = [(97, 136, 32, 1), (129, 72, 96, 1), (33, 264, 160, 2), (256, 8, 224, 1), (40, 48, 128, 1),
+              (200, 136, 4096 + 96, 1)]
+    check(shapes, synth.make_custom(shapes, seed=3232 + cfg), tile_config=cfg, split_mode=split,
+          label="half-atom k")
 
 
 @pytest.mark.parametrize("split", [0, 1])
