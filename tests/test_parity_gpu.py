@@ -277,3 +277,30 @@ def test_empty_call_launches_nothing():
     d = dev.upload(shapes, groups)
     dev.run(shapes, d)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_problems(seed):
+    """Random calls (seeded): 1..8 groups, m in [0, 300], n a multiple of 8 up to
+    320, k a multiple of 32 up to 640 (k % 64 == 32 and k = 0 included), l in
+    {1, 2}; every tile configuration and split mode in turn, through the
+    by-value and the device-table entry points."""
+    rng = np.random.default_rng(9000 + seed)
+    for call in range(4):
+        g = int(rng.integers(1, 9))
+        shapes = [(int(rng.integers(0, 301)), 8 * int(rng.integers(0, 41)), 32 * int(rng.integers(0, 21)),
+                   int(rng.choice([1, 1, 1, 2]))) for _ in range(g)]
+        cfg = int(rng.integers(0, mm.nvfp4_num_tile_configs()))
+        split = [None, 0, 1][call % 3]
+        groups = synth.make_custom(shapes, seed=int(rng.integers(1 << 30)))
+        check(shapes, groups, tile_config=cfg, split_mode=split, label=f"random seed {seed} call {call}")
+        groups = poison_padding(shapes, groups)
+        d = dev.upload(shapes, groups, c_guard=GUARD)
+        status = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+        dev.run_device(dev.device_tables(shapes, d), len(shapes), tile_config=cfg, status=status)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0 and dev.guards_intact(d)
+        ref = O.grouped_gemm(shapes, groups)
+        for (m, n, k, l), c, r in zip(shapes, dev.c_as_numpy(shapes, d), ref):
+            if m and n:
+                assert not O.tolerance_violations(c, r["c16"], r["s"]).any(), (m, n, k, l)
