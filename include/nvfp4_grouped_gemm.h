@@ -39,7 +39,9 @@
  *
  * Ownership and threading: the caller owns every buffer. Host tables are read
  * before a call returns. Calls are stream-ordered and asynchronous. The
- * library's global state is a per-device cache of the compute-unit count and,
+ * library's global state is a per-device cache of the compute-unit count, a
+ * per-thread cache of the last eight plans (keyed by the problem sizes, the
+ * compute units and the forced choices; no buffer address is kept) and,
  * for nvfp4_grouped_gemm / nvfp4_grouped_gemm_config only, a stream-K
  * workspace per (device, stream) that the library allocates with hipMalloc on
  * first need (grown when a call needs more, kept until the process ends).

@@ -1428,6 +1428,42 @@ Plan choose_plan(const int32_t* ps, int G, int cus, int force_cfg, int force_spl
   return plan_for(ps, G, cus, force_cfg >= 0 ? force_cfg : 0, 0);
 }
 
+// The plan depends only on the sizes, the compute-unit count and the forced
+// choices, and choosing it (every configuration and mode modelled) costs
+// 10-25 us of host time for the larger calls; callers repeat the same sizes
+// with other buffers, so each thread keeps its last few plans.
+struct PlanKey {
+  int G, cus, cfg, split;
+  bool split_allowed;
+  int32_t sizes[4 * kMaxGroups];
+  bool operator==(const PlanKey& o) const {
+    return G == o.G && cus == o.cus && cfg == o.cfg && split == o.split && split_allowed == o.split_allowed &&
+           std::memcmp(sizes, o.sizes, sizeof(int32_t) * 4 * G) == 0;
+  }
+};
+
+Plan cached_plan(const int32_t* ps, int G, int cus, int force_cfg, int force_split, bool split_allowed) {
+  constexpr int kSlots = 8;
+  static thread_local PlanKey keys[kSlots];
+  static thread_local Plan plans[kSlots];
+  static thread_local int used = 0, next = 0;
+  PlanKey k{};
+  k.G = G;
+  k.cus = cus;
+  k.cfg = force_cfg;
+  k.split = force_split;
+  k.split_allowed = split_allowed;
+  std::memcpy(k.sizes, ps, sizeof(int32_t) * 4 * G);
+  for (int i = 0; i < used; ++i)
+    if (keys[i] == k) return plans[i];
+  const Plan p = choose_plan(ps, G, cus, force_cfg, force_split, split_allowed);
+  keys[next] = k;
+  plans[next] = p;
+  next = (next + 1) % kSlots;
+  used = used < kSlots ? used + 1 : kSlots;
+  return p;
+}
+
 bool aligned16(uint64_t p) { return (p & 15u) == 0; }
 
 // Library-owned stream-K workspaces, one per (device, stream), grown on demand
@@ -1558,14 +1594,14 @@ int run_call(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, 
   if (crc != NVFP4_OK) return crc;
   const bool can_split = internal_ws || workspace != nullptr;
   if (split == 1 && !can_split) return NVFP4_ERR_WORKSPACE;
-  Plan plan = choose_plan(ps, G, cus, cfg, split, can_split);
+  Plan plan = cached_plan(ps, G, cus, cfg, split, can_split);
   if (plan.split) {
     if (internal_ws) {
       const int wrc = internal_workspace(stream, plan.ws_bytes, &workspace);
       if (wrc != NVFP4_OK) return wrc;
     } else if (ws_bytes < plan.ws_bytes) {
       if (split == 1) return NVFP4_ERR_WORKSPACE;
-      plan = choose_plan(ps, G, cus, cfg, 0, false);  // too small: whole tiles instead
+      plan = cached_plan(ps, G, cus, cfg, 0, false);  // too small: whole tiles instead
     }
   }
   return launch(ps, abc, sf, G, stream, plan, workspace);
@@ -1639,7 +1675,7 @@ int nvfp4_launch_geometry(const int32_t* ps, int G, int num_cus, int cfg, int sp
                           int* grid, int* split_used, size_t* workspace_bytes) {
   if (sizes_ok(ps, G) != NVFP4_OK || num_cus < 1) return NVFP4_ERR_INVALID;
   if (cfg < -1 || cfg >= kNumConfigs || split < -1 || split > 1) return NVFP4_ERR_CONFIG;
-  const Plan p = choose_plan(ps, G, num_cus, cfg, split, true);
+  const Plan p = cached_plan(ps, G, num_cus, cfg, split, true);
   if (total_tiles) *total_tiles = p.tiles;
   if (grid) *grid = p.grid;
   if (split_used) *split_used = p.split;

@@ -243,3 +243,26 @@ def test_device_entry_point_checks_before_any_hip_call():
     for (ps, abc, sf, g, cfg, status), code in cases:
         rc = lib.nvfp4_grouped_gemm_device(ps, abc, sf, g, cfg, status, None)
         assert rc == code, (ps, abc, sf, g, cfg, status, rc)
+
+
+def test_plan_cache_returns_the_plan_of_the_sizes_asked_for():
+    """Plans are cached per thread by sizes (and compute units and forced
+    choices): interleaving many different size sets (more than the cache holds)
+    must return the same geometry as each set's first answer."""
+    sets = [synth.workload_shapes(i) for i in range(5)]
+    sets += [[(m, 136, 256, 1)] for m in (1, 33, 129, 300, 1000)]
+    sets += [[(64, 64, 64, l)] for l in (1, 2, 3)]
+    first = {}
+    for rep in range(3):
+        for i, shapes in enumerate(sets):
+            for cus in (256, 80):
+                for cfg, split in ((-1, -1), (0, 1), (3, 0)):
+                    geo = mm.nvfp4_launch_geometry(shapes, cus, cfg, split)
+                    key = (i, cus, cfg, split)
+                    if rep == 0:
+                        first[key] = geo
+                    assert geo == first[key], key
+    # the two group counts sharing a prefix of sizes are different problems
+    a = mm.nvfp4_launch_geometry([(256, 256, 1024, 1)], 256, 0, 0)
+    b = mm.nvfp4_launch_geometry([(256, 256, 1024, 1), (256, 256, 1024, 1)], 256, 0, 0)
+    assert a["total_tiles"] == 1 and b["total_tiles"] == 2
