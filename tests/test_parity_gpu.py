@@ -163,8 +163,9 @@ def test_heuristic_streamk_with_library_workspace():
 
 def test_streamk_plans_share_library_workspace():
     """Stream-K calls with different tile configurations (so different grids
-    and slot sizes) in a row on one stream share the library's workspace: each
-    must find its arrival counters at zero, not an earlier call's partials."""
+    and slot sizes) in a row on one stream share the library's workspace: the
+    slots of one call overlap those of the call before, and each call's
+    reduction must read only partials its own main kernel wrote."""
     shapes = [(256, 256, 16384, 1), (40, 136, 64, 1)]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     groups = synth.make_custom(shapes, seed=21)
@@ -243,8 +244,8 @@ def test_repeat_is_bitwise_deterministic_and_streams():
 def test_graph_replay_matches_eager(idx, split):
     """A call captured in a HIP graph and replayed several times, with eager
     work and synchronisation between the replays, writes exactly what the
-    eager call writes. Whole tiles, and stream-K with a caller workspace (its
-    arrival counters must be back at zero after every replay)."""
+    eager call writes. Whole tiles, and stream-K with a caller workspace (each
+    replay's reduction reads the partials of the same replay)."""
     shapes, groups = synth.make_workload(idx)
     announce(f"graph replay workload {idx} split {split}")
     d = dev.upload(shapes, groups)
