@@ -254,8 +254,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
-              "the grouped GEMM has no multi-GPU path", file=sys.stderr)
+        print(f"bench.py: one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "the grouped GEMM library has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
     import torch
