@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 
 METRIC = "TFLOPS (2·Σm·n·k) and µs/call per grouped-GEMM config; % of MFMA peak"
 PEAK_F16_TFLOPS = 2500.0  # MI355X dense f16/bf16 MFMA (published)
+PEAK_FP4_TFLOPS = 10100.0  # MI355X dense fp4 MFMA (published)
 PEAK_HBM_GBS = 8000.0
 COLD_BYTES = 1 << 30
 
@@ -57,10 +58,12 @@ def fmt_us(v):
 
 
 def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None, device_tables=False,
-                  super_batch=False):
+                  super_batch=False, pow2=False):
     """Times the grouped GEMM on workload ``idx``. ``device_tables``: through
     nvfp4_grouped_gemm_device (group tables in device memory); ``super_batch``:
-    the groups of 15 calls of the workload in one launch (device tables)."""
+    the groups of 15 calls of the workload in one launch (device tables);
+    ``pow2``: the workload with power-of-two scales through
+    nvfp4_grouped_gemm_pow2 (its status word checked afterwards)."""
     import torch
 
     import moe_matmul_amd as mm
@@ -68,7 +71,12 @@ def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None
     from moe_matmul_amd import synth
 
     device_tables = device_tables or super_batch
-    shapes, groups = synth.make_super_batch(idx) if super_batch else synth.make_workload(idx)
+    if super_batch:
+        shapes, groups = synth.make_super_batch(idx)
+    elif pow2:
+        shapes, groups = synth.make_workload(idx, scale_codes=synth.POW2_SCALE_CODES)
+    else:
+        shapes, groups = synth.make_workload(idx)
     base = dev.upload(shapes, groups)
     flops, nbytes = algorithmic(shapes)
     sets = [base]
@@ -85,8 +93,9 @@ def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None
     # argument tables marshalled once, so the timed loop measures the library
     (ps,) = mm.prepare(problem_sizes=shapes)
     ptrs = [mm.prepare(ptrs_abc=a, ptrs_sfa_sfb=f) for a, f in (dev.pointer_tables(s) for s in sets)]
-    ws = dev.workspace_for(shapes) if split_mode is not None else None
+    ws = dev.workspace_for(shapes) if (split_mode is not None or pow2) else None
     tables = [dev.device_tables(shapes, s) for s in sets] if device_tables else None
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
 
     def call(i, st=stream):
         if device_tables:
@@ -95,7 +104,10 @@ def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None
                                          0, st)
             return
         abc, sf = ptrs[i % len(ptrs)]
-        if split_mode is None:
+        if pow2:
+            mm.nvfp4_grouped_gemm_pow2(ps, abc, sf, status.data_ptr(), len(shapes), ws.data_ptr(), ws.numel(),
+                                       tile_config, -1 if split_mode is None else split_mode, st)
+        elif split_mode is None:
             mm.nvfp4_grouped_gemm_config(ps, abc, sf, len(shapes), st, tile_config)
         else:
             mm.nvfp4_grouped_gemm_ex(ps, abc, sf, len(shapes), ws.data_ptr(), ws.numel(), tile_config,
@@ -163,8 +175,12 @@ def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None
     name = synth.WORKLOADS[idx]["name"]
     if super_batch:
         name = f"superbatch{synth.SUPER_BATCH_COPIES}x_{name}"
+    if pow2:
+        name = f"{name}_pow2scales"
+        if int(status.item()) != 0:
+            raise RuntimeError(f"{name}: the power-of-two entry point reported a scale outside its set")
     return dict(
-        workload=name, device_tables=device_tables, shapes=[list(s) for s in shapes], flops=flops, bytes=nbytes,
+        workload=name, device_tables=device_tables, pow2=pow2, shapes=[list(s) for s in shapes], flops=flops, bytes=nbytes,
         total_ms=total_ms, wall_s=wall, ms_per_call=total_ms / steps,
         us_median=percentile(per, 50) * 1e3, us_p10=percentile(per, 10) * 1e3, us_p90=percentile(per, 90) * 1e3,
         tflops=flops / avg_s / 1e12, gbs=nbytes / avg_s / 1e9, sets=len(sets), tile_config=geo["config"],
@@ -242,6 +258,8 @@ def main():
     ap.add_argument("--all", action="store_true", help="also time every workload (to stderr / --out)")
     ap.add_argument("--super-batch", action="store_true",
                     help="also time 15 calls of workload 2 merged into one 120-group launch (device tables)")
+    ap.add_argument("--pow2", action="store_true",
+                    help="also time workloads 2-4 with power-of-two scales through nvfp4_grouped_gemm_pow2")
     ap.add_argument("--sweep", action="store_true",
                     help="time every workload under every tile configuration and split mode (to stderr / --out)")
     ap.add_argument("--out", default=None, help="write the per-workload details as JSON here")
@@ -298,6 +316,16 @@ def main():
                 f"{r['ms_per_call'] * 1e3:.1f} us/call, median {r['us_median']:.1f}, cfg {r['tile_config']}, "
                 f"{r['tiles']} tiles, graph replay {fmt_us(r['graph_us_per_call'])} us/call")
         details["all"] = allres
+    if args.all or args.pow2:
+        pres = []
+        for i in (2, 3, 4):
+            r = time_workload(i, max(20, args.steps // 2), 5, -1, cold=True, pow2=True)
+            pres.append(r)
+            log(f"[bench] workload {i} {r['workload']} (nvfp4_grouped_gemm_pow2): {r['tflops']:.1f} TFLOP/s, "
+                f"{r['ms_per_call'] * 1e3:.1f} us/call, median {r['us_median']:.1f}, cfg {r['tile_config']}, "
+                f"split {r['split']}, {r['tiles']} tiles, graph replay {fmt_us(r['graph_us_per_call'])} us/call, "
+                f"{100 * r['tflops'] / PEAK_FP4_TFLOPS:.1f}% of the FP4 MFMA peak")
+        details["pow2"] = pres
     if args.all or args.super_batch:
         sb = time_workload(2, max(10, args.steps // 10), 3, args.tile_config, cold=True, super_batch=True)
         log(f"[bench] super-batch {sb['workload']} ({len(sb['shapes'])} groups, device tables): "

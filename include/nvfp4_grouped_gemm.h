@@ -144,6 +144,37 @@ int nvfp4_grouped_gemm_device(const int32_t* d_problem_sizes, const uint64_t* d_
                               int32_t* d_status, void* stream);
 
 /*
+ * nvfp4_grouped_gemm_pow2 - the same grouped GEMM for scale tensors whose
+ * used scales are all zero or positive powers of two (the E4M3 codes 0x00,
+ * 0x01, 0x02, 0x04 and 0x08, 0x10, ..., 0x78: 0 and 2^-9 .. 2^8). Such a
+ * scale is an MX (E8M0) scale, so the block-scaled MMA runs as the FP4 matrix
+ * instruction with per-lane E8M0 scales and without dequantising. This is the
+ * MMA of my_kernel of submission 506336 (kernelindex.com "kernelbot nvfp4
+ * group gemm"), an MX/NV FP4 block-scaled operation whose scale type is a
+ * parameter, taken with MX-compatible scales at the NVFP4 16-element block.
+ * The results equal those of nvfp4_grouped_gemm to the same tolerance (every
+ * product is exact; fp32 accumulation order differs); a zero scale may turn
+ * an exact zero sum into -0.
+ *
+ *   Arguments as nvfp4_grouped_gemm_ex (same checks, same plans, allocates
+ *   nothing), plus
+ *   d_status  device int32, 4-byte aligned, not NULL. The kernel stores 1
+ *             there if a scale of a row below m (column below n) and a
+ *             16-block below k is not one of the codes above; it stores
+ *             nothing otherwise, so the caller clears it before the call.
+ *             With 1 there the C of the call is not valid: repeat it with
+ *             nvfp4_grouped_gemm. Padding rows of the scale tensors and the
+ *             16-blocks past k in a half-used last atom may hold anything.
+ * Calls that share d_status and may overlap in time report together.
+ * Returns NVFP4_ERR_INVALID for a NULL d_status, NVFP4_ERR_MISALIGNED for a
+ * misaligned one, else as nvfp4_grouped_gemm_ex.
+ */
+int nvfp4_grouped_gemm_pow2(const int32_t* problem_sizes, const uint64_t* ptrs_abc,
+                            const uint64_t* ptrs_sfa_sfb, int num_groups, int32_t* d_status,
+                            void* workspace, size_t workspace_bytes, int tile_config, int split_mode,
+                            void* stream);
+
+/*
  * nvfp4_device_group_tiles - the per-group check of nvfp4_grouped_gemm_device,
  * on the host (no HIP call): `size` = (m, n, k, l), `ptrs` = addresses of
  * (A, B, C, SFA, SFB). Returns the tiles the kernel gives the group with

@@ -54,6 +54,8 @@ def load_library() -> ctypes.CDLL:
                                                  i64p, ip, ip, ctypes.POINTER(ctypes.c_size_t)]),
         "nvfp4_grouped_gemm_ex": (ctypes.c_int, [i32p, u64p, u64p, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
                                                  ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
+        "nvfp4_grouped_gemm_pow2": (ctypes.c_int, [i32p, u64p, u64p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                                   ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
         "nvfp4_grouped_gemm_device": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                                      ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]),
         "nvfp4_device_group_tiles": (ctypes.c_int64, [i32p, u64p, ctypes.c_int]),
@@ -175,6 +177,22 @@ def nvfp4_grouped_gemm_ex(problem_sizes, ptrs_abc, ptrs_sfa_sfb, num_groups=None
                                    int(workspace_bytes), int(tile_config), int(split_mode), _stream(stream))
     if rc != NVFP4_OK:
         raise Nvfp4Error(rc, "nvfp4_grouped_gemm_ex")
+
+
+def nvfp4_grouped_gemm_pow2(problem_sizes, ptrs_abc, ptrs_sfa_sfb, d_status, num_groups=None, workspace=0,
+                            workspace_bytes=0, tile_config=-1, split_mode=-1, stream=None) -> None:
+    """Grouped GEMM for scales that are all zero or positive powers of two
+    (FP4 MFMA with E8M0 scales). ``d_status`` is the device address of an
+    int32 the caller clears; the kernel stores 1 there if a scale it used is
+    outside that set (then C is not valid)."""
+    lib = load_library()
+    ps, g = _sizes(problem_sizes)
+    g = g if num_groups is None else int(num_groups)
+    rc = lib.nvfp4_grouped_gemm_pow2(ps, _u64(ptrs_abc, 3), _u64(ptrs_sfa_sfb, 2), g, ctypes.c_void_p(int(d_status)),
+                                     ctypes.c_void_p(int(workspace)), int(workspace_bytes), int(tile_config),
+                                     int(split_mode), _stream(stream))
+    if rc != NVFP4_OK:
+        raise Nvfp4Error(rc, "nvfp4_grouped_gemm_pow2")
 
 
 def nvfp4_grouped_gemm_device(d_problem_sizes, d_ptrs_abc, d_ptrs_sfa_sfb, num_groups, tile_config=-1,

@@ -104,6 +104,9 @@ struct KernelArgs {
   // non-empty; the host sizes the ranges to equal modelled cost, since a stage
   // of a tile that is mostly past m costs less than a full one.
   int32_t wg_unit[kMaxSplitGrid + 1];
+  // power-of-two-scale kernels: set to 1 when a used scale is not zero or a
+  // positive power of two
+  int32_t* status;
 };
 static_assert(sizeof(KernelArgs) <= 4096, "kernel arguments must fit the kernarg segment");
 
@@ -127,6 +130,7 @@ __device__ __forceinline__ int swz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 
 __device__ __forceinline__ int lds_off(int r, int c) { return r * kRowBytes + ((c ^ swz(r)) << 4); }
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
 // Raw buffer resource (4 SGPRs): 48-bit base, stride 0, num_records bytes;
 // offsets at or past num_records read 0.
@@ -321,8 +325,10 @@ struct DeviceSrc {
 
 // KPAD: the instantiation that can meet a k % 64 == 32 group (a tile's last
 // stage then needs its scales patched, a check per stage in the mainloop);
-// calls without such groups use the one without.
-template <int BM, int BN, int WM, int WN, int NS, class Src, bool KPAD = false>
+// calls without such groups use the one without. MX: the mainloop for scales
+// that are all zero or positive powers of two (FP4 MFMA with E8M0 scales, no
+// dequantisation).
+template <int BM, int BN, int WM, int WN, int NS, class Src, bool KPAD = false, bool MX = false>
 struct GemmKernel {
   static constexpr int MB = WM / 32;
   static constexpr int NB = WN / 32;
@@ -799,6 +805,154 @@ struct GemmKernel {
     }
   }
 
+  // ---------------- power-of-two scales: FP4 MFMA with E8M0 scales ----------------
+  // v_mfma_scale_f32_32x32x64_f8f6f4 with E2M1 operands: lane l of an operand
+  // holds 32 codes (four dwords, low nibble first) of row l % 32 at K
+  // 32 (l / 32) .. +31 of the instruction, and one E8M0 scale for all 32 of
+  // them (checked on the MI355X); the result has the layout of the f16 MFMA.
+  // A lane's 16-byte chunk of a half stage spans two 16-blocks (2h, 2h+1),
+  // each with its own scale, so a block pair (i, j) takes two passes: pass p
+  // feeds the B chunk whole and the A chunk with only 16-block 2h + p (zeros
+  // in the other 16 K), with that 16-block's scales. An E4M3 scale that is
+  // a positive power of two is an E8M0 scale exactly, so every product is
+  // exact as in the f16 path. A zero scale becomes 2^-127: with a zero on
+  // both sides (the padding past k) the products vanish below fp32's range;
+  // with one zero side they stay below 2^-100, so they change no fp16 result
+  // (the other terms are multiples of 2^-20), except that an exact zero sum
+  // may come out as -0.
+  struct MxScales {
+    uint32_t a[MB];  // bytes 1 and 3: E8M0 of 16-blocks 2h and 2h+1 of the lane's row
+    uint32_t b[NB];
+  };
+
+  // E4M3 scales in bytes 0 and 1 of w -> two bf16 (exact), shifted left by
+  // one bit: bytes 1 and 3 are then the bf16 exponent fields, the E8M0 codes
+  // of zero and of positive powers of two. The bf16 bits are OR-ed into
+  // `seen`; a sign or mantissa bit there marks a scale outside that set.
+  __device__ __forceinline__ static uint32_t e8m0_pair(uint32_t w, uint32_t& seen) {
+    const uint32_t x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+    seen |= x;
+    return x << 1;
+  }
+
+  template <int AMB>
+  __device__ __forceinline__ void mx_scales(MxScales& s, const Raw& r, uint32_t& seen) const {
+    const int hshift = h * 16;
+#pragma unroll
+    for (int i = 0; i < AMB; ++i) {
+      const u32x4& c = r.sa[i >> 1];
+      s.a[i] = e8m0_pair(__builtin_amdgcn_perm(c[2 * (i & 1) + 1], c[2 * (i & 1)], sa_sel), seen);
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) s.b[j] = e8m0_pair(r.sb[j] >> hshift, seen);
+  }
+
+  // Pass P over block columns [J0, J1), after direct loads U0 .. U1-1 of the
+  // next stage (in a region of their own, as in the f16 steps).
+  template <int P, int J0, int J1, int AMB, int U0, int U1>
+  __device__ __forceinline__ void mx_sub(f32x16 (&acc)[MB][NB], const Raw& r, const MxScales& s,
+                                         const StageIssue* si) const {
+    if constexpr (U0 < U1) {
+      dma_range<U0, U1>(*si);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (AMB == 0) return;
+#pragma unroll
+    for (int i = 0; i < AMB; ++i) {
+      // opaque copy: otherwise the compiler rebuilds the dwords byte by byte
+      u32x4 ra = r.a[i];
+      asm volatile("" : "+v"(ra));
+      const i32x8 a = P == 0 ? i32x8{(int)ra[0], (int)ra[1], 0, 0, 0, 0, 0, 0}
+                             : i32x8{0, 0, (int)ra[2], (int)ra[3], 0, 0, 0, 0};
+#pragma unroll
+      for (int j = J0; j < J1; ++j) {
+        const i32x8 b = {(int)r.b[j][0], (int)r.b[j][1], (int)r.b[j][2], (int)r.b[j][3], 0, 0, 0, 0};
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b, a, acc[i][j], 4, 4, 2 * P + 1, (int)s.b[j],
+                                                                    2 * P + 1, (int)s.a[i]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // One half stage: its scales, then both passes in four parts (the second
+  // pass starts only after 2 * AMB * NB / 2 independent MFMAs), with the
+  // next stage's L direct loads spread over the parts when ISSUE.
+  template <int AMB, bool ISSUE>
+  __device__ __forceinline__ void mx_half(f32x16 (&acc)[MB][NB], const Raw& r, uint32_t& seen,
+                                          const StageIssue* si) const {
+    constexpr int U1 = ISSUE ? (L + 3) / 4 : 0, U2 = ISSUE ? U1 + (L - U1 + 2) / 3 : 0;
+    constexpr int U3 = ISSUE ? U2 + (L - U2 + 1) / 2 : 0, U4 = ISSUE ? L : 0;
+    constexpr int JH = NB / 2;
+    MxScales s;
+    if (AMB > 0) mx_scales<AMB>(s, r, seen);
+    mx_sub<0, 0, JH, AMB, 0, U1>(acc, r, s, si);
+    mx_sub<0, JH, NB, AMB, U1, U2>(acc, r, s, si);
+    mx_sub<1, 0, JH, AMB, U2, U3>(acc, r, s, si);
+    mx_sub<1, JH, NB, AMB, U3, U4>(acc, r, s, si);
+    // the half's MFMAs stay before what follows (the barrier): sunk past it,
+    // they would keep both halves' raw chunks live at once
+#pragma unroll
+    for (int i = 0; i < AMB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) asm volatile("" : "+a"(acc[i][j]));
+  }
+
+  // The MX counterpart of mainloop: the same stages, waits, barriers and
+  // direct loads; a half stage's raw chunks feed the MFMAs directly.
+  template <int AMB>
+  __device__ __forceinline__ void mainloop_mx(f32x16 (&acc)[MB][NB], int n, int g0, Loader& ld, int kpad_g,
+                                              int kpad_grp, uint32_t& seen) const {
+    static_assert(NB % 2 == 0, "two block-column parts per pass");
+    Raw r0, r1;
+    // The loader's sizes are used here, so that any reload of them from the
+    // spill area (after the epilogue, where register pressure peaks) comes
+    // before the wait below; a reload first waited for inside the loop costs
+    // a wait for every direct load in flight at each stage.
+    asm volatile("" : "+v"(ld.ctx.a_rem), "+v"(ld.ctx.b_rem), "+v"(ld.ctx.sf_rem), "+v"(ld.ctx.kbytes));
+    wait_vmem_all();  // stage g0 landed (and earlier C or partial stores are done)
+    if (KPAD && g0 == kpad_g) zero_half_atom((uint32_t)g0 % NS, kpad_grp);
+    block_sync();
+    read_half<AMB>(r0, (uint32_t)g0 % NS, 0);
+    for (int kt = 0; kt < n; ++kt) {
+      const int g = g0 + kt;
+      read_half<AMB>(r1, (uint32_t)g % NS, 1);
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, AMB + NB + 1 + (AMB + 1) / 2, 0);
+      mx_half<AMB, false>(acc, r0, seen, nullptr);
+      wait_vmem<(NS - 2) * L>();
+      if (KPAD && g + 1 == kpad_g) zero_half_atom((uint32_t)(g + 1) % NS, kpad_grp);
+      block_sync();
+      const StageIssue si = prep_issue(ld);
+      read_half<AMB>(r0, (uint32_t)(g + 1) % NS, 0);  // unused after the last stage
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, AMB + NB + 1 + (AMB + 1) / 2, 0);
+      mx_half<AMB, true>(acc, r1, seen, &si);
+      advance(ld);
+    }
+  }
+
+  __device__ __forceinline__ void mainloop_rows_mx(f32x16 (&acc)[MB][NB], const TileCtx& t, int n, int g0,
+                                                   Loader& ld, int kpad_g, uint32_t& seen) const {
+    const int rows = t.M - t.row0;
+    const int nb = rows <= 0 ? 0 : (rows + 31) >> 5;
+    const int amb = nb <= wm ? 0 : min(MB, (nb - wm + 1) >> 1);
+    switch (amb) {
+      case 0: mainloop_mx<0>(acc, n, g0, ld, kpad_g, t.kpad_group, seen); break;
+      case 1: mainloop_mx<(MB >= 1 ? 1 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group, seen); break;
+      case 2: mainloop_mx<(MB >= 2 ? 2 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group, seen); break;
+      case 3: mainloop_mx<(MB >= 3 ? 3 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group, seen); break;
+      default: mainloop_mx<MB>(acc, n, g0, ld, kpad_g, t.kpad_group, seen); break;
+    }
+  }
+
+  // After a segment's mainloop (so that nothing of it is live in the
+  // epilogue): whether any scale this wave converted (the rows of its active
+  // 32-row blocks, so also the padding rows of a scale tensor's last atom
+  // that share a block with rows below m or n) was not zero or a positive
+  // power of two. One register for all of it: a per-block account of which
+  // rows count would cost the hot loop eight. Any wave that saw one stores 1.
+  __device__ __forceinline__ void mx_report(uint32_t seen) const {
+    if (__builtin_amdgcn_ballot_w64((seen & 0x807F807Fu) != 0) != 0 && lane == 0) *src.args.status = 1;
+  }
+
   // Dispatch on this wave's active 32-row blocks (rows below m).
   __device__ __forceinline__ void mainloop_rows(f32x16 (&acc)[MB][NB], const TileCtx& t, int n, int g0,
                                                 Loader& ld, int kpad_g) const {
@@ -927,7 +1081,13 @@ struct GemmKernel {
       // the tile's last stage, if this segment ends the tile and its last
       // scale atom is half used
       const int kpad_g = KPAD && t.kpad_group >= 0 && seg.s1 == t.nk ? g0 + n - 1 : -1;
-      if (n > 0) mainloop_rows(acc, t, n, g0, ld, kpad_g);
+      if constexpr (MX) {
+        uint32_t seen = 0;  // bf16 bits of every scale converted
+        if (n > 0) mainloop_rows_mx(acc, t, n, g0, ld, kpad_g, seen);
+        mx_report(seen);
+      } else {
+        if (n > 0) mainloop_rows(acc, t, n, g0, ld, kpad_g);
+      }
       if constexpr (Src::kCanSplit) {
         if (seg.s0 == 0 && seg.s1 == t.nk) epilogue(acc, t);
         else write_partial(acc, first_seg);
@@ -956,9 +1116,9 @@ __device__ __forceinline__ const KernelArgs& kernel_args() {
 // Stage layout in LDS (bytes): [A: BM rows x 64][B: BN rows x 64]
 // [scale atoms: (BM + BN) / 128 atom rows x 2 k-groups x 512]; A and B rows are
 // swizzled by lds_off, the scale atoms are stored as in global memory.
-template <int BM, int BN, int WM, int WN, int NS, bool KPAD>
+template <int BM, int BN, int WM, int WN, int NS, bool KPAD, bool MX = false>
 __global__ __launch_bounds__(kThreads, 1) void nvfp4_grouped_gemm_kernel(KernelArgs) {
-  using K = GemmKernel<BM, BN, WM, WN, NS, KernargSrc, KPAD>;
+  using K = GemmKernel<BM, BN, WM, WN, NS, KernargSrc, KPAD, MX>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[K::LDS_BYTES];
   const K k(KernargSrc{kernel_args()}, smem);
   k.run();
@@ -1173,6 +1333,8 @@ struct TileConfig {
   int bm, bn, wm, wn;
   void (*kernel)(KernelArgs);       // k % 64 == 0 in every group
   void (*kernel_kpad)(KernelArgs);  // some group with k % 64 == 32
+  void (*kernel_mx)(KernelArgs);    // power-of-two scales
+  void (*kernel_mx_kpad)(KernelArgs);
   void (*reduce)(KernelArgs);
   void (*device_kernel)(DeviceGroupArgs);
   int64_t (*device_tiles)(const int32_t*, const uint64_t*);  // the device kernel's per-group check
@@ -1183,6 +1345,8 @@ constexpr int kStages = 4;  // LDS pipeline depth (4 x 36 KiB for 256x256 tiles)
 #define NVFP4_TILE_CONFIG(bm, bn, wm, wn)                                                       \
   { bm, bn, wm, wn, nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, kStages, false>,              \
     nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, kStages, true>,                                  \
+    nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, kStages, false, true>,                           \
+    nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, kStages, true, true>,                            \
     nvfp4_streamk_reduce_kernel<bm, bn, wm, wn, kStages>, nvfp4_grouped_gemm_device_kernel<bm, bn, wm, wn, kStages>, \
     device_group_tiles<bm, bn> }
 const TileConfig kConfigs[] = {
@@ -1506,7 +1670,7 @@ int internal_workspace(void* stream, size_t need, void** out) {
 }
 
 int launch(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, void* stream, const Plan& plan,
-           void* workspace) {
+           void* workspace, int32_t* mx_status) {
   const TileConfig& tc = kConfigs[plan.cfg];
   KernelArgs args;
   std::memset(&args, 0, sizeof(args));
@@ -1541,6 +1705,7 @@ int launch(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, vo
   args.num_classes = nc > 0 ? nc : 1;
   args.split = plan.split;
   args.grid = plan.grid;
+  args.status = mx_status;
   if (plan.split) {
     args.partials = reinterpret_cast<float*>(workspace);
     split_ranges(cls, nc, plan.grid, args.wg_unit);
@@ -1549,7 +1714,8 @@ int launch(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, vo
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   bool kpad = false;
   for (int g = 0; g < G; ++g) kpad = kpad || (ps[4 * g + 2] % 64 != 0);
-  hipLaunchKernelGGL(kpad ? tc.kernel_kpad : tc.kernel, dim3(plan.grid), dim3(kThreads), 0, st, args);
+  void (*kernel)(KernelArgs) = mx_status ? (kpad ? tc.kernel_mx_kpad : tc.kernel_mx) : (kpad ? tc.kernel_kpad : tc.kernel);
+  hipLaunchKernelGGL(kernel, dim3(plan.grid), dim3(kThreads), 0, st, args);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && plan.split && plan.grid > 1) {
     const int chunks = tc.bm * tc.bn / 4 / kReduceChunkWords;
@@ -1584,8 +1750,9 @@ int sizes_ok(const int32_t* ps, int G) {
   return NVFP4_OK;
 }
 
+// mx_status: non-null selects the power-of-two-scale kernels, which report there.
 int run_call(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, void* stream, int cfg, int split,
-             void* workspace, size_t ws_bytes, bool internal_ws) {
+             void* workspace, size_t ws_bytes, bool internal_ws, int32_t* mx_status = nullptr) {
   const int rc = nvfp4_grouped_gemm_validate(ps, abc, sf, G);
   if (rc != NVFP4_OK) return rc;
   if (cfg < -1 || cfg >= kNumConfigs || split < -1 || split > 1) return NVFP4_ERR_CONFIG;
@@ -1604,7 +1771,7 @@ int run_call(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, 
       plan = cached_plan(ps, G, cus, cfg, 0, false);  // too small: whole tiles instead
     }
   }
-  return launch(ps, abc, sf, G, stream, plan, workspace);
+  return launch(ps, abc, sf, G, stream, plan, workspace, mx_status);
 }
 
 }  // namespace
@@ -1707,6 +1874,14 @@ int nvfp4_grouped_gemm_ex(const int32_t* ps, const uint64_t* abc, const uint64_t
                           size_t workspace_bytes, int tile_config, int split_mode, void* stream) {
   if (workspace != nullptr && (reinterpret_cast<uint64_t>(workspace) & 255u) != 0) return NVFP4_ERR_MISALIGNED;
   return run_call(ps, abc, sf, G, stream, tile_config, split_mode, workspace, workspace_bytes, false);
+}
+
+int nvfp4_grouped_gemm_pow2(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, int32_t* d_status,
+                            void* workspace, size_t workspace_bytes, int tile_config, int split_mode, void* stream) {
+  if (d_status == nullptr) return NVFP4_ERR_INVALID;
+  if ((reinterpret_cast<uint64_t>(d_status) & 3u) != 0) return NVFP4_ERR_MISALIGNED;
+  if (workspace != nullptr && (reinterpret_cast<uint64_t>(workspace) & 255u) != 0) return NVFP4_ERR_MISALIGNED;
+  return run_call(ps, abc, sf, G, stream, tile_config, split_mode, workspace, workspace_bytes, false, d_status);
 }
 
 size_t nvfp4_sf_bytes(int rows, int k, int l) {

@@ -5,7 +5,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from ._binding import nvfp4_grouped_gemm_config, nvfp4_grouped_gemm_device, nvfp4_grouped_gemm_ex
+from ._binding import (nvfp4_grouped_gemm_config, nvfp4_grouped_gemm_device, nvfp4_grouped_gemm_ex,
+                       nvfp4_grouped_gemm_pow2)
 
 FP16_NAN_BITS = 0xFFFF
 
@@ -57,6 +58,19 @@ def run(shapes, dev_groups, stream=None, tile_config=-1, split_mode=None, worksp
         ws_bytes = 0 if workspace is None else workspace.numel()
         nvfp4_grouped_gemm_ex(shapes, abc, sf, len(shapes), ws_ptr, ws_bytes, tile_config,
                               -1 if split_mode is None else split_mode, stream)
+
+
+def run_pow2(shapes, dev_groups, status, stream=None, tile_config=-1, split_mode=-1, workspace=None):
+    """Enqueue nvfp4_grouped_gemm_pow2 (scales all zero or powers of two);
+    ``status`` is an int32 device tensor the caller has cleared, ``workspace``
+    a uint8 device tensor or None (then whole tiles)."""
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    abc, sf = pointer_tables(dev_groups)
+    ws_ptr = 0 if workspace is None else workspace.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    nvfp4_grouped_gemm_pow2(shapes, abc, sf, status.data_ptr(), len(shapes), ws_ptr, ws_bytes, tile_config,
+                            split_mode, stream)
 
 
 def device_tables(shapes, dev_groups, device="cuda"):

@@ -28,6 +28,9 @@ import numpy as np
 
 # The 56 E4M3 codes (exponent field 4..10, any mantissa): positive and finite.
 SCALE_CODES = np.array([(e << 3) | mnt for e in range(4, 11) for mnt in range(8)], dtype=np.uint8)
+# The 7 of them with mantissa 0 (2^-3 .. 2^3): MX-compatible scales, for the
+# power-of-two entry point's workloads.
+POW2_SCALE_CODES = np.array([e << 3 for e in range(4, 11)], dtype=np.uint8)
 
 # (name, per-group (m, n, k, l) or None when m is drawn, n, k)
 WORKLOADS = {
@@ -56,17 +59,20 @@ def workload_shapes(index: int, seed: int | None = None) -> list[tuple[int, int,
     return [(int(m), w["n"], w["k"], 1) for m in ms]
 
 
-def draw_group(rng: np.random.Generator, m: int, n: int, k: int, l: int = 1) -> dict:
+def draw_group(rng: np.random.Generator, m: int, n: int, k: int, l: int = 1, scale_codes=SCALE_CODES) -> dict:
     """Random bytes of one group: packed A, packed B and the two scale buffers."""
     a = rng.integers(0, 256, size=(l, m, k // 2), dtype=np.uint8)
     b = rng.integers(0, 256, size=(l, n, k // 2), dtype=np.uint8)
-    sfa = SCALE_CODES[rng.integers(0, len(SCALE_CODES), size=sf_buffer_bytes(m, k, l))]
-    sfb = SCALE_CODES[rng.integers(0, len(SCALE_CODES), size=sf_buffer_bytes(n, k, l))]
+    sfa = scale_codes[rng.integers(0, len(scale_codes), size=sf_buffer_bytes(m, k, l))]
+    sfb = scale_codes[rng.integers(0, len(scale_codes), size=sf_buffer_bytes(n, k, l))]
     return dict(a=a, b=b, sfa=sfa, sfb=sfb)
 
 
-def make_workload(index: int, seed: int | None = None) -> tuple[list[tuple[int, int, int, int]], list[dict]]:
-    """Seeded workload ``index``: (problem_sizes, per-group byte arrays)."""
+def make_workload(index: int, seed: int | None = None,
+                  scale_codes=SCALE_CODES) -> tuple[list[tuple[int, int, int, int]], list[dict]]:
+    """Seeded workload ``index``: (problem_sizes, per-group byte arrays).
+    ``scale_codes``: the pool the scale bytes are drawn from (POW2_SCALE_CODES
+    for the power-of-two variant of a workload: same shapes, same m draw)."""
     rng = np.random.default_rng(1000 + index if seed is None else seed)
     w = WORKLOADS[index]
     if "shapes" in w:
@@ -74,7 +80,7 @@ def make_workload(index: int, seed: int | None = None) -> tuple[list[tuple[int, 
     else:
         ms = rng.integers(40, 401, size=w["groups"])
         shapes = [(int(m), w["n"], w["k"], 1) for m in ms]
-    groups = [draw_group(rng, *s) for s in shapes]
+    groups = [draw_group(rng, *s, scale_codes=np.asarray(scale_codes, dtype=np.uint8)) for s in shapes]
     return shapes, groups
 
 

@@ -171,6 +171,25 @@ def test_ex_entry_point_checks_before_any_hip_call():
     assert e.value.code == mm.NVFP4_ERR_INVALID
 
 
+def test_pow2_entry_point_checks_before_any_hip_call():
+    """nvfp4_grouped_gemm_pow2: a status word is required (non-null, 4-byte
+    aligned); then the checks of nvfp4_grouped_gemm_ex apply."""
+    shapes = [(128, 128, 128, 1)]
+    abc, sf = _ptrs(1)
+    cases = [(dict(d_status=0), mm.NVFP4_ERR_INVALID),
+             (dict(d_status=0x10002), mm.NVFP4_ERR_MISALIGNED),
+             (dict(d_status=0x10000, workspace=0x10010, workspace_bytes=1 << 20), mm.NVFP4_ERR_MISALIGNED),
+             (dict(d_status=0x10000, split_mode=3), mm.NVFP4_ERR_CONFIG),
+             (dict(d_status=0x10000, tile_config=9), mm.NVFP4_ERR_CONFIG)]
+    for kw, code in cases:
+        with pytest.raises(mm.Nvfp4Error) as e:
+            mm.nvfp4_grouped_gemm_pow2(shapes, abc, sf, **kw)
+        assert e.value.code == code, kw
+    with pytest.raises(mm.Nvfp4Error) as e:
+        mm.nvfp4_grouped_gemm_pow2([(128, 100, 128, 1)], abc, sf, d_status=0x10000)
+    assert e.value.code == mm.NVFP4_ERR_INVALID
+
+
 def test_error_strings():
     for code in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(mm.nvfp4_error_string(code), str)
