@@ -847,23 +847,49 @@ struct GemmKernel {
     for (int j = 0; j < NB; ++j) s.b[j] = e8m0_pair(r.sb[j] >> hshift, seen);
   }
 
-  // Pass P over block columns [J0, J1), after direct loads U0 .. U1-1 of the
-  // next stage (in a region of their own, as in the f16 steps).
-  template <int P, int J0, int J1, int AMB, int U0, int U1>
-  __device__ __forceinline__ void mx_sub(f32x16 (&acc)[MB][NB], const Raw& r, const MxScales& s,
-                                         const StageIssue* si) const {
+  // Operands of a half stage's first pass, prepared during the half before:
+  // the A operands (the chunk's first 16-block, zeros above) and the scales.
+  struct MxOps {
+    u32x4 t[MB];
+    MxScales s;
+  };
+
+  // Each A operand goes through an empty asm: built straight from the loaded
+  // chunk, the compiler reassembles its dwords byte by byte.
+  template <int AMB>
+  __device__ __forceinline__ static void mx_pass0_operands(u32x4 (&t)[MB], const Raw& r) {
+#pragma unroll
+    for (int i = 0; i < AMB; ++i) {
+      t[i] = u32x4{r.a[i][0], r.a[i][1], 0u, 0u};
+      asm volatile("" : "+v"(t[i]));
+    }
+  }
+  // ... and zeros, then the second 16-block (in the chunk's own registers).
+  template <int AMB>
+  __device__ __forceinline__ static void mx_pass1_operands(u32x4 (&t)[MB], const Raw& r) {
+#pragma unroll
+    for (int i = 0; i < AMB; ++i) {
+      t[i] = u32x4{0u, 0u, r.a[i][2], r.a[i][3]};
+      asm volatile("" : "+v"(t[i]));
+    }
+  }
+
+  // One quarter of a half stage: pass P over block columns [J0, J1) with A
+  // operands ta, after direct loads U0 .. U1-1 of the next stage (in a region
+  // of their own, as in the f16 steps); the VALU work `work` emits (VALU
+  // instructions, about) is spread between the MFMAs.
+  template <int P, int J0, int J1, int AMB, int U0, int U1, int VALU, class Work>
+  __device__ __forceinline__ void mx_sub(f32x16 (&acc)[MB][NB], const u32x4 (&ta)[MB], const Raw& r,
+                                         const MxScales& s, const StageIssue* si, Work&& work) const {
     if constexpr (U0 < U1) {
       dma_range<U0, U1>(*si);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (AMB == 0) return;
+    work();
 #pragma unroll
     for (int i = 0; i < AMB; ++i) {
-      // opaque copy: otherwise the compiler rebuilds the dwords byte by byte
-      u32x4 ra = r.a[i];
-      asm volatile("" : "+v"(ra));
-      const i32x8 a = P == 0 ? i32x8{(int)ra[0], (int)ra[1], 0, 0, 0, 0, 0, 0}
-                             : i32x8{0, 0, (int)ra[2], (int)ra[3], 0, 0, 0, 0};
+      const i32x8 a = {(int)ta[i][0], (int)ta[i][1], (int)ta[i][2], (int)ta[i][3], 0, 0, 0, 0};
 #pragma unroll
       for (int j = J0; j < J1; ++j) {
         const i32x8 b = {(int)r.b[j][0], (int)r.b[j][1], (int)r.b[j][2], (int)r.b[j][3], 0, 0, 0, 0};
@@ -871,26 +897,41 @@ struct GemmKernel {
                                                                     2 * P + 1, (int)s.a[i]);
       }
     }
+    constexpr int N = AMB * (J1 - J0);
+    constexpr int PER = (VALU + N - 1) / (N > 0 ? N : 1);
+#pragma unroll
+    for (int q = 0; q < N; ++q) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+      if constexpr (PER > 0) __builtin_amdgcn_sched_group_barrier(kSchedVALU, PER, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // One half stage: its scales, then both passes in four parts (the second
-  // pass starts only after 2 * AMB * NB / 2 independent MFMAs), with the
-  // next stage's L direct loads spread over the parts when ISSUE.
+  // One half stage on `cur` with its prepared operands `o`, in four quarters
+  // (the second pass starts after AMB * NB independent MFMAs), with the next
+  // stage's L direct loads spread over the quarters when ISSUE. Meanwhile the
+  // next half's operands `no` are prepared from `nxt` (whose LDS reads were
+  // issued before this half), so that after the barrier its MFMAs start at
+  // once.
   template <int AMB, bool ISSUE>
-  __device__ __forceinline__ void mx_half(f32x16 (&acc)[MB][NB], const Raw& r, uint32_t& seen,
-                                          const StageIssue* si) const {
+  __device__ __forceinline__ void mx_half(f32x16 (&acc)[MB][NB], const Raw& cur, const MxOps& o, const Raw& nxt,
+                                          MxOps& no, uint32_t& seen, const StageIssue* si) const {
     constexpr int U1 = ISSUE ? (L + 3) / 4 : 0, U2 = ISSUE ? U1 + (L - U1 + 2) / 3 : 0;
     constexpr int U3 = ISSUE ? U2 + (L - U2 + 1) / 2 : 0, U4 = ISSUE ? L : 0;
     constexpr int JH = NB / 2;
-    MxScales s;
-    if (AMB > 0) mx_scales<AMB>(s, r, seen);
-    mx_sub<0, 0, JH, AMB, 0, U1>(acc, r, s, si);
-    mx_sub<0, JH, NB, AMB, U1, U2>(acc, r, s, si);
-    mx_sub<1, 0, JH, AMB, U2, U3>(acc, r, s, si);
-    mx_sub<1, JH, NB, AMB, U3, U4>(acc, r, s, si);
-    // the half's MFMAs stay before what follows (the barrier): sunk past it,
-    // they would keep both halves' raw chunks live at once
+    u32x4 t1[MB];
+    mx_sub<0, 0, JH, AMB, 0, U1, 2 * AMB>(acc, o.t, cur, o.s, si, [&] { mx_pass1_operands<AMB>(t1, cur); });
+    mx_sub<0, JH, NB, AMB, U1, U2, 4 * (AMB + NB)>(acc, o.t, cur, o.s, si,
+                                                   [&] { if (AMB > 0) mx_scales<AMB>(no.s, nxt, seen); });
+    mx_sub<1, 0, JH, AMB, U2, U3, 3 * AMB>(acc, t1, cur, o.s, si, [&] { mx_pass0_operands<AMB>(no.t, nxt); });
+    mx_sub<1, JH, NB, AMB, U3, U4, 0>(acc, t1, cur, o.s, si, [] {});
+    // The next operands and this half's MFMAs stay before what follows (the
+    // barrier): sunk past it, they would keep two halves' chunks live at once
+    // and delay the next MFMAs.
+#pragma unroll
+    for (int i = 0; i < AMB; ++i) asm volatile("" ::"v"(no.t[i]), "v"(no.s.a[i]));
+#pragma unroll
+    for (int j = 0; j < (AMB ? NB : 0); ++j) asm volatile("" ::"v"(no.s.b[j]));
 #pragma unroll
     for (int i = 0; i < AMB; ++i)
 #pragma unroll
@@ -904,6 +945,7 @@ struct GemmKernel {
                                               int kpad_grp, uint32_t& seen) const {
     static_assert(NB % 2 == 0, "two block-column parts per pass");
     Raw r0, r1;
+    MxOps o0, o1;
     // The loader's sizes are used here, so that any reload of them from the
     // spill area (after the epilogue, where register pressure peaks) comes
     // before the wait below; a reload first waited for inside the loop costs
@@ -913,18 +955,20 @@ struct GemmKernel {
     if (KPAD && g0 == kpad_g) zero_half_atom((uint32_t)g0 % NS, kpad_grp);
     block_sync();
     read_half<AMB>(r0, (uint32_t)g0 % NS, 0);
+    if (AMB > 0) mx_scales<AMB>(o0.s, r0, seen);
+    mx_pass0_operands<AMB>(o0.t, r0);
     for (int kt = 0; kt < n; ++kt) {
       const int g = g0 + kt;
       read_half<AMB>(r1, (uint32_t)g % NS, 1);
       __builtin_amdgcn_sched_group_barrier(kSchedDSRead, AMB + NB + 1 + (AMB + 1) / 2, 0);
-      mx_half<AMB, false>(acc, r0, seen, nullptr);
+      mx_half<AMB, false>(acc, r0, o0, r1, o1, seen, nullptr);
       wait_vmem<(NS - 2) * L>();
       if (KPAD && g + 1 == kpad_g) zero_half_atom((uint32_t)(g + 1) % NS, kpad_grp);
       block_sync();
       const StageIssue si = prep_issue(ld);
       read_half<AMB>(r0, (uint32_t)(g + 1) % NS, 0);  // unused after the last stage
       __builtin_amdgcn_sched_group_barrier(kSchedDSRead, AMB + NB + 1 + (AMB + 1) / 2, 0);
-      mx_half<AMB, true>(acc, r1, seen, &si);
+      mx_half<AMB, true>(acc, r1, o1, r0, o0, seen, &si);
       advance(ld);
     }
   }
