@@ -260,6 +260,9 @@ def main():
                     help="also time 15 calls of workload 2 merged into one 120-group launch (device tables)")
     ap.add_argument("--pow2", action="store_true",
                     help="also time workloads 2-4 with power-of-two scales through nvfp4_grouped_gemm_pow2")
+    ap.add_argument("--pow2-workloads", default="2,3,4", help="workloads of the --pow2 legs")
+    ap.add_argument("--no-pow2-line", action="store_true",
+                    help="leave out the power-of-two-scale leg of the headline workload from the JSON line")
     ap.add_argument("--sweep", action="store_true",
                     help="time every workload under every tile configuration and split mode (to stderr / --out)")
     ap.add_argument("--out", default=None, help="write the per-workload details as JSON here")
@@ -294,6 +297,14 @@ def main():
         f"(median of single calls {head['us_median']:.1f}); "
         f"hot {hot['tflops']:.1f} TFLOP/s; graph replay {fmt_us(head['graph_us_per_call'])} us/call")
     details = {"headline": head, "hot": hot}
+    p2 = None
+    if not args.no_pow2_line:
+        # the same workload with power-of-two scales through the MX entry point
+        p2 = time_workload(args.workload, max(20, args.steps // 2), args.warmup, args.tile_config, cold=True,
+                           pow2=True)
+        log(f"[bench] power-of-two scales (nvfp4_grouped_gemm_pow2): {p2['tflops']:.1f} TFLOP/s "
+            f"{p2['ms_per_call'] * 1e3:.1f} us/call (median {p2['us_median']:.1f})")
+        details["pow2_headline"] = p2
     if args.all:
         allres = []
         for i in range(5):
@@ -318,7 +329,7 @@ def main():
         details["all"] = allres
     if args.all or args.pow2:
         pres = []
-        for i in (2, 3, 4):
+        for i in [int(x) for x in args.pow2_workloads.split(",") if x.strip()]:
             r = time_workload(i, max(20, args.steps // 2), 5, -1, cold=True, pow2=True)
             pres.append(r)
             log(f"[bench] workload {i} {r['workload']} (nvfp4_grouped_gemm_pow2): {r['tflops']:.1f} TFLOP/s, "
@@ -391,6 +402,19 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_F16_TFLOPS, 4),
             "traffic": traffic,
+        },
+        "pow2_scales": None if p2 is None else {
+            "entry_point": "nvfp4_grouped_gemm_pow2",
+            "workload": p2["workload"],
+            "scales": "E4M3 codes with mantissa 0 (2^-3 .. 2^3), same shapes and operand bytes distribution",
+            "mfma": "v_mfma_scale_f32_32x32x64_f8f6f4 (E2M1, E8M0 scales), one 16-block per 32-K lane slice",
+            "value": round(p2["tflops"], 2), "unit": "TFLOP/s",
+            "us_per_call": round(p2["ms_per_call"] * 1e3, 2), "us_median": round(p2["us_median"], 2),
+            "roofline": {"bound": "mfma", "achieved": round(p2["tflops"], 2), "peak": PEAK_FP4_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(p2["tflops"] / PEAK_FP4_TFLOPS, 4),
+                         "usable_peak": PEAK_FP4_TFLOPS / 2, "traffic": load_traffic(p2["workload"]),
+                         "note": "half of every FP4 MFMA's K is zero padding (16-element scale blocks on a "
+                                 "32-element scale slice), so this instruction form tops out at half the FP4 peak"},
         },
         "cpu_baseline": None if cpu is None else {k: (round(v, 6) if isinstance(v, float) else v)
                                                   for k, v in cpu.items() if k in ("value", "unit", "cores",
