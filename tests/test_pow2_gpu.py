@@ -110,10 +110,10 @@ def test_pow2_k_tails(cfg, split):
     check_rows(shapes, groups, got)
 
 
-@pytest.mark.parametrize("idx,split", [(2, -1), (3, -1), (4, -1), (2, 1)])
+@pytest.mark.parametrize("idx,split", [(2, -1), (3, -1), (4, -1), (2, 1), (4, 1)])
 def test_pow2_full_workloads(idx, split):
     """The three large workloads at full size with power-of-two scales, in the
-    plan the heuristic picks (and stream-K for workload 2), checked on a
+    plan the heuristic picks (and stream-K for workloads 2 and 4), checked on a
     sample of rows of every group (the first, the last and every 37th)."""
     shapes, groups = synth.make_workload(idx, scale_codes=synth.POW2_SCALE_CODES)
     got, status = run_pow2(shapes, groups, split_mode=split, label=f"workload {idx}")
@@ -150,3 +150,33 @@ def test_pow2_matches_general_entry_point():
     ref = O.grouped_gemm(shapes, groups)
     for a, b, r in zip(got, dev.c_as_numpy(shapes, d), ref):
         assert not O.tolerance_violations(a, b, r["s"]).any()
+
+
+def test_pow2_graph_replay_matches_eager():
+    """Captured calls of the power-of-two entry point (whole tiles, no
+    workspace) write, replay after replay with eager work in between, exactly
+    what the eager call wrote; the status word stays 0."""
+    shapes, groups = synth.make_workload(1, scale_codes=synth.POW2_SCALE_CODES)
+    announce("pow2 graph replay, workload 1")
+    d = dev.upload(shapes, groups)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dev.run_pow2(shapes, d, status)
+    torch.cuda.synchronize()
+    eager = [c.copy() for c in dev.c_as_numpy(shapes, d)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        dev.run_pow2(shapes, d, status, stream=side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        dev.run_pow2(shapes, d, status, stream=side)
+    for _ in range(3):
+        for dd in d:
+            dd["c"].fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(eager, dev.c_as_numpy(shapes, d)):
+            assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    assert int(status.item()) == 0
