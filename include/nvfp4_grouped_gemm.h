@@ -163,8 +163,12 @@ int nvfp4_grouped_gemm_device(const int32_t* d_problem_sizes, const uint64_t* d_
  *             16-block below k is not one of the codes above; it stores
  *             nothing otherwise, so the caller clears it before the call.
  *             With 1 there the C of the call is not valid: repeat it with
- *             nvfp4_grouped_gemm. Padding rows of the scale tensors and the
- *             16-blocks past k in a half-used last atom may hold anything.
+ *             nvfp4_grouped_gemm. The check also sees the padding rows of a
+ *             scale tensor's last 128-row atom (for SFA those in a 32-row
+ *             block that also holds rows below m): padding that is not zero
+ *             or a power of two (zero padding is) reports 1 as well, which
+ *             only costs the fallback. The 16-blocks past k in a half-used
+ *             last atom may hold anything.
  * Calls that share d_status and may overlap in time report together.
  * Returns NVFP4_ERR_INVALID for a NULL d_status, NVFP4_ERR_MISALIGNED for a
  * misaligned one, else as nvfp4_grouped_gemm_ex.

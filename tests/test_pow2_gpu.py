@@ -180,3 +180,23 @@ def test_pow2_graph_replay_matches_eager():
         for a, b in zip(eager, dev.c_as_numpy(shapes, d)):
             assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
     assert int(status.item()) == 0
+
+
+def test_pow2_status_and_scale_padding():
+    """The status check sees the padding rows of the last scale atom only where
+    they are converted: SFA padding in a 32-row block that also holds rows
+    below m, and SFB padding (every block column of a tile is computed). A NaN
+    code in SFA padding rows past m's last 32-row block is not read, so not
+    reported, and the results stay correct either way."""
+    shapes = [(33, 72, 256, 1)]
+    base = synth.make_custom(shapes, seed=3333, scale_codes=synth.POW2_SCALE_CODES)
+    m, n, k, _ = shapes[0]
+    kb = np.arange(k // 16)
+    cases = [("sfa", np.arange(64, 128), 0), ("sfa", np.array([40]), 1), ("sfb", np.array([100]), 1)]
+    for key, pad_rows, expect in cases:
+        groups = [dict(g, **{key: g[key].copy()}) for g in base]
+        rows = m if key == "sfa" else n
+        groups[0][key][O.sf_offset(pad_rows[:, None], kb[None, :], rows, k).reshape(-1)] = 0x7F
+        got, status = run_pow2(shapes, groups, label=f"{key} padding rows {pad_rows[0]}..")
+        assert status == expect, (key, pad_rows[0])
+        check_rows(shapes, groups, got)
