@@ -40,6 +40,10 @@
 //    consecutive columns, stored as 16 bytes, masked to m and n.
 //    Tiles split by stream-K store fp32 partials; a second kernel adds them in
 //    a fixed order and writes fp16.
+//  * Scales that are all zero or powers of two (an MX-compatible special case
+//    of the pages' MX/NV FP4 block-scaled MMA) have their own mainloop: the
+//    packed codes go to v_mfma_scale_f32_32x32x64_f8f6f4 as E2M1 with E8M0
+//    scales, one 16-block per 32-K lane slice, without dequantisation.
 
 #include <hip/hip_runtime.h>
 
