@@ -248,6 +248,47 @@ def load_traffic(workload_name):
     return rec.get("bytes_per_launch")
 
 
+def mainloop_probe(iters_f16=2000, iters_fp4=400, reps=5):
+    """Times the inner loops of the two exact ways of applying the per-16 E4M3
+    scales (libnvfp4_mainloop_probe.so) on every compute unit, and reads what
+    the scaled FP4 conversion does with scales that are not powers of two."""
+    import torch
+
+    from moe_matmul_amd import probe
+
+    grid = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    names = {probe.VARIANT_DEQUANT_F16: "(b) exact f16 dequantisation + v_mfma_f32_32x32x16_f16",
+             probe.VARIANT_FP4_VALU: "(a) FP4 v_mfma_scale per 16-block + scale factors on the VALU",
+             probe.VARIANT_BARE_F16: "bare v_mfma_f32_32x32x16_f16 loop (no dequantisation)"}
+    out = {"grid": grid, "variants": []}
+    for v, iters in ((probe.VARIANT_BARE_F16, iters_f16), (probe.VARIANT_DEQUANT_F16, iters_f16),
+                     (probe.VARIANT_FP4_VALU, iters_fp4)):
+        probe.nvfp4_probe_mainloop(v, iters, grid, sink.data_ptr(), stream.cuda_stream)  # warm-up
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(reps):
+            probe.nvfp4_probe_mainloop(v, iters, grid, sink.data_ptr(), stream.cuda_stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / reps
+        tf = probe.nvfp4_probe_flops_per_iteration(v) * iters * grid / (ms / 1e3) / 1e12
+        out["variants"].append({"variant": v, "what": names[v], "iters": iters, "ms": ms, "tflops": tf,
+                                "frac_f16_peak": tf / PEAK_F16_TFLOPS})
+        log(f"[probe] {names[v]}: {tf:.0f} TFLOP/s of 32x32x16 work ({100 * tf / PEAK_F16_TFLOPS:.1f}% of the "
+            f"f16 MFMA peak), {ms:.2f} ms for {iters} iterations on {grid} workgroups")
+    scales = [1.0, 1.5, 1.875, 3.0, 0.75, 448.0]
+    sc = torch.tensor(scales, dtype=torch.float32, device="cuda")
+    res = torch.empty(len(scales), dtype=torch.int16, device="cuda")
+    probe.nvfp4_probe_cvt_scale(sc.data_ptr(), len(scales), res.data_ptr(), stream.cuda_stream)
+    torch.cuda.synchronize()
+    got = res.cpu().view(torch.float16).float().tolist()
+    out["cvt_scale"] = {"fp4_value": 1.0, "scales": scales, "results": got}
+    log(f"[probe] v_cvt_scalef32_pk_f16_fp4 of 1.0 under scales {scales}: {got}")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -269,6 +310,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=None, help="cap rows per group of the CPU sample")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum CPU work of the baseline leg")
+    ap.add_argument("--mainloop-probe", action="store_true",
+                    help="also time the inner loops of the two exact scale applications (measurement kernels)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
     args = ap.parse_args()
@@ -355,6 +398,9 @@ def main():
                     log(f"[sweep] wl{i} cfg{cfg} split{sm}: {r['ms_per_call'] * 1e3:8.1f} us {r['tflops']:7.1f} TFLOP/s "
                         f"tiles {r['tiles']} grid {r['grid']}")
         details["sweep"] = sweep
+
+    if args.mainloop_probe:
+        details["mainloop_probe"] = mainloop_probe()
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -1,7 +1,9 @@
 """Ahead-of-time build of the HIP library for gfx950 (hipcc, no JIT).
 
 ``python -m moe_matmul_amd.build`` compiles ``csrc/nvfp4_grouped_gemm.hip``
-into ``moe_matmul_amd/libnvfp4_grouped_gemm.so`` next to this file.
+into ``moe_matmul_amd/libnvfp4_grouped_gemm.so`` next to this file, and the
+mainloop measurement kernels ``csrc/mainloop_probe.hip`` into
+``moe_matmul_amd/libnvfp4_mainloop_probe.so``.
 """
 from __future__ import annotations
 
@@ -15,6 +17,9 @@ ROOT = os.path.dirname(HERE)
 SOURCES = [os.path.join(HERE, "csrc", "nvfp4_grouped_gemm.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libnvfp4_grouped_gemm.so")
+# measurement kernels behind the mainloop choice (not part of the GEMM)
+PROBE_SOURCES = [os.path.join(HERE, "csrc", "mainloop_probe.hip")]
+PROBE_LIB = os.path.join(HERE, "libnvfp4_mainloop_probe.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -33,9 +38,16 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile the library (always, even if a built copy exists); return its path."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *SOURCES, "-o", tmp]
+    """Compile the library and the probe library (always, even if built copies
+    exist); return the library's path."""
+    _compile(SOURCES, LIB, verbose)
+    _compile(PROBE_SOURCES, PROBE_LIB, verbose)
+    return LIB
+
+
+def _compile(sources, lib, verbose):
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, *sources, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
@@ -45,8 +57,7 @@ def build(verbose: bool = False) -> str:
         out = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
         if out.strip():
             print(out)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
 
 
 if __name__ == "__main__":

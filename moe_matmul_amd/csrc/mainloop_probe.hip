@@ -1,0 +1,266 @@
+// Measurement kernels behind the mainloop choice of the NVFP4 grouped GEMM on
+// gfx950 (MI355X).
+//
+// NVFP4 gives every 16 K-elements of a row one E4M3 scale (the block-scaled
+// MMA of submissions 506336 / 385043 / 499344, kernelindex.com "kernelbot
+// nvfp4 group gemm"). gfx950's scaled FP4 MFMA takes one E8M0 (power-of-two)
+// scale per lane per 32 K, so it cannot apply an E4M3 scale by itself. Two
+// exact ways remain:
+//  (b) dequantise a * s to f16 in registers (E2M1 x E4M3 needs at most 6
+//      significant bits, so the product is exact) and run the dense f16 MFMA;
+//  (a) run one FP4 MFMA per 16-block, with the power-of-two part of the scales
+//      on the MFMA's scale operands, and apply the remaining factors
+//      (sfa and sfb are 2^e * (1 + m/8)) to each fp32 32x32 partial product on
+//      the VALU: acc += P * (ma[row] * mb[col]).
+// Each kernel here runs one variant's inner loop for a 128x128 wave tile, four
+// waves per workgroup and one workgroup per compute unit, over operand bytes
+// and scale bytes held in LDS. There is no global memory traffic in the loop,
+// so the time per iteration is the loop's issue cost at the clock the chip
+// holds under that load. One iteration is 64 K of the wave tile: 64 MFMAs of
+// 32x32x16 f16 work in (b) and the bare loop, 64 FP4 MFMAs of one 16-block
+// each in (a).
+//
+// A fourth kernel converts FP4 code 0x2 (1.0) with v_cvt_scalef32_pk_f16_fp4
+// under given f32 scales, which shows how much of the scale the conversion
+// applies.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "nvfp4_mainloop_probe.h"
+
+namespace {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kThreads = 256;
+constexpr int kOperandChunks = 2048;  // 32 KiB of operand words, as 16-byte chunks
+constexpr int kScaleChunks = 256;     // 4 KiB of E4M3 scale bytes, as 16-byte chunks
+
+__device__ __forceinline__ uint32_t mix(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+
+// A finite positive E4M3 code with unbiased exponent in [-3, 3] (0.125 .. 15).
+__device__ __forceinline__ uint32_t scale_code(uint32_t r) { return 0x20u + r % 56u; }
+
+// 8 FP4 codes -> 8 f16 values a * s (exact), as in the grouped GEMM.
+__device__ __forceinline__ f16x8 dequant8(uint32_t w, _Float16 s) {
+  const f16x2 ss = {s, s};
+  const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
+  const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * ss;
+  const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * ss;
+  const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * ss;
+  return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+template <int VARIANT>
+__global__ __launch_bounds__(kThreads) void mainloop_probe_kernel(int iters, uint32_t seed, float* sink) {
+  __shared__ u32x4 ops[kOperandChunks];
+  __shared__ u32x4 scl[kScaleChunks];
+  const int tid = (int)threadIdx.x;
+  const uint32_t salt = seed ^ (blockIdx.x * 0x9e3779b9u);
+  for (int c = tid; c < kOperandChunks; c += kThreads) {
+    u32x4 v;
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t r = mix(salt + (uint32_t)(4 * c + q) * 2654435761u);
+      // the bare loop reads f16 pairs: sign, exponent 15 (1.0 .. 2.0), random mantissa
+      v[q] = VARIANT == 2 ? ((r & 0x83ff83ffu) | 0x3c003c00u) : r;
+    }
+    ops[c] = v;
+  }
+  for (int c = tid; c < kScaleChunks; c += kThreads) {
+    u32x4 v;
+    for (int q = 0; q < 4; ++q) {
+      uint32_t w = 0;
+      for (int b = 0; b < 4; ++b) w |= scale_code(mix(~salt + (uint32_t)(16 * c + 4 * q + b))) << (8 * b);
+      v[q] = w;
+    }
+    scl[c] = v;
+  }
+  __syncthreads();
+
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  for (int it = 0; it < iters; ++it) {
+    // operand chunks of this iteration: 4 A fragments, 4 B fragments
+    // (32 FP4 codes = four 16-K steps per lane each, or 8 f16 for the bare loop)
+    u32x4 a[4], b[4], sc;
+    if constexpr (VARIANT != 1) {
+      const int base = it * 8 * 64 + wave * 512 + lane;  // consecutive lanes read consecutive chunks
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        a[f] = ops[(base + f * 64) & (kOperandChunks - 1)];
+        b[f] = ops[(base + (4 + f) * 64) & (kOperandChunks - 1)];
+      }
+      sc = scl[((it + wave) * 64 + lane) & (kScaleChunks - 1)];  // new scale words every iteration
+    }
+    if constexpr (VARIANT == 0) {
+      // (b): one f16 scale per fragment per 16-block (two per 32 codes)
+      _Float16 sa[4][2], sb[4][2];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const f16x2 x = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc[f], 1.0f, false);
+        const f16x2 y = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc[f], 1.0f, true);
+        sa[f][0] = x[0];
+        sa[f][1] = x[1];
+        sb[f][0] = y[0];
+        sb[f][1] = y[1];
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        f16x8 fa[4], fb[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          fa[f] = dequant8(a[f][s], sa[f][s >> 1]);
+          fb[f] = dequant8(b[f][s], sb[f][s >> 1]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+      }
+    } else if constexpr (VARIANT == 1) {
+      // (a): per 16-K step, one FP4 MFMA per 32x32 block carrying that step's
+      // 16-block only (8 codes per lane half, zeros elsewhere), then the
+      // remaining scale factors on the VALU. Each lane's 16 results lie in 16
+      // rows of one column: 16 row factors per A fragment, one column factor
+      // per B fragment, both new for every 16-block. The VALU adds into the
+      // accumulators, so they must sit in the 256 architectural VGPRs: the wave
+      // tile is 128x64 here (half the MFMAs of an iteration of the others), and
+      // each step reads its own operand and scale words, so that no step's
+      // factors are held across another's.
+      const uint32_t* opw = reinterpret_cast<const uint32_t*>(ops);
+      const uint32_t* scw = reinterpret_cast<const uint32_t*>(scl);
+#pragma unroll 1
+      for (int s = 0; s < 4; ++s) {
+        const int step = it * 4 + s;
+        float mb[2];
+        uint32_t bw[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          bw[j] = opw[((step * 6 + 4 + j) * 64 + wave * 512 + lane) & (4 * kOperandChunks - 1)];
+          mb[j] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(scw[((step * 2 + j) * 64 + lane) & (4 * kScaleChunks - 1)],
+                                                           1.0f, false)[0];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t aw = opw[((step * 6 + i) * 64 + wave * 512 + lane) & (4 * kOperandChunks - 1)];
+          const u32x4 rows = scl[((step * 4 + i) * 64 + lane) & (kScaleChunks - 1)];
+          float ma[16];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(rows[q], 1.0f, false);
+            const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(rows[q], 1.0f, true);
+            ma[4 * q + 0] = lo[0];
+            ma[4 * q + 1] = lo[1];
+            ma[4 * q + 2] = hi[0];
+            ma[4 * q + 3] = hi[1];
+          }
+          const i32x8 av = {(int)aw, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const i32x8 bv = {(int)bw[j], 0, 0, 0, 0, 0, 0, 0};
+            const f32x16 p = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, f32x16{}, 4, 4, 0, 127, 0, 127);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = __builtin_fmaf(p[e], ma[e] * mb[j], acc[i][j][e]);
+          }
+        }
+      }
+    } else {
+      // the bare f16 MFMA loop: the same MFMAs on operands read from LDS
+      f16x8 fa[4], fb[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        fa[f] = __builtin_bit_cast(f16x8, a[f]);
+        fb[f] = __builtin_bit_cast(f16x8, b[f]);
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+    }
+  }
+
+  float total = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < (VARIANT == 1 ? 2 : 4); ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) total += acc[i][j][e];
+  sink[(size_t)blockIdx.x * kThreads + tid] = total;
+}
+
+__global__ void cvt_scale_probe_kernel(const float* scales, int n, uint16_t* out) {
+  const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i >= n) return;
+  // byte 0 of the source holds two FP4 codes 0x2 (1.0); the result is two f16
+  const f16x2 v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(0x22u, scales[i], 0);
+  out[i] = __builtin_bit_cast(uint16_t, v[0]);
+}
+
+int g_last_hip_error = 0;
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_probe_mainloop(int variant, int iters, int grid, float* sink, void* stream) {
+  if (variant < 0 || variant > 2 || iters < 1 || grid < 1 || grid > 65536 || sink == nullptr) return -1;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const uint32_t seed = 0x5eed1234u;
+  switch (variant) {
+    case 0: hipLaunchKernelGGL(mainloop_probe_kernel<0>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
+    case 1: hipLaunchKernelGGL(mainloop_probe_kernel<1>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
+    default: hipLaunchKernelGGL(mainloop_probe_kernel<2>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return -3;
+  }
+  return 0;
+}
+
+int nvfp4_probe_cvt_scale(const float* scales, int n, uint16_t* out, void* stream) {
+  if (n < 0 || (n > 0 && (scales == nullptr || out == nullptr))) return -1;
+  if (n == 0) return 0;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(cvt_scale_probe_kernel, dim3((n + 255) / 256), dim3(256), 0, st, scales, n, out);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return -3;
+  }
+  return 0;
+}
+
+int nvfp4_probe_last_hip_error(void) { return g_last_hip_error; }
+
+double nvfp4_probe_flops_per_iteration(int variant) {
+  // per wave 64 MFMAs of 32x32x16 (a 128x128 wave tile over 64 K), or 32 for
+  // variant 1 (128x64); four waves per workgroup
+  return (variant == 1 ? 32.0 : 64.0) * 2.0 * 32.0 * 32.0 * 16.0 * 4.0;
+}
+
+}  // extern "C"

@@ -285,3 +285,27 @@ def test_plan_cache_returns_the_plan_of_the_sizes_asked_for():
     a = mm.nvfp4_launch_geometry([(256, 256, 1024, 1)], 256, 0, 0)
     b = mm.nvfp4_launch_geometry([(256, 256, 1024, 1), (256, 256, 1024, 1)], 256, 0, 0)
     assert a["total_tiles"] == 1 and b["total_tiles"] == 2
+
+
+def test_probe_library_exports_every_declared_symbol():
+    """The measurement library (libnvfp4_mainloop_probe.so) exports exactly what
+    include/nvfp4_mainloop_probe.h declares."""
+    import subprocess
+
+    from moe_matmul_amd import probe
+    text = open(os.path.join(ROOT, "include", "nvfp4_mainloop_probe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = sorted(set(re.findall(r"\b(nvfp4_\w+)\s*\(", text)))
+    assert "nvfp4_probe_mainloop" in names
+    lib = probe.load_probe_library()
+    for name in names:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", probe.PROBE_LIB_PATH], capture_output=True, text=True).stdout
+    assert sorted(set(re.findall(r"\bT (nvfp4_\w+)", out))) == names
+    # argument checks run before any HIP call
+    assert lib.nvfp4_probe_mainloop(3, 1, 1, 0x1000, None) == -1
+    assert lib.nvfp4_probe_mainloop(0, 0, 1, 0x1000, None) == -1
+    assert lib.nvfp4_probe_mainloop(0, 1, 1, None, None) == -1
+    assert lib.nvfp4_probe_cvt_scale(None, 1, None, None) == -1
+    assert lib.nvfp4_probe_cvt_scale(None, 0, None, None) == 0
+    assert probe.nvfp4_probe_flops_per_iteration(0) == 2 * probe.nvfp4_probe_flops_per_iteration(1)

@@ -1,0 +1,51 @@
+"""GPU checks of the measurement kernels behind the mainloop choice
+(libnvfp4_mainloop_probe.so): what the scaled FP4 conversion does with a
+scale that is not a power of two, and the order of the inner-loop costs."""
+import sys
+
+import pytest
+import torch
+
+from moe_matmul_amd import probe
+
+pytestmark = pytest.mark.gpu
+
+
+def announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def test_scaled_fp4_conversion_applies_only_the_scale_exponent():
+    """v_cvt_scalef32_pk_f16_fp4 of FP4 1.0 under an f32 scale gives 2^floor(log2 scale):
+    the mantissa of an E4M3 scale needs a multiply of its own."""
+    announce("nvfp4_probe_cvt_scale")
+    scales = [1.0, 1.5, 1.875, 3.0, 0.75, 448.0, 0.125, 15.0]
+    sc = torch.tensor(scales, dtype=torch.float32, device="cuda")
+    out = torch.full((len(scales),), -1, dtype=torch.int16, device="cuda")
+    probe.nvfp4_probe_cvt_scale(sc.data_ptr(), len(scales), out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    got = out.cpu().view(torch.float16).float().tolist()
+    assert got == [1.0, 1.0, 1.0, 2.0, 0.5, 256.0, 0.125, 8.0]
+
+
+def test_mainloop_probe_costs():
+    """Per unit of useful MFMA work, the FP4-MFMA-plus-VALU loop (a) is far slower
+    than the f16 dequantisation loop (b), and (b) is not faster than the bare
+    f16 MFMA loop."""
+    grid = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    rate = {}
+    for v, iters in ((probe.VARIANT_BARE_F16, 200), (probe.VARIANT_DEQUANT_F16, 200), (probe.VARIANT_FP4_VALU, 50)):
+        announce(f"nvfp4_probe_mainloop variant {v} iters {iters} grid {grid}")
+        probe.nvfp4_probe_mainloop(v, iters, grid, sink.data_ptr(), stream.cuda_stream)
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(3):
+            probe.nvfp4_probe_mainloop(v, iters, grid, sink.data_ptr(), stream.cuda_stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        rate[v] = probe.nvfp4_probe_flops_per_iteration(v) * iters * grid * 3 / (start.elapsed_time(end) / 1e3)
+    assert rate[probe.VARIANT_DEQUANT_F16] > 1.5 * rate[probe.VARIANT_FP4_VALU], rate
+    assert rate[probe.VARIANT_BARE_F16] > 0.95 * rate[probe.VARIANT_DEQUANT_F16], rate
