@@ -140,10 +140,13 @@ def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None
     per = [evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]  # ms
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     if device_tables:
-        cfg = 2 if tile_config < 0 else tile_config
+        cfg = tile_config
+        if cfg < 0:  # the entry point's default: 256x256 tiles (header of the C ABI)
+            cfg = next(c for c in range(mm.nvfp4_num_tile_configs())
+                       if (mm.nvfp4_tile_config_info(c)["bm"], mm.nvfp4_tile_config_info(c)["bn"]) == (256, 256))
         p0 = [0x1000] * 5
         geo = dict(config=cfg, split=0, grid=cus,
-                   total_tiles=sum(mm.nvfp4_device_group_tiles(s, p0, cfg) for s in shapes))
+                   total_tiles=sum(mm.nvfp4_device_group_tiles(s, p0, tile_config) for s in shapes))
     else:
         geo = mm.nvfp4_launch_geometry(shapes, cus, tile_config, -1 if split_mode is None else split_mode)
     avg_s = total_ms / steps / 1e3

@@ -121,7 +121,7 @@ int nvfp4_grouped_gemm_ex(const int32_t* problem_sizes, const uint64_t* ptrs_abc
  *   d_ptrs_abc       device uint64 [num_groups][3] = addresses of A, B, C, 16-byte aligned.
  *   d_ptrs_sfa_sfb   device uint64 [num_groups][2] = addresses of SFA, SFB, 16-byte aligned.
  *   num_groups       1 .. NVFP4_MAX_DEVICE_GROUPS.
- *   tile_config      0 .. nvfp4_num_tile_configs()-1, or -1 for 256x128 tiles.
+ *   tile_config      0 .. nvfp4_num_tile_configs()-1, or -1 for 256x256 tiles.
  *   d_status         device int32, 4-byte aligned, or NULL: the kernel stores
  *                    there the number of groups it rejected (0: none).
  *   stream           a hipStream_t (NULL = the default stream).

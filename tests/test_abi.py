@@ -219,7 +219,7 @@ def test_device_group_check_matches_host_rules():
         for (m, n, k, l) in [(300, 4096, 7168, 1), (1, 8, 64, 1), (129, 136, 0, 2), (0, 64, 64, 1), (64, 0, 64, 1)]:
             want = 0 if m == 0 or n == 0 else -(-m // info["bm"]) * -(-n // info["bn"]) * l
             assert mm.nvfp4_device_group_tiles((m, n, k, l), p, cfg) == want
-    default = mm.nvfp4_tile_config_info(2)
+    default = mm.nvfp4_tile_config_info(0)  # the device-table entry point's default: 256x256
     assert mm.nvfp4_device_group_tiles((300, 512, 64, 1), p) == -(-300 // default["bm"]) * -(-512 // default["bn"])
     bad_sizes = [(128, 128, 80, 1), (128, 100, 128, 1), (-1, 128, 128, 1), (128, -8, 128, 1), (128, 128, -64, 1),
                  (128, 128, 128, 0), (128, 128, 1 << 23, 1), (1 << 20, 128, 4096, 1), (64, 64, 1 << 22, (1 << 31) - 1),

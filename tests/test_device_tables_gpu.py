@@ -67,7 +67,7 @@ def test_device_tables_match_oracle_and_host_path(cfg):
     edge = [(127, 136, 192, 1), (0, 64, 128, 1), (129, 264, 320, 1), (40, 48, 0, 1), (64, 0, 128, 1),
             (100, 136, 192, 2), (1, 8, 64, 1), (257, 8, 128, 1)]  # at most 8: the by-value limit
     cases.append((edge, synth.make_custom(edge, seed=515)))
-    host_cfg = 2 if cfg < 0 else cfg
+    host_cfg = 0 if cfg < 0 else cfg  # -1: the entry point's default, 256x256 tiles
     for shapes, groups in cases:
         announce(f"device tables cfg={cfg} shapes={shapes}")
         d = dev.upload(shapes, groups, c_guard=GUARD)
