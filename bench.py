@@ -264,10 +264,11 @@ def mainloop_probe(iters_f16=2000, iters_fp4=400, reps=5):
     stream = torch.cuda.current_stream()
     names = {probe.VARIANT_DEQUANT_F16: "(b) exact f16 dequantisation + v_mfma_f32_32x32x16_f16",
              probe.VARIANT_FP4_VALU: "(a) FP4 v_mfma_scale per 16-block + scale factors on the VALU",
-             probe.VARIANT_BARE_F16: "bare v_mfma_f32_32x32x16_f16 loop (no dequantisation)"}
+             probe.VARIANT_BARE_F16: "bare v_mfma_f32_32x32x16_f16 loop (no dequantisation)",
+             probe.VARIANT_BARE_FP4: "bare v_mfma_scale_f32_32x32x64_f8f6f4 loop, one 16-block per 32-K slice"}
     out = {"grid": grid, "variants": []}
     for v, iters in ((probe.VARIANT_BARE_F16, iters_f16), (probe.VARIANT_DEQUANT_F16, iters_f16),
-                     (probe.VARIANT_FP4_VALU, iters_fp4)):
+                     (probe.VARIANT_FP4_VALU, iters_fp4), (probe.VARIANT_BARE_FP4, iters_f16)):
         probe.nvfp4_probe_mainloop(v, iters, grid, sink.data_ptr(), stream.cuda_stream)  # warm-up
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         start.record(stream)
@@ -278,7 +279,7 @@ def mainloop_probe(iters_f16=2000, iters_fp4=400, reps=5):
         ms = start.elapsed_time(end) / reps
         tf = probe.nvfp4_probe_flops_per_iteration(v) * iters * grid / (ms / 1e3) / 1e12
         out["variants"].append({"variant": v, "what": names[v], "iters": iters, "ms": ms, "tflops": tf,
-                                "frac_f16_peak": tf / PEAK_F16_TFLOPS})
+                                "frac_f16_peak": tf / PEAK_F16_TFLOPS, "frac_fp4_peak": tf / PEAK_FP4_TFLOPS})
         log(f"[probe] {names[v]}: {tf:.0f} TFLOP/s of 32x32x16 work ({100 * tf / PEAK_F16_TFLOPS:.1f}% of the "
             f"f16 MFMA peak), {ms:.2f} ms for {iters} iterations on {grid} workgroups")
     scales = [1.0, 1.5, 1.875, 3.0, 0.75, 448.0]

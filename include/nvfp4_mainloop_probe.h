@@ -33,7 +33,11 @@ extern "C" {
  *              per MFMA, then each fp32 partial product times the row and
  *              column scale factors added into the accumulator on the VALU
  *              (accumulators in VGPRs, so a 128x64 wave tile);
- *   variant 2: the bare f16 MFMA loop (operands read from LDS, no VALU work).
+ *   variant 2: the bare f16 MFMA loop (operands read from LDS, no VALU work);
+ *   variant 3: the bare v_mfma_scale_f32_32x32x64_f8f6f4 loop on E2M1 codes
+ *              with E8M0 scales, one 16-block per 32-K lane slice (two
+ *              instructions per 32x32 block per 64 K), as in the
+ *              power-of-two-scale path.
  *   sink: device fp32 [grid * 256], written with per-lane sums (so the work
  *         is kept).
  */

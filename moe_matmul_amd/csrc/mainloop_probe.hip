@@ -20,7 +20,10 @@
 // 32x32x16 f16 work in (b) and the bare loop, 64 FP4 MFMAs of one 16-block
 // each in (a).
 //
-// A fourth kernel converts FP4 code 0x2 (1.0) with v_cvt_scalef32_pk_f16_fp4
+// A fourth loop is the bare scaled FP4 MFMA in the form the power-of-two-scale
+// kernel uses (one 16-block per 32-K lane slice, two instructions per 32x32
+// block per 64 K), the ceiling of that path. Another kernel converts FP4 code
+// 0x2 (1.0) with v_cvt_scalef32_pk_f16_fp4
 // under given f32 scales, which shows how much of the scale the conversion
 // applies.
 
@@ -63,6 +66,28 @@ __device__ __forceinline__ f16x8 dequant8(uint32_t w, _Float16 s) {
   const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * ss;
   const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * ss;
   return f16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// One pass of the bare scaled FP4 loop over the 4x4 blocks of a wave tile:
+// B codes whole, A codes of 16-block P of each lane slice, E8M0 scales near 1
+// (bytes 124 .. 127) taken from the scale words (byte P of each selected by
+// op_sel).
+template <int P>
+__device__ __forceinline__ void fp4_pass(f32x16 (&acc)[4][4], const u32x4 (&a)[4], const u32x4 (&b)[4],
+                                         const u32x4& sc) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const i32x8 av = P == 0 ? i32x8{(int)a[i][0], (int)a[i][1], 0, 0, 0, 0, 0, 0}
+                            : i32x8{0, 0, (int)a[i][2], (int)a[i][3], 0, 0, 0, 0};
+    const int sa = (int)((sc[i] & 0x03030303u) | 0x7c7c7c7cu);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const i32x8 bv = {(int)b[j][0], (int)b[j][1], (int)b[j][2], (int)b[j][3], 0, 0, 0, 0};
+      const int sb = (int)((sc[j] & 0x03030303u) | 0x7c7c7c7cu);
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bv, av, acc[i][j], 4, 4, 2 * P + 1, sb,
+                                                                  2 * P + 1, sa);
+    }
+  }
 }
 
 template <int VARIANT>
@@ -184,6 +209,13 @@ __global__ __launch_bounds__(kThreads) void mainloop_probe_kernel(int iters, uin
           }
         }
       }
+    } else if constexpr (VARIANT == 3) {
+      // the bare scaled FP4 MFMA loop in the form the power-of-two-scale
+      // kernel uses: per 32x32 block and 64 K, two instructions; pass p feeds
+      // the B codes whole and the A codes of 16-block p of each lane slice
+      // (the other half zero), with E8M0 scales from the scale words
+      fp4_pass<0>(acc, a, b, sc);
+      fp4_pass<1>(acc, a, b, sc);
     } else {
       // the bare f16 MFMA loop: the same MFMAs on operands read from LDS
       f16x8 fa[4], fb[4];
@@ -226,13 +258,14 @@ int g_last_hip_error = 0;
 extern "C" {
 
 int nvfp4_probe_mainloop(int variant, int iters, int grid, float* sink, void* stream) {
-  if (variant < 0 || variant > 2 || iters < 1 || grid < 1 || grid > 65536 || sink == nullptr) return -1;
+  if (variant < 0 || variant > 3 || iters < 1 || grid < 1 || grid > 65536 || sink == nullptr) return -1;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const uint32_t seed = 0x5eed1234u;
   switch (variant) {
     case 0: hipLaunchKernelGGL(mainloop_probe_kernel<0>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
     case 1: hipLaunchKernelGGL(mainloop_probe_kernel<1>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
-    default: hipLaunchKernelGGL(mainloop_probe_kernel<2>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
+    case 2: hipLaunchKernelGGL(mainloop_probe_kernel<2>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
+    default: hipLaunchKernelGGL(mainloop_probe_kernel<3>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
@@ -258,8 +291,9 @@ int nvfp4_probe_cvt_scale(const float* scales, int n, uint16_t* out, void* strea
 int nvfp4_probe_last_hip_error(void) { return g_last_hip_error; }
 
 double nvfp4_probe_flops_per_iteration(int variant) {
-  // per wave 64 MFMAs of 32x32x16 (a 128x128 wave tile over 64 K), or 32 for
-  // variant 1 (128x64); four waves per workgroup
+  // per wave the work of 64 MFMAs of 32x32x16 (a 128x128 wave tile over 64 K;
+  // variant 3 does it in 32 scaled FP4 MFMAs), or 32 for variant 1 (128x64);
+  // four waves per workgroup
   return (variant == 1 ? 32.0 : 64.0) * 2.0 * 32.0 * 32.0 * 16.0 * 4.0;
 }
 

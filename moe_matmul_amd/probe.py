@@ -13,6 +13,7 @@ PROBE_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnv
 VARIANT_DEQUANT_F16 = 0   # (b) exact dequantisation to f16, v_mfma_f32_32x32x16_f16
 VARIANT_FP4_VALU = 1      # (a) FP4 MFMA per 16-block, scale factors applied on the VALU
 VARIANT_BARE_F16 = 2      # the f16 MFMA loop alone
+VARIANT_BARE_FP4 = 3      # the scaled FP4 MFMA loop alone, one 16-block per 32-K lane slice
 
 _lib = None
 

@@ -32,12 +32,13 @@ def test_scaled_fp4_conversion_applies_only_the_scale_exponent():
 def test_mainloop_probe_costs():
     """Per unit of useful MFMA work, the FP4-MFMA-plus-VALU loop (a) is far slower
     than the f16 dequantisation loop (b), and (b) is not faster than the bare
-    f16 MFMA loop."""
+    f16 MFMA loop; the bare scaled FP4 loop runs too."""
     grid = torch.cuda.get_device_properties(0).multi_processor_count
     sink = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     rate = {}
-    for v, iters in ((probe.VARIANT_BARE_F16, 200), (probe.VARIANT_DEQUANT_F16, 200), (probe.VARIANT_FP4_VALU, 50)):
+    for v, iters in ((probe.VARIANT_BARE_F16, 200), (probe.VARIANT_DEQUANT_F16, 200), (probe.VARIANT_FP4_VALU, 50),
+                     (probe.VARIANT_BARE_FP4, 200)):
         announce(f"nvfp4_probe_mainloop variant {v} iters {iters} grid {grid}")
         probe.nvfp4_probe_mainloop(v, iters, grid, sink.data_ptr(), stream.cuda_stream)
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -49,3 +50,4 @@ def test_mainloop_probe_costs():
         rate[v] = probe.nvfp4_probe_flops_per_iteration(v) * iters * grid * 3 / (start.elapsed_time(end) / 1e3)
     assert rate[probe.VARIANT_DEQUANT_F16] > 1.5 * rate[probe.VARIANT_FP4_VALU], rate
     assert rate[probe.VARIANT_BARE_F16] > 0.95 * rate[probe.VARIANT_DEQUANT_F16], rate
+    assert rate[probe.VARIANT_BARE_FP4] > rate[probe.VARIANT_FP4_VALU], rate
