@@ -9,7 +9,7 @@
  * Calls are asynchronous on `stream` (a hipStream_t, NULL = default stream);
  * the caller owns every buffer. Return 0, -1 for invalid arguments (nothing is
  * launched), -3 if the launch failed (nvfp4_probe_last_hip_error() has the HIP
- * code).
+ * code of the calling thread's last failed launch).
  */
 #ifndef NVFP4_MAINLOOP_PROBE_H
 #define NVFP4_MAINLOOP_PROBE_H
@@ -37,7 +37,9 @@ extern "C" {
  *   variant 3: the bare v_mfma_scale_f32_32x32x64_f8f6f4 loop on E2M1 codes
  *              with E8M0 scales, one 16-block per 32-K lane slice (two
  *              instructions per 32x32 block per 64 K), as in the
- *              power-of-two-scale path.
+ *              power-of-two-scale path;
+ *   variant 4: a bare f16 loop with v_mfma_f32_16x16x32_f16 doing the same
+ *              work per iteration (8 x 4 blocks of 16x16, four 32-K steps).
  *   sink: device fp32 [grid * 256], written with per-lane sums (so the work
  *         is kept).
  */

@@ -20,7 +20,8 @@
 // 32x32x16 f16 work in (b) and the bare loop, 64 FP4 MFMAs of one 16-block
 // each in (a).
 //
-// A fourth loop is the bare scaled FP4 MFMA in the form the power-of-two-scale
+// A fifth loop is the bare f16 loop with the 16x16x32 instruction shape. A
+// fourth loop is the bare scaled FP4 MFMA in the form the power-of-two-scale
 // kernel uses (one 16-block per 32-K lane slice, two instructions per 32x32
 // block per 64 K), the ceiling of that path. Another kernel converts FP4 code
 // 0x2 (1.0) with v_cvt_scalef32_pk_f16_fp4
@@ -38,6 +39,7 @@ namespace {
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
@@ -123,6 +125,11 @@ __global__ __launch_bounds__(kThreads) void mainloop_probe_kernel(int iters, uin
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+  f32x4 acc16[8][4];  // variant 4
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc16[i][j] = f32x4{};
 
   for (int it = 0; it < iters; ++it) {
     // operand chunks of this iteration: 4 A fragments, 4 B fragments
@@ -216,6 +223,23 @@ __global__ __launch_bounds__(kThreads) void mainloop_probe_kernel(int iters, uin
       // (the other half zero), with E8M0 scales from the scale words
       fp4_pass<0>(acc, a, b, sc);
       fp4_pass<1>(acc, a, b, sc);
+    } else if constexpr (VARIANT == 4) {
+      // the bare f16 loop with the 16x16x32 shape and the same work per
+      // iteration: 8 x 4 blocks of 16x16 (a 128x64 wave tile, so that the
+      // accumulators leave the register allocator room), four 32-K steps
+      f16x8 fa[4], fb[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        fa[f] = __builtin_bit_cast(f16x8, a[f]);
+        fb[f] = __builtin_bit_cast(f16x8, b[f]);
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc16[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[(j + s) & 3], fa[(i + s) & 3], acc16[i][j], 0, 0, 0);
     } else {
       // the bare f16 MFMA loop: the same MFMAs on operands read from LDS
       f16x8 fa[4], fb[4];
@@ -240,6 +264,14 @@ __global__ __launch_bounds__(kThreads) void mainloop_probe_kernel(int iters, uin
     for (int j = 0; j < (VARIANT == 1 ? 2 : 4); ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) total += acc[i][j][e];
+  if constexpr (VARIANT == 4) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) total += acc16[i][j][e];
+  }
   sink[(size_t)blockIdx.x * kThreads + tid] = total;
 }
 
@@ -251,21 +283,22 @@ __global__ void cvt_scale_probe_kernel(const float* scales, int n, uint16_t* out
   out[i] = __builtin_bit_cast(uint16_t, v[0]);
 }
 
-int g_last_hip_error = 0;
+thread_local int g_last_hip_error = 0;  // per calling thread, like the library's
 
 }  // namespace
 
 extern "C" {
 
 int nvfp4_probe_mainloop(int variant, int iters, int grid, float* sink, void* stream) {
-  if (variant < 0 || variant > 3 || iters < 1 || grid < 1 || grid > 65536 || sink == nullptr) return -1;
+  if (variant < 0 || variant > 4 || iters < 1 || grid < 1 || grid > 65536 || sink == nullptr) return -1;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const uint32_t seed = 0x5eed1234u;
   switch (variant) {
     case 0: hipLaunchKernelGGL(mainloop_probe_kernel<0>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
     case 1: hipLaunchKernelGGL(mainloop_probe_kernel<1>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
     case 2: hipLaunchKernelGGL(mainloop_probe_kernel<2>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
-    default: hipLaunchKernelGGL(mainloop_probe_kernel<3>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
+    case 3: hipLaunchKernelGGL(mainloop_probe_kernel<3>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
+    default: hipLaunchKernelGGL(mainloop_probe_kernel<4>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
@@ -292,7 +325,8 @@ int nvfp4_probe_last_hip_error(void) { return g_last_hip_error; }
 
 double nvfp4_probe_flops_per_iteration(int variant) {
   // per wave the work of 64 MFMAs of 32x32x16 (a 128x128 wave tile over 64 K;
-  // variant 3 does it in 32 scaled FP4 MFMAs), or 32 for variant 1 (128x64);
+  // variant 3 does it in 32 scaled FP4 MFMAs, variant 4 in 128 MFMAs of
+  // 16x16x32 on a 128x64 tile), or 32 for variant 1 (128x64);
   // four waves per workgroup
   return (variant == 1 ? 32.0 : 64.0) * 2.0 * 32.0 * 32.0 * 16.0 * 4.0;
 }

@@ -14,6 +14,7 @@ VARIANT_DEQUANT_F16 = 0   # (b) exact dequantisation to f16, v_mfma_f32_32x32x16
 VARIANT_FP4_VALU = 1      # (a) FP4 MFMA per 16-block, scale factors applied on the VALU
 VARIANT_BARE_F16 = 2      # the f16 MFMA loop alone
 VARIANT_BARE_FP4 = 3      # the scaled FP4 MFMA loop alone, one 16-block per 32-K lane slice
+VARIANT_BARE_F16_16X16 = 4  # the f16 MFMA loop alone with the 16x16x32 shape
 
 _lib = None
 
