@@ -260,17 +260,20 @@ def mainloop_probe(iters_f16=2000, iters_fp4=400, reps=5):
     from moe_matmul_amd import probe
 
     grid = torch.cuda.get_device_properties(0).multi_processor_count
-    sink = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    sink = torch.empty(grid * probe.SINK_PER_WORKGROUP, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     names = {probe.VARIANT_DEQUANT_F16: "(b) exact f16 dequantisation + v_mfma_f32_32x32x16_f16",
              probe.VARIANT_FP4_VALU: "(a) FP4 v_mfma_scale per 16-block + scale factors on the VALU",
              probe.VARIANT_BARE_F16: "bare v_mfma_f32_32x32x16_f16 loop (no dequantisation)",
              probe.VARIANT_BARE_FP4: "bare v_mfma_scale_f32_32x32x64_f8f6f4 loop, one 16-block per 32-K slice",
-             probe.VARIANT_BARE_F16_16X16: "bare v_mfma_f32_16x16x32_f16 loop (same work per iteration)"}
+             probe.VARIANT_BARE_F16_16X16: "bare v_mfma_f32_16x16x32_f16 loop (same work per iteration)",
+             probe.VARIANT_DEQUANT_128X64: "(b) on a 128x64 wave tile, one wave per SIMD",
+             probe.VARIANT_DEQUANT_128X64_2W: "(b) on a 128x64 wave tile, two waves per SIMD"}
     out = {"grid": grid, "variants": []}
     for v, iters in ((probe.VARIANT_BARE_F16, iters_f16), (probe.VARIANT_DEQUANT_F16, iters_f16),
                      (probe.VARIANT_FP4_VALU, iters_fp4), (probe.VARIANT_BARE_FP4, iters_f16),
-                     (probe.VARIANT_BARE_F16_16X16, iters_f16)):
+                     (probe.VARIANT_BARE_F16_16X16, iters_f16), (probe.VARIANT_DEQUANT_128X64, iters_f16),
+                     (probe.VARIANT_DEQUANT_128X64_2W, iters_f16)):
         probe.nvfp4_probe_mainloop(v, iters, grid, sink.data_ptr(), stream.cuda_stream)  # warm-up
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         start.record(stream)

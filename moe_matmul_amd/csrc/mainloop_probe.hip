@@ -45,6 +45,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 256;
+constexpr int kMaxThreads = 512;  // sink entries per workgroup
 constexpr int kOperandChunks = 2048;  // 32 KiB of operand words, as 16-byte chunks
 constexpr int kScaleChunks = 256;     // 4 KiB of E4M3 scale bytes, as 16-byte chunks
 
@@ -92,13 +93,13 @@ __device__ __forceinline__ void fp4_pass(f32x16 (&acc)[4][4], const u32x4 (&a)[4
   }
 }
 
-template <int VARIANT>
-__global__ __launch_bounds__(kThreads) void mainloop_probe_kernel(int iters, uint32_t seed, float* sink) {
+template <int VARIANT, int NT = kThreads>
+__global__ __launch_bounds__(NT) void mainloop_probe_kernel(int iters, uint32_t seed, float* sink) {
   __shared__ u32x4 ops[kOperandChunks];
   __shared__ u32x4 scl[kScaleChunks];
   const int tid = (int)threadIdx.x;
   const uint32_t salt = seed ^ (blockIdx.x * 0x9e3779b9u);
-  for (int c = tid; c < kOperandChunks; c += kThreads) {
+  for (int c = tid; c < kOperandChunks; c += NT) {
     u32x4 v;
     for (int q = 0; q < 4; ++q) {
       const uint32_t r = mix(salt + (uint32_t)(4 * c + q) * 2654435761u);
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void mainloop_probe_kernel(int iters, uin
     }
     ops[c] = v;
   }
-  for (int c = tid; c < kScaleChunks; c += kThreads) {
+  for (int c = tid; c < kScaleChunks; c += NT) {
     u32x4 v;
     for (int q = 0; q < 4; ++q) {
       uint32_t w = 0;
@@ -144,8 +145,11 @@ __global__ __launch_bounds__(kThreads) void mainloop_probe_kernel(int iters, uin
       }
       sc = scl[((it + wave) * 64 + lane) & (kScaleChunks - 1)];  // new scale words every iteration
     }
-    if constexpr (VARIANT == 0) {
-      // (b): one f16 scale per fragment per 16-block (two per 32 codes)
+    if constexpr (VARIANT == 0 || VARIANT == 5 || VARIANT == 6) {
+      // (b): one f16 scale per fragment per 16-block (two per 32 codes).
+      // Variants 5 and 6 run it on a 128x64 wave tile (two B fragments),
+      // one and two waves per SIMD.
+      constexpr int NBV = VARIANT == 0 ? 4 : 2;
       _Float16 sa[4][2], sb[4][2];
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
@@ -160,14 +164,13 @@ __global__ __launch_bounds__(kThreads) void mainloop_probe_kernel(int iters, uin
       for (int s = 0; s < 4; ++s) {
         f16x8 fa[4], fb[4];
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-          fa[f] = dequant8(a[f][s], sa[f][s >> 1]);
-          fb[f] = dequant8(b[f][s], sb[f][s >> 1]);
-        }
+        for (int f = 0; f < 4; ++f) fa[f] = dequant8(a[f][s], sa[f][s >> 1]);
+#pragma unroll
+        for (int f = 0; f < NBV; ++f) fb[f] = dequant8(b[f][s], sb[f][s >> 1]);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < NBV; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
       }
     } else if constexpr (VARIANT == 1) {
       // (a): per 16-K step, one FP4 MFMA per 32x32 block carrying that step's
@@ -261,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void mainloop_probe_kernel(int iters, uin
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < (VARIANT == 1 ? 2 : 4); ++j)
+    for (int j = 0; j < (VARIANT == 1 || VARIANT >= 5 ? 2 : 4); ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) total += acc[i][j][e];
   if constexpr (VARIANT == 4) {
@@ -272,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void mainloop_probe_kernel(int iters, uin
 #pragma unroll
         for (int e = 0; e < 4; ++e) total += acc16[i][j][e];
   }
-  sink[(size_t)blockIdx.x * kThreads + tid] = total;
+  sink[(size_t)blockIdx.x * kMaxThreads + tid] = total;
 }
 
 __global__ void cvt_scale_probe_kernel(const float* scales, int n, uint16_t* out) {
@@ -290,7 +293,7 @@ thread_local int g_last_hip_error = 0;  // per calling thread, like the library'
 extern "C" {
 
 int nvfp4_probe_mainloop(int variant, int iters, int grid, float* sink, void* stream) {
-  if (variant < 0 || variant > 4 || iters < 1 || grid < 1 || grid > 65536 || sink == nullptr) return -1;
+  if (variant < 0 || variant > 6 || iters < 1 || grid < 1 || grid > 65536 || sink == nullptr) return -1;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const uint32_t seed = 0x5eed1234u;
   switch (variant) {
@@ -298,7 +301,11 @@ int nvfp4_probe_mainloop(int variant, int iters, int grid, float* sink, void* st
     case 1: hipLaunchKernelGGL(mainloop_probe_kernel<1>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
     case 2: hipLaunchKernelGGL(mainloop_probe_kernel<2>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
     case 3: hipLaunchKernelGGL(mainloop_probe_kernel<3>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
-    default: hipLaunchKernelGGL(mainloop_probe_kernel<4>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
+    case 4: hipLaunchKernelGGL(mainloop_probe_kernel<4>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
+    case 5: hipLaunchKernelGGL(mainloop_probe_kernel<5>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
+    default:
+      hipLaunchKernelGGL((mainloop_probe_kernel<6, kMaxThreads>), dim3(grid), dim3(kMaxThreads), 0, st, iters, seed, sink);
+      break;
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
@@ -326,9 +333,10 @@ int nvfp4_probe_last_hip_error(void) { return g_last_hip_error; }
 double nvfp4_probe_flops_per_iteration(int variant) {
   // per wave the work of 64 MFMAs of 32x32x16 (a 128x128 wave tile over 64 K;
   // variant 3 does it in 32 scaled FP4 MFMAs, variant 4 in 128 MFMAs of
-  // 16x16x32 on a 128x64 tile), or 32 for variant 1 (128x64);
-  // four waves per workgroup
-  return (variant == 1 ? 32.0 : 64.0) * 2.0 * 32.0 * 32.0 * 16.0 * 4.0;
+  // 16x16x32 on a 128x64 tile), or 32 for variants 1, 5 and 6 (128x64);
+  // four waves per workgroup, eight for variant 6
+  const double per_wave = (variant == 1 || variant >= 5) ? 32.0 : 64.0;
+  return per_wave * 2.0 * 32.0 * 32.0 * 16.0 * (variant == 6 ? 8.0 : 4.0);
 }
 
 }  // extern "C"

@@ -15,6 +15,9 @@ VARIANT_FP4_VALU = 1      # (a) FP4 MFMA per 16-block, scale factors applied on 
 VARIANT_BARE_F16 = 2      # the f16 MFMA loop alone
 VARIANT_BARE_FP4 = 3      # the scaled FP4 MFMA loop alone, one 16-block per 32-K lane slice
 VARIANT_BARE_F16_16X16 = 4  # the f16 MFMA loop alone with the 16x16x32 shape
+VARIANT_DEQUANT_128X64 = 5  # (b) on a 128x64 wave tile, one wave per SIMD
+VARIANT_DEQUANT_128X64_2W = 6  # the same, two waves per SIMD (512-thread workgroups)
+SINK_PER_WORKGROUP = 512
 
 _lib = None
 

@@ -34,7 +34,7 @@ def test_mainloop_probe_costs():
     than the f16 dequantisation loop (b), and (b) is not faster than the bare
     f16 MFMA loop; the bare scaled FP4 loop runs too."""
     grid = torch.cuda.get_device_properties(0).multi_processor_count
-    sink = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    sink = torch.empty(grid * probe.SINK_PER_WORKGROUP, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
     rate = {}
     for v, iters in ((probe.VARIANT_BARE_F16, 200), (probe.VARIANT_DEQUANT_F16, 200), (probe.VARIANT_FP4_VALU, 50),
