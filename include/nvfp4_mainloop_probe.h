@@ -42,14 +42,18 @@ extern "C" {
  *              work per iteration (8 x 4 blocks of 16x16, four 32-K steps);
  *   variant 5: variant 0 on a 128x64 wave tile (6 dequantisation VALU per
  *              MFMA), four waves per workgroup (one per SIMD);
- *   variant 6: variant 5 with eight waves per workgroup (two per SIMD).
+ *   variant 6: variant 5 with eight waves per workgroup (two per SIMD);
+ *   variant 7: (b) on a 256x128 workgroup tile as four 64x128 wave tiles, B
+ *              dequantised once per workgroup (each wave one of the four B
+ *              fragments) and shared through LDS with one barrier per
+ *              iteration (3 dequantisation VALU per MFMA).
  *   sink: device fp32 [grid * 512], written with per-lane sums (so the work
  *         is kept).
  */
 int nvfp4_probe_mainloop(int variant, int iters, int grid, float* sink, void* stream);
 
 /* Useful flops of one iteration of one workgroup (4 waves x 64 MFMAs, or x 32
- * for variants 1 and 5, or 8 waves x 32 for variant 6, of 32x32x16). */
+ * for variants 1, 5 and 7, or 8 waves x 32 for variant 6, of 32x32x16). */
 double nvfp4_probe_flops_per_iteration(int variant);
 
 /*

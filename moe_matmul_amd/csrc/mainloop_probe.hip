@@ -48,6 +48,9 @@ constexpr int kThreads = 256;
 constexpr int kMaxThreads = 512;  // sink entries per workgroup
 constexpr int kOperandChunks = 2048;  // 32 KiB of operand words, as 16-byte chunks
 constexpr int kScaleChunks = 256;     // 4 KiB of E4M3 scale bytes, as 16-byte chunks
+// variant 7: dequantised B fragments shared through LDS, two buffers of
+// 4 fragments x 4 K-steps x 64 lanes x 16 bytes
+constexpr int kShareChunks = 2 * 4 * 4 * 64;
 
 __device__ __forceinline__ uint32_t mix(uint32_t x) {
   x ^= x >> 16;
@@ -97,6 +100,7 @@ template <int VARIANT, int NT = kThreads>
 __global__ __launch_bounds__(NT) void mainloop_probe_kernel(int iters, uint32_t seed, float* sink) {
   __shared__ u32x4 ops[kOperandChunks];
   __shared__ u32x4 scl[kScaleChunks];
+  __shared__ f16x8 shared_b[VARIANT == 7 ? kShareChunks : 1];
   const int tid = (int)threadIdx.x;
   const uint32_t salt = seed ^ (blockIdx.x * 0x9e3779b9u);
   for (int c = tid; c < kOperandChunks; c += NT) {
@@ -171,6 +175,38 @@ __global__ __launch_bounds__(NT) void mainloop_probe_kernel(int iters, uint32_t 
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < NBV; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+      }
+    } else if constexpr (VARIANT == 7) {
+      // (b) with B shared: a 256x128 workgroup tile as four 64x128 wave tiles
+      // (2 A and 4 B fragments each). Each wave dequantises its 2 A fragments
+      // and one of the 4 B fragments (for all four 16-K steps), writes that B
+      // fragment to LDS, and after one barrier reads all four back as f16:
+      // 3 dequantisation VALU per MFMA instead of 6, plus the LDS exchange.
+      f16x8* xb = shared_b + (it & 1) * (4 * 4 * 64);
+      {
+        const f16x2 y = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc[0], 1.0f, true);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) xb[(wave * 4 + s) * 64 + lane] = dequant8(b[0][s], y[s >> 1]);
+      }
+      _Float16 sa[2][2];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const f16x2 x = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc[f], 1.0f, false);
+        sa[f][0] = x[0];
+        sa[f][1] = x[1];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        f16x8 fa[2], fb[4];
+#pragma unroll
+        for (int f = 0; f < 2; ++f) fa[f] = dequant8(a[f][s], sa[f][s >> 1]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fb[j] = xb[(j * 4 + s) * 64 + lane];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
       }
     } else if constexpr (VARIANT == 1) {
       // (a): per 16-K step, one FP4 MFMA per 32x32 block carrying that step's
@@ -262,9 +298,9 @@ __global__ __launch_bounds__(NT) void mainloop_probe_kernel(int iters, uint32_t 
 
   float total = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < (VARIANT == 7 ? 2 : 4); ++i)
 #pragma unroll
-    for (int j = 0; j < (VARIANT == 1 || VARIANT >= 5 ? 2 : 4); ++j)
+    for (int j = 0; j < (VARIANT == 1 || VARIANT == 5 || VARIANT == 6 ? 2 : 4); ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) total += acc[i][j][e];
   if constexpr (VARIANT == 4) {
@@ -293,7 +329,7 @@ thread_local int g_last_hip_error = 0;  // per calling thread, like the library'
 extern "C" {
 
 int nvfp4_probe_mainloop(int variant, int iters, int grid, float* sink, void* stream) {
-  if (variant < 0 || variant > 6 || iters < 1 || grid < 1 || grid > 65536 || sink == nullptr) return -1;
+  if (variant < 0 || variant > 7 || iters < 1 || grid < 1 || grid > 65536 || sink == nullptr) return -1;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const uint32_t seed = 0x5eed1234u;
   switch (variant) {
@@ -303,9 +339,10 @@ int nvfp4_probe_mainloop(int variant, int iters, int grid, float* sink, void* st
     case 3: hipLaunchKernelGGL(mainloop_probe_kernel<3>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
     case 4: hipLaunchKernelGGL(mainloop_probe_kernel<4>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
     case 5: hipLaunchKernelGGL(mainloop_probe_kernel<5>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
-    default:
+    case 6:
       hipLaunchKernelGGL((mainloop_probe_kernel<6, kMaxThreads>), dim3(grid), dim3(kMaxThreads), 0, st, iters, seed, sink);
       break;
+    default: hipLaunchKernelGGL(mainloop_probe_kernel<7>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
@@ -335,7 +372,7 @@ double nvfp4_probe_flops_per_iteration(int variant) {
   // variant 3 does it in 32 scaled FP4 MFMAs, variant 4 in 128 MFMAs of
   // 16x16x32 on a 128x64 tile), or 32 for variants 1, 5 and 6 (128x64);
   // four waves per workgroup, eight for variant 6
-  const double per_wave = (variant == 1 || variant >= 5) ? 32.0 : 64.0;
+  const double per_wave = (variant == 1 || variant >= 5) ? 32.0 : 64.0;  // variant 7: 64x128 wave tiles
   return per_wave * 2.0 * 32.0 * 32.0 * 16.0 * (variant == 6 ? 8.0 : 4.0);
 }
 

@@ -17,6 +17,7 @@ VARIANT_BARE_FP4 = 3      # the scaled FP4 MFMA loop alone, one 16-block per 32-
 VARIANT_BARE_F16_16X16 = 4  # the f16 MFMA loop alone with the 16x16x32 shape
 VARIANT_DEQUANT_128X64 = 5  # (b) on a 128x64 wave tile, one wave per SIMD
 VARIANT_DEQUANT_128X64_2W = 6  # the same, two waves per SIMD (512-thread workgroups)
+VARIANT_DEQUANT_SHARED_B = 7  # (b) on 64x128 wave tiles with B dequantised once per workgroup, shared in LDS
 SINK_PER_WORKGROUP = 512
 
 _lib = None
