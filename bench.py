@@ -191,6 +191,19 @@ def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None
     )
 
 
+def cpu_model():
+    """The host CPU's model name (Linux), or the platform's processor string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(idx, max_rows=None, min_seconds=10.0):
     """The CPU oracle, as it stands, on workload ``idx`` (rows capped per group)."""
     from threadpoolctl import threadpool_info
@@ -213,7 +226,8 @@ def cpu_baseline(idx, max_rows=None, min_seconds=10.0):
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     sample = (f"{synth.WORKLOADS[idx]['name']}, " +
               ("all rows" if max_rows is None else f"first {max_rows} rows per group") +
-              f", {reps} pass(es), {fl / 1e9:.1f} GFLOP of C in {dt:.1f} s (float64 dequant + BLAS, C and S)")
+              f", {reps} pass(es), {fl / 1e9:.1f} GFLOP of C in {dt:.1f} s (float64 dequant + BLAS, C and S)"
+              f"; BLAS threads {threads} of {os.cpu_count()} host CPUs, {cpu_model()}")
     return dict(value=fl / dt / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle", sample=sample,
                 seconds=dt, cpu_count=os.cpu_count())
 
