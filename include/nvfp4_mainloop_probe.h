@@ -46,14 +46,16 @@ extern "C" {
  *   variant 7: (b) on a 256x128 workgroup tile as four 64x128 wave tiles, B
  *              dequantised once per workgroup (each wave one of the four B
  *              fragments) and shared through LDS with one barrier per
- *              iteration (3 dequantisation VALU per MFMA).
+ *              iteration (3 dequantisation VALU per MFMA);
+ *   variant 8: variant 7 with the exchange a step ahead (each iteration
+ *              writes the next one's B while its MFMAs run).
  *   sink: device fp32 [grid * 512], written with per-lane sums (so the work
  *         is kept).
  */
 int nvfp4_probe_mainloop(int variant, int iters, int grid, float* sink, void* stream);
 
 /* Useful flops of one iteration of one workgroup (4 waves x 64 MFMAs, or x 32
- * for variants 1, 5 and 7, or 8 waves x 32 for variant 6, of 32x32x16). */
+ * for variants 1, 5, 7 and 8, or 8 waves x 32 for variant 6, of 32x32x16). */
 double nvfp4_probe_flops_per_iteration(int variant);
 
 /*

@@ -100,7 +100,7 @@ template <int VARIANT, int NT = kThreads>
 __global__ __launch_bounds__(NT) void mainloop_probe_kernel(int iters, uint32_t seed, float* sink) {
   __shared__ u32x4 ops[kOperandChunks];
   __shared__ u32x4 scl[kScaleChunks];
-  __shared__ f16x8 shared_b[VARIANT == 7 ? kShareChunks : 1];
+  __shared__ f16x8 shared_b[VARIANT == 7 || VARIANT == 8 ? kShareChunks : 1];
   const int tid = (int)threadIdx.x;
   const uint32_t salt = seed ^ (blockIdx.x * 0x9e3779b9u);
   for (int c = tid; c < kOperandChunks; c += NT) {
@@ -208,6 +208,37 @@ __global__ __launch_bounds__(NT) void mainloop_probe_kernel(int iters, uint32_t 
 #pragma unroll
           for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
       }
+    } else if constexpr (VARIANT == 8) {
+      // variant 7 with the exchange a step ahead: after the one barrier of the
+      // iteration, the waves read this iteration's B (written during the
+      // previous iteration), and while its MFMAs run each wave dequantises its
+      // quarter of the next iteration's B (from the same words, standing in
+      // for the next stage's) into the other buffer. The writes are long done
+      // by the next barrier, which only absorbs the waves' skew.
+      __syncthreads();
+      const f16x8* rb = shared_b + (it & 1) * (4 * 4 * 64);
+      f16x8* wb = shared_b + ((it + 1) & 1) * (4 * 4 * 64);
+      const f16x2 y = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc[0], 1.0f, true);
+      _Float16 sa[2][2];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const f16x2 x = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc[f], 1.0f, false);
+        sa[f][0] = x[0];
+        sa[f][1] = x[1];
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        f16x8 fa[2], fb[4];
+#pragma unroll
+        for (int f = 0; f < 2; ++f) fa[f] = dequant8(a[f][s], sa[f][s >> 1]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fb[j] = rb[(j * 4 + s) * 64 + lane];
+        wb[(wave * 4 + s) * 64 + lane] = dequant8(b[0][s], y[s >> 1]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+      }
     } else if constexpr (VARIANT == 1) {
       // (a): per 16-K step, one FP4 MFMA per 32x32 block carrying that step's
       // 16-block only (8 codes per lane half, zeros elsewhere), then the
@@ -298,7 +329,7 @@ __global__ __launch_bounds__(NT) void mainloop_probe_kernel(int iters, uint32_t 
 
   float total = 0.0f;
 #pragma unroll
-  for (int i = 0; i < (VARIANT == 7 ? 2 : 4); ++i)
+  for (int i = 0; i < (VARIANT == 7 || VARIANT == 8 ? 2 : 4); ++i)
 #pragma unroll
     for (int j = 0; j < (VARIANT == 1 || VARIANT == 5 || VARIANT == 6 ? 2 : 4); ++j)
 #pragma unroll
@@ -329,7 +360,7 @@ thread_local int g_last_hip_error = 0;  // per calling thread, like the library'
 extern "C" {
 
 int nvfp4_probe_mainloop(int variant, int iters, int grid, float* sink, void* stream) {
-  if (variant < 0 || variant > 7 || iters < 1 || grid < 1 || grid > 65536 || sink == nullptr) return -1;
+  if (variant < 0 || variant > 8 || iters < 1 || grid < 1 || grid > 65536 || sink == nullptr) return -1;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const uint32_t seed = 0x5eed1234u;
   switch (variant) {
@@ -342,7 +373,8 @@ int nvfp4_probe_mainloop(int variant, int iters, int grid, float* sink, void* st
     case 6:
       hipLaunchKernelGGL((mainloop_probe_kernel<6, kMaxThreads>), dim3(grid), dim3(kMaxThreads), 0, st, iters, seed, sink);
       break;
-    default: hipLaunchKernelGGL(mainloop_probe_kernel<7>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
+    case 7: hipLaunchKernelGGL(mainloop_probe_kernel<7>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
+    default: hipLaunchKernelGGL(mainloop_probe_kernel<8>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
@@ -372,7 +404,7 @@ double nvfp4_probe_flops_per_iteration(int variant) {
   // variant 3 does it in 32 scaled FP4 MFMAs, variant 4 in 128 MFMAs of
   // 16x16x32 on a 128x64 tile), or 32 for variants 1, 5 and 6 (128x64);
   // four waves per workgroup, eight for variant 6
-  const double per_wave = (variant == 1 || variant >= 5) ? 32.0 : 64.0;  // variant 7: 64x128 wave tiles
+  const double per_wave = (variant == 1 || variant >= 5) ? 32.0 : 64.0;  // variants 7, 8: 64x128 wave tiles
   return per_wave * 2.0 * 32.0 * 32.0 * 16.0 * (variant == 6 ? 8.0 : 4.0);
 }
 

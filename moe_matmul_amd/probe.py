@@ -18,6 +18,7 @@ VARIANT_BARE_F16_16X16 = 4  # the f16 MFMA loop alone with the 16x16x32 shape
 VARIANT_DEQUANT_128X64 = 5  # (b) on a 128x64 wave tile, one wave per SIMD
 VARIANT_DEQUANT_128X64_2W = 6  # the same, two waves per SIMD (512-thread workgroups)
 VARIANT_DEQUANT_SHARED_B = 7  # (b) on 64x128 wave tiles with B dequantised once per workgroup, shared in LDS
+VARIANT_DEQUANT_SHARED_B_AHEAD = 8  # the same with the exchange a step ahead
 SINK_PER_WORKGROUP = 512
 
 _lib = None
