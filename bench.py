@@ -284,13 +284,16 @@ def mainloop_probe(iters_f16=2000, iters_fp4=400, reps=5):
              probe.VARIANT_DEQUANT_128X64: "(b) on a 128x64 wave tile, one wave per SIMD",
              probe.VARIANT_DEQUANT_128X64_2W: "(b) on a 128x64 wave tile, two waves per SIMD",
              probe.VARIANT_DEQUANT_SHARED_B: "(b) on 64x128 wave tiles, B dequantised once and shared in LDS",
-             probe.VARIANT_DEQUANT_SHARED_B_AHEAD: "the same with the exchange a step ahead"}
+             probe.VARIANT_DEQUANT_SHARED_B_AHEAD: "the same with the exchange a step ahead",
+             probe.VARIANT_BARE_F16_6BIT: "bare f16 loop, operands with 6 significant bits (like a * s)",
+             probe.VARIANT_BARE_BF16_6BIT: "bare v_mfma_f32_32x32x16_bf16 loop, operands with 6 significant bits"}
     out = {"grid": grid, "variants": []}
     for v, iters in ((probe.VARIANT_BARE_F16, iters_f16), (probe.VARIANT_DEQUANT_F16, iters_f16),
                      (probe.VARIANT_FP4_VALU, iters_fp4), (probe.VARIANT_BARE_FP4, iters_f16),
                      (probe.VARIANT_BARE_F16_16X16, iters_f16), (probe.VARIANT_DEQUANT_128X64, iters_f16),
                      (probe.VARIANT_DEQUANT_128X64_2W, iters_f16), (probe.VARIANT_DEQUANT_SHARED_B, iters_f16),
-                     (probe.VARIANT_DEQUANT_SHARED_B_AHEAD, iters_f16)):
+                     (probe.VARIANT_DEQUANT_SHARED_B_AHEAD, iters_f16), (probe.VARIANT_BARE_F16_6BIT, iters_f16),
+                     (probe.VARIANT_BARE_BF16_6BIT, iters_f16)):
         probe.nvfp4_probe_mainloop(v, iters, grid, sink.data_ptr(), stream.cuda_stream)  # warm-up
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         start.record(stream)

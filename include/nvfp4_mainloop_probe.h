@@ -48,7 +48,11 @@ extern "C" {
  *              fragments) and shared through LDS with one barrier per
  *              iteration (3 dequantisation VALU per MFMA);
  *   variant 8: variant 7 with the exchange a step ahead (each iteration
- *              writes the next one's B while its MFMAs run).
+ *              writes the next one's B while its MFMAs run);
+ *   variant 9: variant 2 on operands with 6 significant bits (like the
+ *              dequantised a * s) instead of a random 10-bit mantissa;
+ *   variant 10: the bare bf16 MFMA loop (v_mfma_f32_32x32x16_bf16) on
+ *              operands with 6 significant bits.
  *   sink: device fp32 [grid * 512], written with per-lane sums (so the work
  *         is kept).
  */

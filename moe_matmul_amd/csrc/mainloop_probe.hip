@@ -38,6 +38,7 @@ namespace {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -107,8 +108,13 @@ __global__ __launch_bounds__(NT) void mainloop_probe_kernel(int iters, uint32_t 
     u32x4 v;
     for (int q = 0; q < 4; ++q) {
       const uint32_t r = mix(salt + (uint32_t)(4 * c + q) * 2654435761u);
-      // the bare loop reads f16 pairs: sign, exponent 15 (1.0 .. 2.0), random mantissa
-      v[q] = VARIANT == 2 ? ((r & 0x83ff83ffu) | 0x3c003c00u) : r;
+      // the bare loops read f16 (or bf16) pairs in [1, 2) with a random sign:
+      // a random 10-bit mantissa (variant 2), or 6 significant bits like the
+      // dequantised a * s operands (variant 9: f16, variant 10: bf16)
+      v[q] = VARIANT == 2    ? ((r & 0x83ff83ffu) | 0x3c003c00u)
+             : VARIANT == 9  ? ((r & 0x83e083e0u) | 0x3c003c00u)
+             : VARIANT == 10 ? ((r & 0x807c807cu) | 0x3f803f80u)
+                             : r;
     }
     ops[c] = v;
   }
@@ -310,8 +316,23 @@ __global__ __launch_bounds__(NT) void mainloop_probe_kernel(int iters, uint32_t 
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             acc16[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(fb[(j + s) & 3], fa[(i + s) & 3], acc16[i][j], 0, 0, 0);
+    } else if constexpr (VARIANT == 10) {
+      // the bare bf16 MFMA loop on 6-significant-bit operands
+      bf16x8 fa[4], fb[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        fa[f] = __builtin_bit_cast(bf16x8, a[f]);
+        fb[f] = __builtin_bit_cast(bf16x8, b[f]);
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
     } else {
-      // the bare f16 MFMA loop: the same MFMAs on operands read from LDS
+      // the bare f16 MFMA loop (variants 2 and 9): the same MFMAs on operands
+      // read from LDS
       f16x8 fa[4], fb[4];
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
@@ -331,7 +352,7 @@ __global__ __launch_bounds__(NT) void mainloop_probe_kernel(int iters, uint32_t 
 #pragma unroll
   for (int i = 0; i < (VARIANT == 7 || VARIANT == 8 ? 2 : 4); ++i)
 #pragma unroll
-    for (int j = 0; j < (VARIANT == 1 || VARIANT == 5 || VARIANT == 6 ? 2 : 4); ++j)
+    for (int j = 0; j < (VARIANT == 1 || VARIANT == 5 || VARIANT == 6 ? 2 : 4); ++j)  // 9, 10: 4
 #pragma unroll
       for (int e = 0; e < 16; ++e) total += acc[i][j][e];
   if constexpr (VARIANT == 4) {
@@ -360,7 +381,7 @@ thread_local int g_last_hip_error = 0;  // per calling thread, like the library'
 extern "C" {
 
 int nvfp4_probe_mainloop(int variant, int iters, int grid, float* sink, void* stream) {
-  if (variant < 0 || variant > 8 || iters < 1 || grid < 1 || grid > 65536 || sink == nullptr) return -1;
+  if (variant < 0 || variant > 10 || iters < 1 || grid < 1 || grid > 65536 || sink == nullptr) return -1;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const uint32_t seed = 0x5eed1234u;
   switch (variant) {
@@ -374,7 +395,9 @@ int nvfp4_probe_mainloop(int variant, int iters, int grid, float* sink, void* st
       hipLaunchKernelGGL((mainloop_probe_kernel<6, kMaxThreads>), dim3(grid), dim3(kMaxThreads), 0, st, iters, seed, sink);
       break;
     case 7: hipLaunchKernelGGL(mainloop_probe_kernel<7>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
-    default: hipLaunchKernelGGL(mainloop_probe_kernel<8>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
+    case 8: hipLaunchKernelGGL(mainloop_probe_kernel<8>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
+    case 9: hipLaunchKernelGGL(mainloop_probe_kernel<9>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
+    default: hipLaunchKernelGGL(mainloop_probe_kernel<10>, dim3(grid), dim3(kThreads), 0, st, iters, seed, sink); break;
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
@@ -404,7 +427,7 @@ double nvfp4_probe_flops_per_iteration(int variant) {
   // variant 3 does it in 32 scaled FP4 MFMAs, variant 4 in 128 MFMAs of
   // 16x16x32 on a 128x64 tile), or 32 for variants 1, 5 and 6 (128x64);
   // four waves per workgroup, eight for variant 6
-  const double per_wave = (variant == 1 || variant >= 5) ? 32.0 : 64.0;  // variants 7, 8: 64x128 wave tiles
+  const double per_wave = (variant == 1 || (variant >= 5 && variant <= 8)) ? 32.0 : 64.0;  // 7, 8: 64x128 wave tiles
   return per_wave * 2.0 * 32.0 * 32.0 * 16.0 * (variant == 6 ? 8.0 : 4.0);
 }
 

@@ -19,6 +19,8 @@ VARIANT_DEQUANT_128X64 = 5  # (b) on a 128x64 wave tile, one wave per SIMD
 VARIANT_DEQUANT_128X64_2W = 6  # the same, two waves per SIMD (512-thread workgroups)
 VARIANT_DEQUANT_SHARED_B = 7  # (b) on 64x128 wave tiles with B dequantised once per workgroup, shared in LDS
 VARIANT_DEQUANT_SHARED_B_AHEAD = 8  # the same with the exchange a step ahead
+VARIANT_BARE_F16_6BIT = 9  # the bare f16 loop on 6-significant-bit operands (like a * s)
+VARIANT_BARE_BF16_6BIT = 10  # the bare bf16 loop on 6-significant-bit operands
 SINK_PER_WORKGROUP = 512
 
 _lib = None

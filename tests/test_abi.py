@@ -303,7 +303,7 @@ def test_probe_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", probe.PROBE_LIB_PATH], capture_output=True, text=True).stdout
     assert sorted(set(re.findall(r"\bT (nvfp4_\w+)", out))) == names
     # argument checks run before any HIP call
-    assert lib.nvfp4_probe_mainloop(9, 1, 1, 0x1000, None) == -1
+    assert lib.nvfp4_probe_mainloop(11, 1, 1, 0x1000, None) == -1
     assert lib.nvfp4_probe_mainloop(0, 0, 1, 0x1000, None) == -1
     assert lib.nvfp4_probe_mainloop(0, 1, 1, None, None) == -1
     assert lib.nvfp4_probe_cvt_scale(None, 1, None, None) == -1
