@@ -57,13 +57,45 @@ def fmt_us(v):
     return "n/a" if v is None else f"{v:.1f}"
 
 
+def settle(call, seconds):
+    """Runs the hot path back to back for about ``seconds`` before the warm-up
+    steps. After the GPU has idled (input generation and upload take seconds
+    on the host), its power management lets the first millisecond or so run at
+    a high clock, then cuts the clock hard and takes some 10-20 ms to reach
+    its steady state: the GEMM kernel's duration on the dense workload goes
+    ~310 us -> ~390 us -> ~320 us over the first ~40 calls (rocprofv3 kernel
+    trace of bench.py --steps 20 --warmup 5). A few warm-up steps end inside
+    that dip, so the timed steps would measure the controller's transient, not
+    the kernel. Returns the number of calls made."""
+    import torch
+    if seconds <= 0:
+        return 0
+    n = 0
+    t0 = time.perf_counter()
+    for _ in range(4):
+        call(n)
+        n += 1
+    torch.cuda.synchronize()
+    per = max((time.perf_counter() - t0) / 4, 1e-6)
+    # the rest in one go (no synchronisation, so the GPU never idles)
+    for _ in range(max(0, int(seconds / per) - 4)):
+        call(n)
+        n += 1
+    torch.cuda.synchronize()
+    return n
+
+
 def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None, device_tables=False,
-                  super_batch=False, pow2=False):
+                  super_batch=False, pow2=False, settle_s=0.0, from_idle=False):
     """Times the grouped GEMM on workload ``idx``. ``device_tables``: through
     nvfp4_grouped_gemm_device (group tables in device memory); ``super_batch``:
     the groups of 15 calls of the workload in one launch (device tables);
     ``pow2``: the workload with power-of-two scales through
-    nvfp4_grouped_gemm_pow2 (its status word checked afterwards)."""
+    nvfp4_grouped_gemm_pow2 (its status word checked afterwards).
+    ``settle_s``: seconds of back-to-back calls before the warm-up steps (see
+    settle). ``from_idle``: also time ``steps`` calls after only the warm-up
+    steps, straight after the input set-up (before the settle), as a run
+    without the settle would."""
     import torch
 
     import moe_matmul_amd as mm
@@ -113,6 +145,21 @@ def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None
             mm.nvfp4_grouped_gemm_ex(ps, abc, sf, len(shapes), ws.data_ptr(), ws.numel(), tile_config,
                                      split_mode, st)
 
+    idle_ms = None
+    if from_idle:
+        for i in range(warmup):
+            call(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(steps):
+            call(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        idle_ms = a.elapsed_time(b) / steps
+    settle_t0 = time.perf_counter()
+    settle_calls = settle(call, settle_s)
+    settle_wall = time.perf_counter() - settle_t0
     for i in range(warmup):
         call(i)
     torch.cuda.synchronize()
@@ -148,14 +195,14 @@ def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None
         geo = dict(config=cfg, split=0, grid=cus,
                    total_tiles=sum(mm.nvfp4_device_group_tiles(s, p0, tile_config) for s in shapes))
     else:
-        geo = mm.nvfp4_launch_geometry(shapes, cus, tile_config, -1 if split_mode is None else split_mode)
+        # without a workspace (split_mode None: nvfp4_grouped_gemm_config) the library plans whole tiles
+        geo = mm.nvfp4_launch_geometry(shapes, cus, tile_config, 0 if split_mode is None else split_mode)
     avg_s = total_ms / steps / 1e3
     # The same calls replayed from a captured HIP graph: GPU time per call
     # without host launch overhead (what matters for the microsecond-sized
-    # workloads). Whole-tile plans only (a stream-K plan's library workspace
-    # would be allocated during capture).
+    # workloads).
     graph_us = None
-    if split_mode is None and geo["split"] == 0:
+    if split_mode is None:
         reps = min(steps, 50)
         side = torch.cuda.Stream()
         side.wait_stream(stream)
@@ -168,6 +215,14 @@ def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None
                 call(i, side)
         g.replay()
         torch.cuda.synchronize()
+        # capture idled the GPU: replays for the settle time before the timed one
+        if settle_s > 0:
+            t_rep = time.perf_counter()
+            g.replay()
+            torch.cuda.synchronize()
+            for _ in range(int(settle_s / max(time.perf_counter() - t_rep, 1e-6))):
+                g.replay()
+            torch.cuda.synchronize()
         ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         ga.record(stream)
         g.replay()
@@ -188,7 +243,28 @@ def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None
         us_median=percentile(per, 50) * 1e3, us_p10=percentile(per, 10) * 1e3, us_p90=percentile(per, 90) * 1e3,
         tflops=flops / avg_s / 1e12, gbs=nbytes / avg_s / 1e9, sets=len(sets), tile_config=geo["config"],
         tiles=geo["total_tiles"], grid=geo["grid"], split=geo["split"], graph_us_per_call=graph_us,
+        settle_calls=settle_calls, settle_s=settle_wall, from_idle_ms_per_call=idle_ms,
     )
+
+
+def config_row(idx, r):
+    """One workload's row of the JSON line: time per call, throughput, and the
+    fraction of the roofline that bounds it (the dense f16 MFMA peak or HBM,
+    whichever takes longer for the algorithmic FLOPs and bytes)."""
+    t = r["ms_per_call"] / 1e3
+    t_mfma = r["flops"] / (PEAK_F16_TFLOPS * 1e12)
+    t_hbm = r["bytes"] / (PEAK_HBM_GBS * 1e9)
+    bound = "mfma" if t_mfma >= t_hbm else "hbm"
+    return {
+        "workload": r["workload"], "index": idx, "shapes_mnkl": r["shapes"],
+        "us_per_call": {"timed_mean": round(r["ms_per_call"] * 1e3, 2), "median": round(r["us_median"], 2),
+                        "graph_replay": None if r["graph_us_per_call"] is None else round(r["graph_us_per_call"], 2)},
+        "tflops": round(r["tflops"], 2), "algorithmic_gbs": round(r["gbs"], 1),
+        "roofline": {"bound": bound, "frac": round(max(t_mfma, t_hbm) / t, 4),
+                     "mfma_frac": round(t_mfma / t, 4), "hbm_frac": round(t_hbm / t, 4),
+                     "roofline_us": round(max(t_mfma, t_hbm) * 1e6, 3)},
+        "plan": {"tile_config": r["tile_config"], "stream_k": bool(r["split"]), "tiles": r["tiles"], "grid": r["grid"]},
+    }
 
 
 def cpu_model():
@@ -343,6 +419,11 @@ def main():
                     help="also time the inner loops of the two exact scale applications (measurement kernels)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (counter calibration)")
+    ap.add_argument("--settle", type=float, default=0.3,
+                    help="seconds of untimed back-to-back calls before each leg's warm-up steps, so the timed "
+                         "steps run at the GPU's steady-state clock (0 disables)")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="leave out the rows of the other workloads (0-3) from the JSON line")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -363,17 +444,32 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
-    head = time_workload(args.workload, args.steps, args.warmup, args.tile_config, cold=True)
-    hot = time_workload(args.workload, args.steps, args.warmup, args.tile_config, cold=False)
+    head = time_workload(args.workload, args.steps, args.warmup, args.tile_config, cold=True, settle_s=args.settle,
+                         from_idle=True)
+    hot = time_workload(args.workload, args.steps, args.warmup, args.tile_config, cold=False, settle_s=args.settle)
     log(f"[bench] cold {head['tflops']:.1f} TFLOP/s {head['ms_per_call'] * 1e3:.1f} us/call "
-        f"(median of single calls {head['us_median']:.1f}); "
-        f"hot {hot['tflops']:.1f} TFLOP/s; graph replay {fmt_us(head['graph_us_per_call'])} us/call")
+        f"(median of single calls {head['us_median']:.1f}; from idle, without the settle, "
+        f"{head['from_idle_ms_per_call'] * 1e3:.1f}); "
+        f"hot {hot['tflops']:.1f} TFLOP/s; graph replay {fmt_us(head['graph_us_per_call'])} us/call; "
+        f"settle {head['settle_calls']} calls in {head['settle_s']:.2f} s")
     details = {"headline": head, "hot": hot}
+    rows = []
+    if not args.no_per_config:
+        for i in range(5):
+            if i == args.workload:
+                r = head
+            else:
+                r = time_workload(i, args.steps, args.warmup, -1, cold=True, settle_s=args.settle)
+            rows.append(config_row(i, r))
+            log(f"[bench] workload {i} {r['workload']}: {r['ms_per_call'] * 1e3:.2f} us/call (median "
+                f"{r['us_median']:.2f}, graph replay {fmt_us(r['graph_us_per_call'])}), {r['tflops']:.1f} TFLOP/s, "
+                f"{rows[-1]['roofline']['bound']}-bound, frac {rows[-1]['roofline']['frac']:.3f}")
+        details["per_config"] = rows
     p2 = None
     if not args.no_pow2_line:
         # the same workload with power-of-two scales through the MX entry point
         p2 = time_workload(args.workload, max(20, args.steps // 2), args.warmup, args.tile_config, cold=True,
-                           pow2=True)
+                           pow2=True, settle_s=args.settle)
         log(f"[bench] power-of-two scales (nvfp4_grouped_gemm_pow2): {p2['tflops']:.1f} TFLOP/s "
             f"{p2['ms_per_call'] * 1e3:.1f} us/call (median {p2['us_median']:.1f})")
         details["pow2_headline"] = p2
@@ -467,7 +563,12 @@ def main():
                         "median": round(head["us_median"], 2), "p10": round(head["us_p10"], 2),
                         "p90": round(head["us_p90"], 2),
                         "graph_replay": None if head["graph_us_per_call"] is None
-                        else round(head["graph_us_per_call"], 2)},
+                        else round(head["graph_us_per_call"], 2),
+                        "timed_mean_from_idle": round(head["from_idle_ms_per_call"] * 1e3, 2)},
+        "settle": {"seconds": round(head["settle_s"], 3), "calls": head["settle_calls"],
+                   "why": "untimed back-to-back calls before the warm-up steps: after idling, the GPU's power "
+                          "management runs the first ~1 ms fast, then throttles for ~10-20 ms before its steady "
+                          "state; timed_mean_from_idle is the same K steps right after the input set-up"},
         "hot": {"value": round(hot["tflops"], 2), "us_median": round(hot["us_median"], 2)},
         "algorithmic_gbs": round(head["gbs"], 1),
         "roofline": {
@@ -491,6 +592,7 @@ def main():
                          "note": "half of every FP4 MFMA's K is zero padding (16-element scale blocks on a "
                                  "32-element scale slice), so this instruction form tops out at half the FP4 peak"},
         },
+        "per_config": rows,
         "cpu_baseline": None if cpu is None else {k: (round(v, 6) if isinstance(v, float) else v)
                                                   for k, v in cpu.items() if k in ("value", "unit", "cores",
                                                                                    "kind", "sample")},

@@ -37,15 +37,15 @@
  * workspace of two fp32 tile-sized slots per workgroup; it holds no state
  * between calls.
  *
- * Ownership and threading: the caller owns every buffer. Host tables are read
- * before a call returns. Calls are stream-ordered and asynchronous. The
- * library's global state is a per-device cache of the compute-unit count, a
- * per-thread cache of the last eight plans (keyed by the problem sizes, the
- * compute units and the forced choices; no buffer address is kept) and,
- * for nvfp4_grouped_gemm / nvfp4_grouped_gemm_config only, a stream-K
- * workspace per (device, stream) that the library allocates with hipMalloc on
- * first need (grown when a call needs more, kept until the process ends).
- * nvfp4_grouped_gemm_ex takes a caller workspace and allocates nothing.
+ * Ownership and threading: the caller owns every buffer, the workspace
+ * included; the library allocates no device memory and makes no synchronising
+ * HIP call, so every entry point can be captured in a HIP graph. Host tables
+ * are read before a call returns. Calls are stream-ordered and asynchronous.
+ * The library's global state is a per-device cache of the compute-unit count
+ * and a per-thread cache of the last eight plans (keyed by the problem sizes,
+ * the compute units, the forced choices and the workspace size; no buffer
+ * address is kept). Without a workspace (nvfp4_grouped_gemm,
+ * nvfp4_grouped_gemm_config, or a NULL workspace) a call uses whole tiles.
  */
 #ifndef NVFP4_GROUPED_GEMM_H
 #define NVFP4_GROUPED_GEMM_H
@@ -84,8 +84,9 @@ extern "C" {
  *   non-null and 16-byte aligned, and when k > 0 also A, B, SFA and SFB.
  * Semantics at the edges: a group with m == 0 or n == 0 leaves C untouched;
  * k == 0 writes C = 0 (the empty sum).
+ * Whole tiles only (no workspace); nothing is allocated.
  * Returns NVFP4_OK once the kernel is enqueued, NVFP4_ERR_HIP if the launch
- * (or the first allocation of the stream-K workspace) failed.
+ * failed.
  */
 int nvfp4_grouped_gemm(const int32_t* problem_sizes, const uint64_t* ptrs_abc,
                        const uint64_t* ptrs_sfa_sfb, int num_groups, void* stream);
@@ -105,6 +106,21 @@ int nvfp4_grouped_gemm(const int32_t* problem_sizes, const uint64_t* ptrs_abc,
 int nvfp4_grouped_gemm_ex(const int32_t* problem_sizes, const uint64_t* ptrs_abc,
                           const uint64_t* ptrs_sfa_sfb, int num_groups, void* workspace,
                           size_t workspace_bytes, int tile_config, int split_mode, void* stream);
+
+/*
+ * nvfp4_grouped_gemm_stages - as nvfp4_grouped_gemm_ex with the depth of the
+ * LDS operand pipeline chosen: `stages` 4 (the depth every other entry point
+ * uses) or 3. For verification: the results are bitwise identical to those of
+ * nvfp4_grouped_gemm_ex with the same tile_config and split_mode (same
+ * plan, same per-tile arithmetic), while each LDS buffer is reloaded one stage
+ * sooner after its last reads, so a missing wait or barrier between a buffer's
+ * readers and its next loads shows up as a difference. Returns
+ * NVFP4_ERR_CONFIG for another `stages`, else as nvfp4_grouped_gemm_ex.
+ */
+int nvfp4_grouped_gemm_stages(const int32_t* problem_sizes, const uint64_t* ptrs_abc,
+                              const uint64_t* ptrs_sfa_sfb, int num_groups, void* workspace,
+                              size_t workspace_bytes, int tile_config, int split_mode, int stages,
+                              void* stream);
 
 /*
  * nvfp4_grouped_gemm_device - the same grouped GEMM with the group tables in

@@ -54,6 +54,9 @@ def load_library() -> ctypes.CDLL:
                                                  i64p, ip, ip, ctypes.POINTER(ctypes.c_size_t)]),
         "nvfp4_grouped_gemm_ex": (ctypes.c_int, [i32p, u64p, u64p, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
                                                  ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
+        "nvfp4_grouped_gemm_stages": (ctypes.c_int, [i32p, u64p, u64p, ctypes.c_int, ctypes.c_void_p,
+                                                     ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                     ctypes.c_void_p]),
         "nvfp4_grouped_gemm_pow2": (ctypes.c_int, [i32p, u64p, u64p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                                    ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
         "nvfp4_grouped_gemm_device": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
@@ -86,6 +89,19 @@ def _u64(rows, width):
     if len(flat) % width:
         raise ValueError(f"pointer table rows must have {width} entries")
     return (ctypes.c_uint64 * max(len(flat), 1))(*flat)
+
+
+def _groups(num_groups, ps, g, tables=()):
+    """The group count to pass to C: ``num_groups`` or the rows of the sizes
+    table. It may not exceed the rows of any marshalled table, or the library
+    would read host memory past the ctypes arrays."""
+    if num_groups is None:
+        return g
+    n = int(num_groups)
+    rows = [len(ps) // 4] + [len(t) // w for t, w in tables]
+    if n > min(rows):
+        raise ValueError(f"num_groups {n} exceeds the rows of the argument tables ({min(rows)})")
+    return n
 
 
 def _stream(stream) -> ctypes.c_void_p:
@@ -124,9 +140,9 @@ def nvfp4_grouped_gemm_config(problem_sizes, ptrs_abc, ptrs_sfa_sfb, num_groups=
                               tile_config=-1) -> None:
     lib = load_library()
     ps, g = _sizes(problem_sizes)
-    g = g if num_groups is None else int(num_groups)
-    rc = lib.nvfp4_grouped_gemm_config(ps, _u64(ptrs_abc, 3), _u64(ptrs_sfa_sfb, 2), g,
-                                       _stream(stream), int(tile_config))
+    abc, sf = _u64(ptrs_abc, 3), _u64(ptrs_sfa_sfb, 2)
+    g = _groups(num_groups, ps, g, ((abc, 3), (sf, 2)))
+    rc = lib.nvfp4_grouped_gemm_config(ps, abc, sf, g, _stream(stream), int(tile_config))
     if rc != NVFP4_OK:
         raise Nvfp4Error(rc, "nvfp4_grouped_gemm")
 
@@ -134,8 +150,9 @@ def nvfp4_grouped_gemm_config(problem_sizes, ptrs_abc, ptrs_sfa_sfb, num_groups=
 def nvfp4_grouped_gemm_validate(problem_sizes, ptrs_abc, ptrs_sfa_sfb, num_groups=None) -> int:
     lib = load_library()
     ps, g = _sizes(problem_sizes)
-    g = g if num_groups is None else int(num_groups)
-    return lib.nvfp4_grouped_gemm_validate(ps, _u64(ptrs_abc, 3), _u64(ptrs_sfa_sfb, 2), g)
+    abc, sf = _u64(ptrs_abc, 3), _u64(ptrs_sfa_sfb, 2)
+    g = _groups(num_groups, ps, g, ((abc, 3), (sf, 2)))
+    return lib.nvfp4_grouped_gemm_validate(ps, abc, sf, g)
 
 
 def nvfp4_num_tile_configs() -> int:
@@ -152,14 +169,14 @@ def nvfp4_tile_config_info(cfg: int):
 
 def nvfp4_select_tile_config(problem_sizes, num_cus: int, num_groups=None) -> int:
     ps, g = _sizes(problem_sizes)
-    return load_library().nvfp4_select_tile_config(ps, g if num_groups is None else num_groups, int(num_cus))
+    return load_library().nvfp4_select_tile_config(ps, _groups(num_groups, ps, g), int(num_cus))
 
 
 def nvfp4_launch_geometry(problem_sizes, num_cus: int, cfg: int = -1, split: int = -1, num_groups=None):
     ps, g = _sizes(problem_sizes)
     tiles, grid, used = ctypes.c_int64(), ctypes.c_int(), ctypes.c_int()
     ws = ctypes.c_size_t()
-    rc = load_library().nvfp4_launch_geometry(ps, g if num_groups is None else num_groups, int(num_cus),
+    rc = load_library().nvfp4_launch_geometry(ps, _groups(num_groups, ps, g), int(num_cus),
                                               int(cfg), int(split), ctypes.byref(tiles), ctypes.byref(grid),
                                               ctypes.byref(used), ctypes.byref(ws))
     if rc < 0:
@@ -172,11 +189,26 @@ def nvfp4_grouped_gemm_ex(problem_sizes, ptrs_abc, ptrs_sfa_sfb, num_groups=None
     """Grouped GEMM with a caller workspace (device address) and explicit choices."""
     lib = load_library()
     ps, g = _sizes(problem_sizes)
-    g = g if num_groups is None else int(num_groups)
-    rc = lib.nvfp4_grouped_gemm_ex(ps, _u64(ptrs_abc, 3), _u64(ptrs_sfa_sfb, 2), g, ctypes.c_void_p(int(workspace)),
-                                   int(workspace_bytes), int(tile_config), int(split_mode), _stream(stream))
+    abc, sf = _u64(ptrs_abc, 3), _u64(ptrs_sfa_sfb, 2)
+    g = _groups(num_groups, ps, g, ((abc, 3), (sf, 2)))
+    rc = lib.nvfp4_grouped_gemm_ex(ps, abc, sf, g, ctypes.c_void_p(int(workspace)), int(workspace_bytes),
+                                   int(tile_config), int(split_mode), _stream(stream))
     if rc != NVFP4_OK:
         raise Nvfp4Error(rc, "nvfp4_grouped_gemm_ex")
+
+
+def nvfp4_grouped_gemm_stages(problem_sizes, ptrs_abc, ptrs_sfa_sfb, num_groups=None, workspace=0,
+                              workspace_bytes=0, tile_config=-1, split_mode=-1, stages=4, stream=None) -> None:
+    """As nvfp4_grouped_gemm_ex with the LDS pipeline depth chosen (3 or 4);
+    for verification (the results are bitwise those of the default depth)."""
+    lib = load_library()
+    ps, g = _sizes(problem_sizes)
+    abc, sf = _u64(ptrs_abc, 3), _u64(ptrs_sfa_sfb, 2)
+    g = _groups(num_groups, ps, g, ((abc, 3), (sf, 2)))
+    rc = lib.nvfp4_grouped_gemm_stages(ps, abc, sf, g, ctypes.c_void_p(int(workspace)), int(workspace_bytes),
+                                       int(tile_config), int(split_mode), int(stages), _stream(stream))
+    if rc != NVFP4_OK:
+        raise Nvfp4Error(rc, "nvfp4_grouped_gemm_stages")
 
 
 def nvfp4_grouped_gemm_pow2(problem_sizes, ptrs_abc, ptrs_sfa_sfb, d_status, num_groups=None, workspace=0,
@@ -187,8 +219,9 @@ def nvfp4_grouped_gemm_pow2(problem_sizes, ptrs_abc, ptrs_sfa_sfb, d_status, num
     outside that set (then C is not valid)."""
     lib = load_library()
     ps, g = _sizes(problem_sizes)
-    g = g if num_groups is None else int(num_groups)
-    rc = lib.nvfp4_grouped_gemm_pow2(ps, _u64(ptrs_abc, 3), _u64(ptrs_sfa_sfb, 2), g, ctypes.c_void_p(int(d_status)),
+    abc, sf = _u64(ptrs_abc, 3), _u64(ptrs_sfa_sfb, 2)
+    g = _groups(num_groups, ps, g, ((abc, 3), (sf, 2)))
+    rc = lib.nvfp4_grouped_gemm_pow2(ps, abc, sf, g, ctypes.c_void_p(int(d_status)),
                                      ctypes.c_void_p(int(workspace)), int(workspace_bytes), int(tile_config),
                                      int(split_mode), _stream(stream))
     if rc != NVFP4_OK:
@@ -218,7 +251,7 @@ def nvfp4_device_group_tiles(size, ptrs, tile_config=-1) -> int:
 
 def nvfp4_workspace_bytes(problem_sizes, num_cus: int, num_groups=None) -> int:
     ps, g = _sizes(problem_sizes)
-    return int(load_library().nvfp4_workspace_bytes(ps, g if num_groups is None else num_groups, int(num_cus)))
+    return int(load_library().nvfp4_workspace_bytes(ps, _groups(num_groups, ps, g), int(num_cus)))
 
 
 def nvfp4_sf_bytes(rows: int, k: int, l: int = 1) -> int:

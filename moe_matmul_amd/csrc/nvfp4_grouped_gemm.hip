@@ -148,13 +148,13 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, int32_t num_bytes) 
 // 16 bytes per lane from global (buffer, bounds-checked) straight into LDS at
 // lds_block + 16 * lane (M0 holds the wave's LDS base). Issued as inline asm so
 // the compiler does not treat it as an LDS write it must wait for: the kernel
-// tracks these loads itself with exact vmcnt waits.
+// tracks these loads itself with exact vmcnt waits. The LDS base is an M0
+// input operand, so the compiler sets M0 itself and knows what it holds.
 __device__ __forceinline__ void load_lds16(i32x4 rsrc, uint32_t lds_block, int voffset) {
   // the resource and the LDS address are wave-uniform (the caller passes rsrc
   // through readfirstlane); say so, so they stay in SGPRs
   const uint32_t lds_addr = __builtin_amdgcn_readfirstlane(lds_block);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(lds_addr), "v"(voffset), "s"(rsrc) : "memory", "m0");
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" :: "v"(voffset), "s"(rsrc), "{m0}"(lds_addr) : "memory");
 }
 
 // The waits are emitted with the builtin (not as asm text) so that the
@@ -1386,6 +1386,10 @@ struct TileConfig {
   void (*reduce)(KernelArgs);
   void (*device_kernel)(DeviceGroupArgs);
   int64_t (*device_tiles)(const int32_t*, const uint64_t*);  // the device kernel's per-group check
+  // The same computation with a three-stage LDS pipeline (any k), for
+  // verification: each LDS buffer is then rewritten one stage sooner after
+  // its last reads, so a missing wait or barrier shows up as a difference.
+  void (*kernel_ns3)(KernelArgs);
 };
 
 constexpr int kStages = 4;  // LDS pipeline depth (4 x 36 KiB for 256x256 tiles)
@@ -1396,7 +1400,7 @@ constexpr int kStages = 4;  // LDS pipeline depth (4 x 36 KiB for 256x256 tiles)
     nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, kStages, false, true>,                           \
     nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, kStages, true, true>,                            \
     nvfp4_streamk_reduce_kernel<bm, bn, wm, wn, kStages>, nvfp4_grouped_gemm_device_kernel<bm, bn, wm, wn, kStages>, \
-    device_group_tiles<bm, bn> }
+    device_group_tiles<bm, bn>, nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, 3, true> }
 const TileConfig kConfigs[] = {
     NVFP4_TILE_CONFIG(256, 256, 128, 128),
     NVFP4_TILE_CONFIG(128, 256, 64, 128),
@@ -1623,16 +1627,17 @@ Plan plan_for(const int32_t* ps, int G, int cus, int cfg, int split) {
 // Picks the cheapest (config, mode): the best whole-tile plan, unless the best
 // stream-K plan is modelled at least 15% cheaper (measured on the workloads:
 // stream-K only pays when whole tiles would leave most compute units idle for
-// long, e.g. few tiles with a long K). Forced values are honoured.
-Plan choose_plan(const int32_t* ps, int G, int cus, int force_cfg, int force_split, bool split_allowed) {
+// long, e.g. few tiles with a long K). Stream-K plans whose workspace exceeds
+// ws_cap are not candidates. Forced values are honoured.
+Plan choose_plan(const int32_t* ps, int G, int cus, int force_cfg, int force_split, size_t ws_cap) {
   Plan best[2] = {};
   bool have[2] = {false, false};
   for (int c = 0; c < kNumConfigs; ++c) {
     if (force_cfg >= 0 && c != force_cfg) continue;
     for (int sp = 0; sp < 2; ++sp) {
-      if ((force_split >= 0 && sp != force_split) || (sp == 1 && !split_allowed)) continue;
+      if (force_split >= 0 && sp != force_split) continue;
       const Plan p = plan_for(ps, G, cus, c, sp);
-      if (sp == 1 && p.units == 0) continue;  // nothing to split (all k = 0)
+      if (sp == 1 && (p.units == 0 || p.ws_bytes > ws_cap)) continue;  // nothing to split, or no room
       if (!have[sp] || p.cost < best[sp].cost) {
         best[sp] = p;
         have[sp] = true;
@@ -1650,15 +1655,15 @@ Plan choose_plan(const int32_t* ps, int G, int cus, int force_cfg, int force_spl
 // with other buffers, so each thread keeps its last few plans.
 struct PlanKey {
   int G, cus, cfg, split;
-  bool split_allowed;
+  size_t ws_cap;
   int32_t sizes[4 * kMaxGroups];
   bool operator==(const PlanKey& o) const {
-    return G == o.G && cus == o.cus && cfg == o.cfg && split == o.split && split_allowed == o.split_allowed &&
+    return G == o.G && cus == o.cus && cfg == o.cfg && split == o.split && ws_cap == o.ws_cap &&
            std::memcmp(sizes, o.sizes, sizeof(int32_t) * 4 * G) == 0;
   }
 };
 
-Plan cached_plan(const int32_t* ps, int G, int cus, int force_cfg, int force_split, bool split_allowed) {
+Plan cached_plan(const int32_t* ps, int G, int cus, int force_cfg, int force_split, size_t ws_cap) {
   constexpr int kSlots = 8;
   static thread_local PlanKey keys[kSlots];
   static thread_local Plan plans[kSlots];
@@ -1668,11 +1673,11 @@ Plan cached_plan(const int32_t* ps, int G, int cus, int force_cfg, int force_spl
   k.cus = cus;
   k.cfg = force_cfg;
   k.split = force_split;
-  k.split_allowed = split_allowed;
+  k.ws_cap = ws_cap;
   std::memcpy(k.sizes, ps, sizeof(int32_t) * 4 * G);
   for (int i = 0; i < used; ++i)
     if (keys[i] == k) return plans[i];
-  const Plan p = choose_plan(ps, G, cus, force_cfg, force_split, split_allowed);
+  const Plan p = choose_plan(ps, G, cus, force_cfg, force_split, ws_cap);
   keys[next] = k;
   plans[next] = p;
   next = (next + 1) % kSlots;
@@ -1682,47 +1687,8 @@ Plan cached_plan(const int32_t* ps, int G, int cus, int force_cfg, int force_spl
 
 bool aligned16(uint64_t p) { return (p & 15u) == 0; }
 
-// Library-owned stream-K workspaces, one per (device, stream), grown on demand
-// and kept until the process ends.
-struct Workspace {
-  int dev;
-  void* stream;
-  void* ptr;
-  size_t bytes;
-};
-std::mutex g_ws_mutex;
-std::vector<Workspace> g_ws;
-
-int internal_workspace(void* stream, size_t need, void** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) { t_last_hip_error = (int)e; return NVFP4_ERR_HIP; }
-  std::lock_guard<std::mutex> lock(g_ws_mutex);
-  for (Workspace& w : g_ws) {
-    if (w.dev != dev || w.stream != stream) continue;
-    if (w.bytes >= need) { *out = w.ptr; return NVFP4_OK; }
-    // grow: the old buffer may still be in use by earlier calls on this stream
-    e = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
-    if (e == hipSuccess) e = hipFree(w.ptr);
-    if (e != hipSuccess) { t_last_hip_error = (int)e; return NVFP4_ERR_HIP; }
-    w.ptr = nullptr;
-    w.bytes = 0;
-    e = hipMalloc(&w.ptr, need);
-    if (e != hipSuccess) { t_last_hip_error = (int)e; return NVFP4_ERR_HIP; }
-    w.bytes = need;
-    *out = w.ptr;
-    return NVFP4_OK;
-  }
-  void* ptr = nullptr;
-  e = hipMalloc(&ptr, need);
-  if (e != hipSuccess) { t_last_hip_error = (int)e; return NVFP4_ERR_HIP; }
-  g_ws.push_back(Workspace{dev, stream, ptr, need});
-  *out = ptr;
-  return NVFP4_OK;
-}
-
 int launch(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, void* stream, const Plan& plan,
-           void* workspace, int32_t* mx_status) {
+           void* workspace, int32_t* mx_status, int stages) {
   const TileConfig& tc = kConfigs[plan.cfg];
   KernelArgs args;
   std::memset(&args, 0, sizeof(args));
@@ -1767,6 +1733,7 @@ int launch(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, vo
   bool kpad = false;
   for (int g = 0; g < G; ++g) kpad = kpad || (ps[4 * g + 2] % 64 != 0);
   void (*kernel)(KernelArgs) = mx_status ? (kpad ? tc.kernel_mx_kpad : tc.kernel_mx) : (kpad ? tc.kernel_kpad : tc.kernel);
+  if (stages == 3) kernel = tc.kernel_ns3;
   hipLaunchKernelGGL(kernel, dim3(plan.grid), dim3(kThreads), 0, st, args);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && plan.split && plan.grid > 1) {
@@ -1802,28 +1769,22 @@ int sizes_ok(const int32_t* ps, int G) {
   return NVFP4_OK;
 }
 
-// mx_status: non-null selects the power-of-two-scale kernels, which report there.
+// mx_status: non-null selects the power-of-two-scale kernels, which report
+// there. Stream-K needs a workspace: without one (or with one too small for
+// every stream-K plan) the call runs whole tiles, unless stream-K is forced.
 int run_call(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, void* stream, int cfg, int split,
-             void* workspace, size_t ws_bytes, bool internal_ws, int32_t* mx_status = nullptr) {
+             void* workspace, size_t ws_bytes, int32_t* mx_status = nullptr, int stages = kStages) {
   const int rc = nvfp4_grouped_gemm_validate(ps, abc, sf, G);
   if (rc != NVFP4_OK) return rc;
   if (cfg < -1 || cfg >= kNumConfigs || split < -1 || split > 1) return NVFP4_ERR_CONFIG;
   int cus = 0;
   const int crc = device_cu_count(&cus);
   if (crc != NVFP4_OK) return crc;
-  const bool can_split = internal_ws || workspace != nullptr;
-  if (split == 1 && !can_split) return NVFP4_ERR_WORKSPACE;
-  Plan plan = cached_plan(ps, G, cus, cfg, split, can_split);
-  if (plan.split) {
-    if (internal_ws) {
-      const int wrc = internal_workspace(stream, plan.ws_bytes, &workspace);
-      if (wrc != NVFP4_OK) return wrc;
-    } else if (ws_bytes < plan.ws_bytes) {
-      if (split == 1) return NVFP4_ERR_WORKSPACE;
-      plan = cached_plan(ps, G, cus, cfg, 0, false);  // too small: whole tiles instead
-    }
-  }
-  return launch(ps, abc, sf, G, stream, plan, workspace, mx_status);
+  const size_t cap = workspace != nullptr ? ws_bytes : 0;
+  // forced stream-K is planned without the cap, so that a plan with no room is an error
+  const Plan plan = cached_plan(ps, G, cus, cfg, split, split == 1 ? SIZE_MAX : cap);
+  if (plan.split && plan.ws_bytes > cap) return NVFP4_ERR_WORKSPACE;
+  return launch(ps, abc, sf, G, stream, plan, workspace, mx_status, stages);
 }
 
 }  // namespace
@@ -1887,14 +1848,14 @@ int nvfp4_tile_config_info(int cfg, int* bm, int* bn, int* bk, int* threads) {
 
 int nvfp4_select_tile_config(const int32_t* ps, int G, int num_cus) {
   if (sizes_ok(ps, G) != NVFP4_OK || num_cus < 1) return NVFP4_ERR_INVALID;
-  return choose_plan(ps, G, num_cus, -1, -1, true).cfg;
+  return choose_plan(ps, G, num_cus, -1, -1, SIZE_MAX).cfg;
 }
 
 int nvfp4_launch_geometry(const int32_t* ps, int G, int num_cus, int cfg, int split, int64_t* total_tiles,
                           int* grid, int* split_used, size_t* workspace_bytes) {
   if (sizes_ok(ps, G) != NVFP4_OK || num_cus < 1) return NVFP4_ERR_INVALID;
   if (cfg < -1 || cfg >= kNumConfigs || split < -1 || split > 1) return NVFP4_ERR_CONFIG;
-  const Plan p = cached_plan(ps, G, num_cus, cfg, split, true);
+  const Plan p = cached_plan(ps, G, num_cus, cfg, split, SIZE_MAX);
   if (total_tiles) *total_tiles = p.tiles;
   if (grid) *grid = p.grid;
   if (split_used) *split_used = p.split;
@@ -1915,17 +1876,24 @@ size_t nvfp4_workspace_bytes(const int32_t* ps, int G, int num_cus) {
 
 int nvfp4_grouped_gemm_config(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, void* stream,
                               int cfg) {
-  return run_call(ps, abc, sf, G, stream, cfg, -1, nullptr, 0, true);
+  return run_call(ps, abc, sf, G, stream, cfg, -1, nullptr, 0);
 }
 
 int nvfp4_grouped_gemm(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, void* stream) {
-  return run_call(ps, abc, sf, G, stream, -1, -1, nullptr, 0, true);
+  return run_call(ps, abc, sf, G, stream, -1, -1, nullptr, 0);
 }
 
 int nvfp4_grouped_gemm_ex(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, void* workspace,
                           size_t workspace_bytes, int tile_config, int split_mode, void* stream) {
   if (workspace != nullptr && (reinterpret_cast<uint64_t>(workspace) & 255u) != 0) return NVFP4_ERR_MISALIGNED;
-  return run_call(ps, abc, sf, G, stream, tile_config, split_mode, workspace, workspace_bytes, false);
+  return run_call(ps, abc, sf, G, stream, tile_config, split_mode, workspace, workspace_bytes);
+}
+
+int nvfp4_grouped_gemm_stages(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, void* workspace,
+                              size_t workspace_bytes, int tile_config, int split_mode, int stages, void* stream) {
+  if (stages != 3 && stages != kStages) return NVFP4_ERR_CONFIG;
+  if (workspace != nullptr && (reinterpret_cast<uint64_t>(workspace) & 255u) != 0) return NVFP4_ERR_MISALIGNED;
+  return run_call(ps, abc, sf, G, stream, tile_config, split_mode, workspace, workspace_bytes, nullptr, stages);
 }
 
 int nvfp4_grouped_gemm_pow2(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, int32_t* d_status,
@@ -1933,7 +1901,7 @@ int nvfp4_grouped_gemm_pow2(const int32_t* ps, const uint64_t* abc, const uint64
   if (d_status == nullptr) return NVFP4_ERR_INVALID;
   if ((reinterpret_cast<uint64_t>(d_status) & 3u) != 0) return NVFP4_ERR_MISALIGNED;
   if (workspace != nullptr && (reinterpret_cast<uint64_t>(workspace) & 255u) != 0) return NVFP4_ERR_MISALIGNED;
-  return run_call(ps, abc, sf, G, stream, tile_config, split_mode, workspace, workspace_bytes, false, d_status);
+  return run_call(ps, abc, sf, G, stream, tile_config, split_mode, workspace, workspace_bytes, d_status);
 }
 
 size_t nvfp4_sf_bytes(int rows, int k, int l) {

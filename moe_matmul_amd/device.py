@@ -47,7 +47,7 @@ def run(shapes, dev_groups, stream=None, tile_config=-1, split_mode=None, worksp
 
     With ``split_mode`` or ``workspace`` given, the call goes through
     nvfp4_grouped_gemm_ex with that (uint8 tensor) workspace; otherwise through
-    nvfp4_grouped_gemm_config (library-owned workspace)."""
+    nvfp4_grouped_gemm_config (no workspace: whole tiles)."""
     if stream is None:
         stream = torch.cuda.current_stream()
     abc, sf = pointer_tables(dev_groups)

@@ -122,6 +122,48 @@ def test_compute_call_validates_before_any_hip_call():
     assert e.value.code in (mm.NVFP4_ERR_CONFIG,)
 
 
+def test_num_groups_beyond_the_tables_is_refused():
+    """A group count larger than the rows of any argument table would make the
+    library read host memory past the marshalled arrays: the binding refuses
+    it before calling C, for pre-marshalled arrays too."""
+    shapes = [(64, 64, 64, 1)] * 2
+    abc, sf = _ptrs(2)
+    ps, pabc, psf = mm.prepare(problem_sizes=shapes, ptrs_abc=abc, ptrs_sfa_sfb=sf)
+    calls = [
+        lambda g: mm.nvfp4_grouped_gemm_validate(shapes, abc, sf, g),
+        lambda g: mm.nvfp4_grouped_gemm_validate(ps, pabc, psf, g),
+        lambda g: mm.nvfp4_grouped_gemm_validate(shapes, abc[:1], sf, g),
+        lambda g: mm.nvfp4_grouped_gemm_validate(shapes, abc, sf[:1], g),
+        lambda g: mm.nvfp4_grouped_gemm(shapes, abc, sf, g),
+        lambda g: mm.nvfp4_grouped_gemm_config(ps, pabc, psf, g, None, 0),
+        lambda g: mm.nvfp4_grouped_gemm_ex(shapes, abc, sf, g),
+        lambda g: mm.nvfp4_grouped_gemm_stages(shapes, abc, sf, g, stages=3),
+        lambda g: mm.nvfp4_grouped_gemm_pow2(shapes, abc, sf, 0x10000, g),
+        lambda g: mm.nvfp4_launch_geometry(shapes, 256, num_groups=g),
+        lambda g: mm.nvfp4_select_tile_config(shapes, 256, num_groups=g),
+        lambda g: mm.nvfp4_workspace_bytes(shapes, 256, num_groups=g),
+    ]
+    for i, call in enumerate(calls):
+        with pytest.raises(ValueError):
+            call(3 if i not in (2, 3) else 2)
+    # fewer groups than rows is fine (only the first rows are read)
+    assert mm.nvfp4_grouped_gemm_validate(ps, pabc, psf, 1) == mm.NVFP4_OK
+
+
+def test_stages_entry_point_checks_before_any_hip_call():
+    shapes = [(128, 128, 128, 1)]
+    for stages in (0, 2, 5):
+        with pytest.raises(mm.Nvfp4Error) as e:
+            mm.nvfp4_grouped_gemm_stages(shapes, *_ptrs(1), stages=stages)
+        assert e.value.code == mm.NVFP4_ERR_CONFIG
+    with pytest.raises(mm.Nvfp4Error) as e:
+        mm.nvfp4_grouped_gemm_stages([(128, 100, 128, 1)], *_ptrs(1), stages=3)
+    assert e.value.code == mm.NVFP4_ERR_INVALID
+    with pytest.raises(mm.Nvfp4Error) as e:
+        mm.nvfp4_grouped_gemm_stages(shapes, *_ptrs(1), workspace=0x1010, workspace_bytes=1 << 20, stages=3)
+    assert e.value.code == mm.NVFP4_ERR_MISALIGNED
+
+
 def test_sf_bytes_matches_atom_padding():
     for rows, k, l in [(1, 64, 1), (128, 256, 1), (129, 64, 2), (300, 7168, 1), (0, 64, 1), (5, 0, 1)]:
         assert mm.nvfp4_sf_bytes(rows, k, l) == synth.sf_buffer_bytes(rows, k, l)

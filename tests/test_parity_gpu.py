@@ -152,18 +152,44 @@ def test_streamk_full_workloads(idx):
     check(shapes, groups, split_mode=1, label=f"workload {idx} stream-K")
 
 
-def test_heuristic_streamk_with_library_workspace():
-    """Few tiles with a long K: the heuristic splits K over the whole grid, using
-    the workspace the library allocates itself (default entry point)."""
+def test_default_entry_point_allocates_nothing_and_captures():
+    """Few tiles with a long K: with a workspace the heuristic would split K
+    over the grid, but the default entry point has none and allocates none, so
+    it runs whole tiles, and a HIP graph captured around it replays to the
+    oracle's result (eager work and synchronisation between the replays)."""
     shapes = [(256, 256, 16384, 1), (40, 136, 64, 1)]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    assert mm.nvfp4_launch_geometry(shapes, cus)["split"] == 1
-    check(shapes, synth.make_custom(shapes, seed=12), label="long-K heuristic stream-K")
+    assert mm.nvfp4_launch_geometry(shapes, cus)["split"] == 1  # the plan with a workspace
+    groups = poison_padding(shapes, synth.make_custom(shapes, seed=12))
+    ref = O.grouped_gemm(shapes, groups)
+    announce(f"default entry point, graph capture, shapes={shapes}")
+    d = dev.upload(shapes, groups, c_guard=GUARD)
+    abc, sf = dev.pointer_tables(d)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mm.nvfp4_grouped_gemm(shapes, abc, sf, len(shapes), side)
+    torch.cuda.synchronize()
+    eager = [c.copy() for c in dev.c_as_numpy(shapes, d)]
+    for c, r in zip(eager, ref):
+        assert not O.tolerance_violations(c, r["c16"], r["s"]).any()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        mm.nvfp4_grouped_gemm(shapes, abc, sf, len(shapes), side)
+    for rep in range(3):
+        for dd in d:
+            dd["c"].fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert dev.guards_intact(d)
+        for a, b in zip(eager, dev.c_as_numpy(shapes, d)):
+            assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), f"replay {rep} differs"
 
 
-def test_streamk_plans_share_library_workspace():
+def test_streamk_plans_share_a_workspace():
     """Stream-K calls with different tile configurations (so different grids
-    and slot sizes) in a row on one stream share the library's workspace: the
+    and slot sizes) in a row on one stream share one caller workspace: the
     slots of one call overlap those of the call before, and each call's
     reduction must read only partials its own main kernel wrote."""
     shapes = [(256, 256, 16384, 1), (40, 136, 64, 1)]
@@ -172,15 +198,15 @@ def test_streamk_plans_share_library_workspace():
     ref = O.grouped_gemm(shapes, poison_padding(shapes, groups))
     for cfg in (0, 3, 1, 0):
         assert mm.nvfp4_launch_geometry(shapes, cus, cfg)["split"] == 1
-        check(shapes, groups, tile_config=cfg, ref=ref, label=f"stream-K cfg {cfg} after others")
+        check(shapes, groups, tile_config=cfg, split_mode=-1, ref=ref, label=f"stream-K cfg {cfg} after others")
 
 
-@pytest.mark.parametrize("split", [None, 0])
+@pytest.mark.parametrize("split", [-1, 0])
 def test_max_k(split):
     """The largest K the library accepts (2^22): fp32 accumulation over 4M
-    products; with the heuristic every workgroup contributes a range of stages
-    to the one tile (stream-K), forced whole tiles run all 32768 stages in one
-    workgroup."""
+    products; with the heuristic and a workspace every workgroup contributes a
+    range of stages to the one tile (stream-K), forced whole tiles run all
+    32768 stages in one workgroup."""
     shapes = [(33, 24, 1 << 22, 1)]
     assert mm.nvfp4_grouped_gemm_validate(shapes, [(16, 16, 16)], [(16, 16)]) == mm.NVFP4_OK
     check(shapes, synth.make_custom(shapes, seed=4242), split_mode=split, label="k = 2^22")
@@ -305,3 +331,64 @@ def test_random_problems(seed):
         for (m, n, k, l), c, r in zip(shapes, dev.c_as_numpy(shapes, d), ref):
             if m and n:
                 assert not O.tolerance_violations(c, r["c16"], r["s"]).any(), (m, n, k, l)
+
+
+STAGE_CASES = [("workload", 1), ("workload", 2), ("workload", 3), ("workload", 4),
+               ("edge", "g8_ragged"), ("edge", "ragged_m_n_k"), ("edge", "batch_l2"),
+               ("edge", "empty_groups_in_middle")]
+
+
+@pytest.mark.parametrize("split", [0, 1])
+@pytest.mark.parametrize("kind,which", STAGE_CASES)
+def test_three_stage_pipeline_is_bitwise_identical(kind, which, split):
+    """The kernels with a three-stage LDS pipeline (each buffer reloaded one
+    stage sooner after its last reads) write exactly what the four-stage ones
+    write, for every tile configuration, whole tiles and stream-K: an LDS
+    buffer overwritten before all its readers are done would differ."""
+    if kind == "workload":
+        shapes, groups = synth.make_workload(which)
+    else:
+        shapes = EDGE_CASES[which]
+        groups = synth.make_custom(shapes, seed=zlib.crc32(which.encode()) % 100000)
+    groups = poison_padding(shapes, groups)
+    d = dev.upload(shapes, groups, c_guard=GUARD)
+    abc, sf = dev.pointer_tables(d)
+    ws = dev.workspace_for(shapes)
+    for cfg in range(mm.nvfp4_num_tile_configs()):
+        outs = []
+        for stages in (4, 3):
+            announce(f"{kind} {which} cfg {cfg} split {split} stages {stages}")
+            for dd in d:
+                dd["c"].fill_(-1)
+            mm.nvfp4_grouped_gemm_stages(shapes, abc, sf, len(shapes), ws.data_ptr(), ws.numel(), cfg, split,
+                                         stages, torch.cuda.current_stream())
+            torch.cuda.synchronize()
+            assert dev.guards_intact(d)
+            outs.append([c.copy() for c in dev.c_as_numpy(shapes, d)])
+        for (m, n, k, l), a, b in zip(shapes, *outs):
+            assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), (cfg, (m, n, k, l))
+
+
+def test_three_stage_pipeline_half_atom_k():
+    """The same check on k % 64 == 32 groups (the padding 16-blocks zeroed in
+    LDS between the loads of a stage and its readers)."""
+    shapes = [(97, 136, 32, 1), (129, 72, 96, 1), (33, 264, 160, 2), (256, 8, 224, 1), (200, 136, 4096 + 96, 1)]
+    groups = poison_padding(shapes, synth.make_custom(shapes, seed=3737))
+    d = dev.upload(shapes, groups, c_guard=GUARD)
+    abc, sf = dev.pointer_tables(d)
+    ws = dev.workspace_for(shapes)
+    ref = O.grouped_gemm(shapes, groups)
+    for cfg in range(mm.nvfp4_num_tile_configs()):
+        for split in (0, 1):
+            outs = []
+            for stages in (4, 3):
+                announce(f"half-atom k cfg {cfg} split {split} stages {stages}")
+                for dd in d:
+                    dd["c"].fill_(-1)
+                mm.nvfp4_grouped_gemm_stages(shapes, abc, sf, len(shapes), ws.data_ptr(), ws.numel(), cfg, split,
+                                             stages, torch.cuda.current_stream())
+                torch.cuda.synchronize()
+                outs.append([c.copy() for c in dev.c_as_numpy(shapes, d)])
+            for a, b, r in zip(*outs, ref):
+                assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), (cfg, split)
+                assert not O.tolerance_violations(b, r["c16"], r["s"]).any()

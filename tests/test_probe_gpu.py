@@ -1,6 +1,7 @@
-"""GPU checks of the measurement kernels behind the mainloop choice
+"""GPU check of the measurement kernels behind the mainloop choice
 (libnvfp4_mainloop_probe.so): what the scaled FP4 conversion does with a
-scale that is not a power of two, and the order of the inner-loop costs."""
+scale that is not a power of two. The inner-loop rates are measurements, not
+correctness properties: ``bench.py --mainloop-probe`` reports them."""
 import sys
 
 import pytest
@@ -27,28 +28,3 @@ def test_scaled_fp4_conversion_applies_only_the_scale_exponent():
     torch.cuda.synchronize()
     got = out.cpu().view(torch.float16).float().tolist()
     assert got == [1.0, 1.0, 1.0, 2.0, 0.5, 256.0, 0.125, 8.0]
-
-
-def test_mainloop_probe_costs():
-    """Per unit of useful MFMA work, the FP4-MFMA-plus-VALU loop (a) is far slower
-    (about 6x) than the f16 dequantisation loop (b), (b) is not clearly faster
-    than the bare f16 MFMA loop, and the bare scaled FP4 loop runs too."""
-    grid = torch.cuda.get_device_properties(0).multi_processor_count
-    sink = torch.empty(grid * probe.SINK_PER_WORKGROUP, dtype=torch.float32, device="cuda")
-    stream = torch.cuda.current_stream()
-    rate = {}
-    for v, iters in ((probe.VARIANT_BARE_F16, 200), (probe.VARIANT_DEQUANT_F16, 200), (probe.VARIANT_FP4_VALU, 50),
-                     (probe.VARIANT_BARE_FP4, 200)):
-        announce(f"nvfp4_probe_mainloop variant {v} iters {iters} grid {grid}")
-        probe.nvfp4_probe_mainloop(v, iters, grid, sink.data_ptr(), stream.cuda_stream)
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        start.record(stream)
-        for _ in range(3):
-            probe.nvfp4_probe_mainloop(v, iters, grid, sink.data_ptr(), stream.cuda_stream)
-        end.record(stream)
-        torch.cuda.synchronize()
-        rate[v] = probe.nvfp4_probe_flops_per_iteration(v) * iters * grid * 3 / (start.elapsed_time(end) / 1e3)
-    assert rate[probe.VARIANT_DEQUANT_F16] > 1.5 * rate[probe.VARIANT_FP4_VALU], rate
-    # measured 3-9% apart on several boxes; the bound leaves room for clock drift between the two timings
-    assert rate[probe.VARIANT_BARE_F16] > 0.8 * rate[probe.VARIANT_DEQUANT_F16], rate
-    assert rate[probe.VARIANT_BARE_FP4] > rate[probe.VARIANT_FP4_VALU], rate
