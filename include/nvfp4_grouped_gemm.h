@@ -65,7 +65,7 @@ extern "C" {
 #define NVFP4_ERR_MISALIGNED (-2) /* a device pointer is not 16-byte aligned */
 #define NVFP4_ERR_HIP (-3)        /* the HIP runtime reported an error; see nvfp4_last_hip_error */
 #define NVFP4_ERR_CONFIG (-4)     /* unknown tile configuration id or split mode */
-#define NVFP4_ERR_WORKSPACE (-5)  /* stream-K requested without a large enough workspace */
+#define NVFP4_ERR_WORKSPACE (-5)  /* stream-K requested without a large enough workspace (or scratch) */
 
 /*
  * nvfp4_grouped_gemm - run the grouped GEMM on `stream`.
@@ -106,6 +106,30 @@ int nvfp4_grouped_gemm(const int32_t* problem_sizes, const uint64_t* ptrs_abc,
 int nvfp4_grouped_gemm_ex(const int32_t* problem_sizes, const uint64_t* ptrs_abc,
                           const uint64_t* ptrs_sfa_sfb, int num_groups, void* workspace,
                           size_t workspace_bytes, int tile_config, int split_mode, void* stream);
+
+/*
+ * nvfp4_grouped_gemm_scratch - as nvfp4_grouped_gemm_ex, for callers that
+ * cannot allocate device memory or pass a workspace (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the
+ * stream-K partials go to a fixed array of NVFP4_SCRATCH_BYTES that the
+ * library's code object holds on each device it runs on (until the process
+ * ends). The call allocates nothing.
+ *   tile_config, split_mode  as nvfp4_grouped_gemm_ex. With split_mode -1 the
+ *                  heuristic considers only stream-K plans whose partials
+ *                  (two fp32 tiles per workgroup) fit NVFP4_SCRATCH_BYTES;
+ *                  split_mode 1 with a plan that needs more returns
+ *                  NVFP4_ERR_WORKSPACE and launches nothing.
+ * Every call on a device shares that device's array: calls that may overlap
+ * in time on one device (other streams, other threads) race and must not be
+ * issued. Nothing in the array needs clearing (a call writes every partial it
+ * reads). The device's array address is looked up once per device, on the
+ * first call with that device current. Returns as nvfp4_grouped_gemm_ex
+ * (NVFP4_ERR_HIP if the lookup fails).
+ */
+#define NVFP4_SCRATCH_BYTES ((size_t)32 << 20)
+int nvfp4_grouped_gemm_scratch(const int32_t* problem_sizes, const uint64_t* ptrs_abc,
+                               const uint64_t* ptrs_sfa_sfb, int num_groups, int tile_config,
+                               int split_mode, void* stream);
 
 /*
  * nvfp4_grouped_gemm_stages - as nvfp4_grouped_gemm_ex with the depth of the

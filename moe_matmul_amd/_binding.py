@@ -18,6 +18,7 @@ NVFP4_ERR_HIP = -3
 NVFP4_ERR_CONFIG = -4
 NVFP4_ERR_WORKSPACE = -5
 NVFP4_MAX_GROUPS = 8
+NVFP4_SCRATCH_BYTES = 32 << 20
 NVFP4_MAX_DEVICE_GROUPS = 512
 
 _lib = None
@@ -54,6 +55,8 @@ def load_library() -> ctypes.CDLL:
                                                  i64p, ip, ip, ctypes.POINTER(ctypes.c_size_t)]),
         "nvfp4_grouped_gemm_ex": (ctypes.c_int, [i32p, u64p, u64p, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
                                                  ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
+        "nvfp4_grouped_gemm_scratch": (ctypes.c_int, [i32p, u64p, u64p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                      ctypes.c_void_p]),
         "nvfp4_grouped_gemm_stages": (ctypes.c_int, [i32p, u64p, u64p, ctypes.c_int, ctypes.c_void_p,
                                                      ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                      ctypes.c_void_p]),
@@ -195,6 +198,20 @@ def nvfp4_grouped_gemm_ex(problem_sizes, ptrs_abc, ptrs_sfa_sfb, num_groups=None
                                    int(tile_config), int(split_mode), _stream(stream))
     if rc != NVFP4_OK:
         raise Nvfp4Error(rc, "nvfp4_grouped_gemm_ex")
+
+
+def nvfp4_grouped_gemm_scratch(problem_sizes, ptrs_abc, ptrs_sfa_sfb, num_groups=None, tile_config=-1,
+                               split_mode=-1, stream=None) -> None:
+    """As nvfp4_grouped_gemm_ex with the library's fixed device scratch array
+    (NVFP4_SCRATCH_BYTES) as the workspace: allocates nothing. Calls that may
+    overlap in time on one device share that array and must not be issued."""
+    lib = load_library()
+    ps, g = _sizes(problem_sizes)
+    abc, sf = _u64(ptrs_abc, 3), _u64(ptrs_sfa_sfb, 2)
+    g = _groups(num_groups, ps, g, ((abc, 3), (sf, 2)))
+    rc = lib.nvfp4_grouped_gemm_scratch(ps, abc, sf, g, int(tile_config), int(split_mode), _stream(stream))
+    if rc != NVFP4_OK:
+        raise Nvfp4Error(rc, "nvfp4_grouped_gemm_scratch")
 
 
 def nvfp4_grouped_gemm_stages(problem_sizes, ptrs_abc, ptrs_sfa_sfb, num_groups=None, workspace=0,

@@ -57,6 +57,9 @@
 
 #include "nvfp4_grouped_gemm.h"
 
+// Stream-K partials of nvfp4_grouped_gemm_scratch (see scratch_address).
+static __device__ __align__(256) uint8_t scratch[NVFP4_SCRATCH_BYTES];
+
 namespace {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -1687,6 +1690,37 @@ Plan cached_plan(const int32_t* ps, int G, int cus, int force_cfg, int force_spl
 
 bool aligned16(uint64_t p) { return (p & 15u) == 0; }
 
+// The stream-K partials of nvfp4_grouped_gemm_scratch, for callers that
+// cannot allocate: a fixed device array (each device that runs the library
+// holds its own copy until the process ends). Kernels take its address as
+// found by hipGetSymbolAddress (the name itself is a host-side stand-in),
+// looked up once per device.
+constexpr size_t kScratchBytes = NVFP4_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0, "scratch size");
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) { t_last_hip_error = (int)e; return NVFP4_ERR_HIP; }
+  if (dev < 0 || dev >= kMaxDevices) return NVFP4_ERR_INVALID;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // this device's copy (the device is current)
+      if (e != hipSuccess || p == nullptr) { t_last_hip_error = (int)e; return NVFP4_ERR_HIP; }
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return NVFP4_OK;
+}
+
 int launch(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, void* stream, const Plan& plan,
            void* workspace, int32_t* mx_status, int stages) {
   const TileConfig& tc = kConfigs[plan.cfg];
@@ -1896,6 +1930,18 @@ int nvfp4_grouped_gemm_stages(const int32_t* ps, const uint64_t* abc, const uint
   return run_call(ps, abc, sf, G, stream, tile_config, split_mode, workspace, workspace_bytes, nullptr, stages);
 }
 
+int nvfp4_grouped_gemm_scratch(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, int tile_config,
+                               int split_mode, void* stream) {
+  // the host checks run first, so a rejected call makes no HIP call at all
+  const int rc = nvfp4_grouped_gemm_validate(ps, abc, sf, G);
+  if (rc != NVFP4_OK) return rc;
+  if (tile_config < -1 || tile_config >= kNumConfigs || split_mode < -1 || split_mode > 1) return NVFP4_ERR_CONFIG;
+  void* ws = nullptr;
+  const int src = scratch_address(&ws);
+  if (src != NVFP4_OK) return src;
+  return run_call(ps, abc, sf, G, stream, tile_config, split_mode, ws, kScratchBytes);
+}
+
 int nvfp4_grouped_gemm_pow2(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, int32_t* d_status,
                             void* workspace, size_t workspace_bytes, int tile_config, int split_mode, void* stream) {
   if (d_status == nullptr) return NVFP4_ERR_INVALID;
@@ -1918,7 +1964,7 @@ const char* nvfp4_error_string(int code) {
     case NVFP4_ERR_MISALIGNED: return "pointer not aligned (16 bytes; 256 for a workspace)";
     case NVFP4_ERR_HIP: return "HIP runtime error (see nvfp4_last_hip_error)";
     case NVFP4_ERR_CONFIG: return "unknown tile configuration or split mode";
-    case NVFP4_ERR_WORKSPACE: return "stream-K requested without a large enough workspace";
+    case NVFP4_ERR_WORKSPACE: return "stream-K requested without a large enough workspace (or scratch)";
     default: return "unknown error code";
   }
 }
