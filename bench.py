@@ -215,12 +215,16 @@ def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None
                 call(i, side)
         g.replay()
         torch.cuda.synchronize()
-        # capture idled the GPU: replays for the settle time before the timed one
+        # capture idled the GPU: a few replays (at least ~30 ms of GPU time, the
+        # power-management transient, but no more than 20 graphs: a thousand
+        # queued replays of a graph of microsecond kernels made the next one
+        # several times slower) before the timed one
         if settle_s > 0:
             t_rep = time.perf_counter()
             g.replay()
             torch.cuda.synchronize()
-            for _ in range(int(settle_s / max(time.perf_counter() - t_rep, 1e-6))):
+            per = max(time.perf_counter() - t_rep, 1e-6)
+            for _ in range(min(20, int(min(settle_s, 0.03) / per) + 1)):
                 g.replay()
             torch.cuda.synchronize()
         ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -355,6 +355,10 @@ struct GemmKernel {
   // Direct loads every wave issues per stage: its A and B rows and one scale
   // atom row (waves past the last atom row load nothing into a 1 KiB dummy).
   static constexpr int L = A_INSTR + B_INSTR + 1;
+  // Stores every wave issues in an unmasked epilogue (one 16-byte store per
+  // lane per run pair of each 32x32 block), all unconditional.
+  static constexpr int S = MB * NB * 2;
+  static_assert((NS - 1) * L + S < 64, "vmcnt range (counted waits across the epilogue's stores)");
   static constexpr int DUMMY_OFF = NS * STAGE_BYTES;
   static constexpr int LDS_BYTES = NS * STAGE_BYTES + 1024;
   static_assert(NS >= 3 && NS <= 4 && LDS_BYTES <= 160 * 1024, "LDS stages");
@@ -764,21 +768,55 @@ struct GemmKernel {
     *w = *w & 0x0000FFFFu;
   }
 
+  // What a segment's mainloop may assume about the vector-memory operations
+  // in flight when it starts (vmcnt counts loads and stores, retired in issue
+  // order): kPendPrologue - only the NS stages the prologue issued; kPendStores
+  // - stages g0 .. g0 + NS - 1, then exactly S epilogue stores (the previous
+  // segment ran at least NS stages, so it issued all of them, and ended in an
+  // unmasked epilogue); kPendUnknown - anything (wait for all).
+  static constexpr int kPendPrologue = 0, kPendStores = 1, kPendUnknown = 2;
+  // Only the 128x128-wave-tile kernels overlap the epilogue's stores with the
+  // next tile: their epilogue is the longest (all compute units write 128 KiB
+  // at once), and in the smaller kernels the extra branch in the loop body
+  // measured slower (256x128 tiles, workload 2: +2%).
+  static constexpr bool kOverlapStores = MB * NB == 16;
+
+  // Wait until stage g0 of a segment has landed, given `pend`.
+  __device__ __forceinline__ static void wait_first_stage(int pend) {
+    if (pend == kPendPrologue) wait_vmem<(NS - 1) * L>();
+    else if (pend == kPendStores) wait_vmem<(NS - 1) * L + S>();
+    else wait_vmem_all();
+  }
+
+  // The mid-stage wait of iteration kt (stage g0 + kt + 1 must have landed).
+  // The stages after it are exactly NS - 2; with kPendStores the epilogue's S
+  // stores sit between them for the first NS - 1 iterations, so they need not
+  // have drained: the next tile's MFMAs run while they do.
+  __device__ __forceinline__ static void wait_next_stage(int pend, int kt) {
+    if constexpr (kOverlapStores) {
+      if (pend == kPendStores && kt < NS - 1) {
+        wait_vmem<(NS - 2) * L + S>();
+        return;
+      }
+    }
+    wait_vmem<(NS - 2) * L>();
+  }
+
   // n stages of one segment, whose first stage is global stage g0. Every
   // iteration issues exactly one stage (L loads per wave), so on entry stages
   // up to g0 + NS - 1 are issued, and at the mid-stage wait of stage g the
-  // stages after g + 1 are exactly NS - 2. With KPAD, global stage kpad_g
-  // (or none, -1) is a tile's last stage with a half-used scale atom in 64-K
-  // group kpad_grp.
+  // stages after g + 1 are exactly NS - 2 (plus the epilogue's stores, see
+  // wait_next_stage). With KPAD, global stage kpad_g (or none, -1) is a
+  // tile's last stage with a half-used scale atom in 64-K group kpad_grp.
   template <int AMB>
   __device__ __forceinline__ void mainloop(f32x16 (&acc)[MB][NB], int n, int g0, Loader& ld, int kpad_g,
-                                           int kpad_grp) const {
+                                           int kpad_grp, int pend) const {
     // split of a stage's L loads over the four steps of a half stage
     constexpr int U1 = (L + 3) / 4, U2 = U1 + (L - U1 + 2) / 3, U3 = U2 + (L - U2 + 1) / 2;
     Raw r0, r1;
     Scales s0, s1;
     Frags f0, f1;
-    wait_vmem_all();  // stage g0 landed (and earlier C or partial stores are done)
+    wait_first_stage(pend);
     if (KPAD && g0 == kpad_g) zero_half_atom((uint32_t)g0 % NS, kpad_grp);
     block_sync();
     read_half<AMB>(r0, (uint32_t)g0 % NS, 0);
@@ -797,7 +835,7 @@ struct GemmKernel {
       // ---- second half: raw data in r1. Stage g+1 must have landed before its
       // first half is read; every wave is done with stage g's buffer here, so
       // stage g + NS can take it.
-      wait_vmem<(NS - 2) * L>();
+      wait_next_stage(pend, kt);
       if (KPAD && g + 1 == kpad_g) zero_half_atom((uint32_t)(g + 1) % NS, kpad_grp);
       block_sync();
       const StageIssue si = prep_issue(ld);
@@ -949,7 +987,7 @@ struct GemmKernel {
   // direct loads; a half stage's raw chunks feed the MFMAs directly.
   template <int AMB>
   __device__ __forceinline__ void mainloop_mx(f32x16 (&acc)[MB][NB], int n, int g0, Loader& ld, int kpad_g,
-                                              int kpad_grp, uint32_t& seen) const {
+                                              int kpad_grp, uint32_t& seen, int pend) const {
     static_assert(NB % 2 == 0, "two block-column parts per pass");
     Raw r0, r1;
     MxOps o0, o1;
@@ -958,7 +996,7 @@ struct GemmKernel {
     // before the wait below; a reload first waited for inside the loop costs
     // a wait for every direct load in flight at each stage.
     asm volatile("" : "+v"(ld.ctx.a_rem), "+v"(ld.ctx.b_rem), "+v"(ld.ctx.sf_rem), "+v"(ld.ctx.kbytes));
-    wait_vmem_all();  // stage g0 landed (and earlier C or partial stores are done)
+    wait_first_stage(pend);
     if (KPAD && g0 == kpad_g) zero_half_atom((uint32_t)g0 % NS, kpad_grp);
     block_sync();
     read_half<AMB>(r0, (uint32_t)g0 % NS, 0);
@@ -969,7 +1007,7 @@ struct GemmKernel {
       read_half<AMB>(r1, (uint32_t)g % NS, 1);
       __builtin_amdgcn_sched_group_barrier(kSchedDSRead, AMB + NB + 1 + (AMB + 1) / 2, 0);
       mx_half<AMB, false>(acc, r0, o0, r1, o1, seen, nullptr);
-      wait_vmem<(NS - 2) * L>();
+      wait_next_stage(pend, kt);
       if (KPAD && g + 1 == kpad_g) zero_half_atom((uint32_t)(g + 1) % NS, kpad_grp);
       block_sync();
       const StageIssue si = prep_issue(ld);
@@ -981,16 +1019,16 @@ struct GemmKernel {
   }
 
   __device__ __forceinline__ void mainloop_rows_mx(f32x16 (&acc)[MB][NB], const TileCtx& t, int n, int g0,
-                                                   Loader& ld, int kpad_g, uint32_t& seen) const {
+                                                   Loader& ld, int kpad_g, uint32_t& seen, int pend) const {
     const int rows = t.M - t.row0;
     const int nb = rows <= 0 ? 0 : (rows + 31) >> 5;
     const int amb = nb <= wm ? 0 : min(MB, (nb - wm + 1) >> 1);
     switch (amb) {
-      case 0: mainloop_mx<0>(acc, n, g0, ld, kpad_g, t.kpad_group, seen); break;
-      case 1: mainloop_mx<(MB >= 1 ? 1 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group, seen); break;
-      case 2: mainloop_mx<(MB >= 2 ? 2 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group, seen); break;
-      case 3: mainloop_mx<(MB >= 3 ? 3 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group, seen); break;
-      default: mainloop_mx<MB>(acc, n, g0, ld, kpad_g, t.kpad_group, seen); break;
+      case 0: mainloop_mx<0>(acc, n, g0, ld, kpad_g, t.kpad_group, seen, pend); break;
+      case 1: mainloop_mx<(MB >= 1 ? 1 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group, seen, pend); break;
+      case 2: mainloop_mx<(MB >= 2 ? 2 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group, seen, pend); break;
+      case 3: mainloop_mx<(MB >= 3 ? 3 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group, seen, pend); break;
+      default: mainloop_mx<MB>(acc, n, g0, ld, kpad_g, t.kpad_group, seen, pend); break;
     }
   }
 
@@ -1006,17 +1044,17 @@ struct GemmKernel {
 
   // Dispatch on this wave's active 32-row blocks (rows below m).
   __device__ __forceinline__ void mainloop_rows(f32x16 (&acc)[MB][NB], const TileCtx& t, int n, int g0,
-                                                Loader& ld, int kpad_g) const {
+                                                Loader& ld, int kpad_g, int pend) const {
     const int rows = t.M - t.row0;
     const int nb = rows <= 0 ? 0 : (rows + 31) >> 5;  // row blocks of the tile below m
     const int amb = nb <= wm ? 0 : min(MB, (nb - wm + 1) >> 1);
     static_assert(MB <= 4, "active-block dispatch covers MB <= 4");
     switch (amb) {
-      case 0: mainloop<0>(acc, n, g0, ld, kpad_g, t.kpad_group); break;
-      case 1: mainloop<(MB >= 1 ? 1 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group); break;
-      case 2: mainloop<(MB >= 2 ? 2 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group); break;
-      case 3: mainloop<(MB >= 3 ? 3 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group); break;
-      default: mainloop<MB>(acc, n, g0, ld, kpad_g, t.kpad_group); break;
+      case 0: mainloop<0>(acc, n, g0, ld, kpad_g, t.kpad_group, pend); break;
+      case 1: mainloop<(MB >= 1 ? 1 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group, pend); break;
+      case 2: mainloop<(MB >= 2 ? 2 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group, pend); break;
+      case 3: mainloop<(MB >= 3 ? 3 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group, pend); break;
+      default: mainloop<MB>(acc, n, g0, ld, kpad_g, t.kpad_group, pend); break;
     }
   }
 
@@ -1031,11 +1069,38 @@ struct GemmKernel {
     return __builtin_bit_cast(uint32_t, v);
   }
 
-  __device__ __forceinline__ void epilogue(const f32x16 (&acc)[MB][NB], const TileCtx& t) const {
+  // 128x128 wave tiles: the accumulators take all 256 AGPRs, and left to
+  // itself the compiler copies every one of them to VGPRs right after the
+  // mainloop, which do not hold them all, and spills; they are kept in AGPRs
+  // (pin_acc) and each element is read where the epilogue needs it. Smaller
+  // wave tiles fit in VGPRs and are left to the compiler.
+  static constexpr bool kAccInAgprs = MB * NB == 16;
+  __device__ __forceinline__ static float acc_read(float x) {
+    if constexpr (!kAccInAgprs) return x;
+    float v;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(x));
+    return v;
+  }
+  __device__ __forceinline__ static void pin_acc(f32x16 (&acc)[MB][NB]) {
+    if constexpr (kAccInAgprs) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) asm volatile("" : "+a"(acc[i][j]));
+    }
+  }
+
+  // Returns true for an unmasked epilogue: every wave then issued exactly S
+  // stores (see kPendStores).
+  __device__ __forceinline__ bool epilogue(const f32x16 (&acc)[MB][NB], const TileCtx& t) const {
     // Tiles wholly inside m and n (all but the edges) store without masks,
     // i.e. without an exec-mask branch around every store.
-    if (t.row0 + BM <= t.M && t.col0 + BN <= t.N) epilogue_impl<false>(acc, t);
-    else epilogue_impl<true>(acc, t);
+    if (t.row0 + BM <= t.M && t.col0 + BN <= t.N) {
+      epilogue_impl<false>(acc, t);
+      return true;
+    }
+    epilogue_impl<true>(acc, t);
+    return false;
   }
 
   template <bool MASKED>
@@ -1047,26 +1112,29 @@ struct GemmKernel {
     int lro = lr, h8 = h * 8;
     asm volatile("" : "+v"(lro), "+v"(h8));
     const int col0 = t.col0 + wn * WN;
-    uint16_t* clane = t.c + (size_t)(t.row0 + lro) * t.N + col0 + h8;
+    // global (not flat) stores: they count in vmcnt only, not in the lgkmcnt
+    // the barriers wait for
+    typedef __attribute__((address_space(1))) uint16_t gu16;
+    gu16* clane = (gu16*)t.c + (size_t)(t.row0 + lro) * t.N + col0 + h8;
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
       const int rb = row_block(wm, i) * 32;
-      uint16_t* crow = clane + (size_t)rb * t.N;
+      gu16* crow = clane + (size_t)rb * t.N;
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
           // runs 2p (kept by lanes h = 0) and 2p + 1 (kept by lanes h = 1)
-          const f32x16& a = acc[i][j];
-          const auto s0 = __builtin_amdgcn_permlane32_swap(pack_f16(a[8 * p + 0], a[8 * p + 1]),
-                                                           pack_f16(a[8 * p + 4], a[8 * p + 5]), false, false);
-          const auto s1 = __builtin_amdgcn_permlane32_swap(pack_f16(a[8 * p + 2], a[8 * p + 3]),
-                                                           pack_f16(a[8 * p + 6], a[8 * p + 7]), false, false);
+          float a[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) a[e] = acc_read(acc[i][j][8 * p + e]);
+          const auto s0 = __builtin_amdgcn_permlane32_swap(pack_f16(a[0], a[1]), pack_f16(a[4], a[5]), false, false);
+          const auto s1 = __builtin_amdgcn_permlane32_swap(pack_f16(a[2], a[3]), pack_f16(a[6], a[7]), false, false);
           const int cu = j * 32 + 2 * p * 8;  // uniform part of the column
           // n % 8 == 0: an 8-column chunk is all in or all out
           if (!MASKED || (lro < t.M - t.row0 - rb && h8 < t.N - col0 - cu)) {
             const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
-            *reinterpret_cast<u32x4*>(crow + cu) = v;
+            *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(crow + cu) = v;
           }
         }
       }
@@ -1121,6 +1189,7 @@ struct GemmKernel {
     first_segment(seg);
     bool first_seg = true;
     int g0 = 0;
+    int pend = kPendPrologue;
     while (seg.valid) {
       const TileCtx t = setup(seg.tile);
       const int n = seg.s1 - seg.s0;
@@ -1134,17 +1203,22 @@ struct GemmKernel {
       const int kpad_g = KPAD && t.kpad_group >= 0 && seg.s1 == t.nk ? g0 + n - 1 : -1;
       if constexpr (MX) {
         uint32_t seen = 0;  // bf16 bits of every scale converted
-        if (n > 0) mainloop_rows_mx(acc, t, n, g0, ld, kpad_g, seen);
+        if (n > 0) mainloop_rows_mx(acc, t, n, g0, ld, kpad_g, seen, pend);
         mx_report(seen);
       } else {
-        if (n > 0) mainloop_rows(acc, t, n, g0, ld, kpad_g);
+        if (n > 0) mainloop_rows(acc, t, n, g0, ld, kpad_g, pend);
       }
+      pin_acc(acc);  // (128x128 wave tiles) in AGPRs until the epilogue reads them
+      bool unmasked = false;
       if constexpr (Src::kCanSplit) {
-        if (seg.s0 == 0 && seg.s1 == t.nk) epilogue(acc, t);
+        if (seg.s0 == 0 && seg.s1 == t.nk) unmasked = epilogue(acc, t);
         else write_partial(acc, first_seg);
       } else {
-        epilogue(acc, t);  // whole tiles only
+        unmasked = epilogue(acc, t);  // whole tiles only
       }
+      // the next segment's first NS stages were all issued by this mainloop,
+      // after any earlier stores, iff it ran at least NS stages
+      pend = (kOverlapStores && unmasked && n >= NS) ? kPendStores : kPendUnknown;
       g0 += n;
       first_seg = false;
       next_segment(seg);
