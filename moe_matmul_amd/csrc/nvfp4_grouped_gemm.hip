@@ -198,6 +198,10 @@ struct TileCtx {
   int32_t sf_rem;
   uint16_t* c;             // C of the tile's batch
   int M, N, kbytes, nk, row0, col0;
+  // Tiles narrower than a 128-row scale atom (64 rows or columns) use half of
+  // it: the word offset (0 or 2) inside each 16-byte atom chunk of their first
+  // row (A: bits 0-3, B: bits 4-7; 0 for tiles of 128 or more).
+  int sub_words;
   // k % 64 == 32: the last 64-K scale atom is half used; its 16-blocks 2 and
   // 3 (bytes 2 and 3 of every 4-byte row word) are padding and may hold
   // anything. kpad_group is the 64-K group of the last stage that holds that
@@ -344,13 +348,20 @@ struct GemmKernel {
   static_assert(WAVES_M == 2, "row-block interleave assumes two wave rows");
   static constexpr int A_BYTES = BM * kRowBytes;
   static constexpr int B_BYTES = BN * kRowBytes;
-  static constexpr int SF_ATOMS = (BM + BN) / 128;
+  // Scale atom rows staged per operand: a 64-row (column) tile stages the
+  // whole 128-row atom it lies in and uses half of it.
+  static constexpr int A_ATOMS = BM >= 128 ? BM / 128 : 1;
+  static constexpr int B_ATOMS = BN >= 128 ? BN / 128 : 1;
+  static constexpr bool kSubAtomA = BM < 128, kSubAtomB = BN < 128;
+  static_assert((BM % 128 == 0 || BM == 64) && (BN % 128 == 0 || BN == 64), "tile shape");
+  static constexpr int SF_ATOMS = A_ATOMS + B_ATOMS;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SF_ATOMS * 1024;
   static constexpr int A_INSTR = A_BYTES / 1024 / 4;  // 1 KiB direct loads per wave per stage
   static constexpr int B_INSTR = B_BYTES / 1024 / 4;
   static constexpr int TILE_FLOATS = BM * BN;
   static_assert((BM / WM) * (BN / WN) == kThreads / 64, "four waves per workgroup");
-  static_assert(WM <= 128 && WN <= 128 && 128 % WM == 0 && 128 % WN == 0, "wave tile inside one scale atom");
+  static_assert(WM <= 128 && WN <= 128 && 128 % WM == 0 && 128 % WN == 0 && WM >= 32 && WN >= 32,
+                "wave tile inside one scale atom");
   static_assert(A_INSTR >= 1 && B_INSTR >= 1 && SF_ATOMS <= 4, "tile shape");
   // Direct loads every wave issues per stage: its A and B rows and one scale
   // atom row (waves past the last atom row load nothing into a 1 KiB dummy).
@@ -383,6 +394,7 @@ struct GemmKernel {
 
   const Src src;
   uint8_t* smem;
+  mutable int sub_words = 0;  // TileCtx::sub_words of the segment being computed
   int wave, wm, wn, h, lr, lane;
   int vwg;  // this workgroup's virtual index
   // Row blocks are interleaved over the two wave rows: 32-row block i of wave
@@ -425,7 +437,7 @@ struct GemmKernel {
       b_base[kk] = A_BYTES + lds_off(wn * WN + lr, kk * 2 + h);
     }
     sa_base = A_BYTES + B_BYTES + lr * 16;
-    sb_base = A_BYTES + B_BYTES + (BM / 128 + ((wn * WN) >> 7)) * 1024 + lr * 16 + (((wn * WN) & 127) >> 5) * 4;
+    sb_base = A_BYTES + B_BYTES + (A_ATOMS + ((wn * WN) >> 7)) * 1024 + lr * 16 + (((wn * WN) & 127) >> 5) * 4;
     sa_sel = (uint32_t)(wm * 4 + 2 * h) | ((uint32_t)(wm * 4 + 2 * h + 1) << 8) | 0x0C0C0000u;
   }
 
@@ -540,15 +552,16 @@ struct GemmKernel {
     t.c = G.c + (size_t)li * M * N;
     t.sf_row = nullptr;
     t.sf_rem = 0;
-    if (wave < BM / 128) {
-      const int atom = tm * (BM / 128) + wave;
+    if (wave < A_ATOMS) {
+      const int atom = (tm * BM >> 7) + wave;
       t.sf_row = G.sfa + ((size_t)li * Mt + atom) * Kt * kAtomBytes;
       t.sf_rem = atom < Mt ? Kt * kAtomBytes : 0;
     } else if (wave < SF_ATOMS) {
-      const int atom = tn * (BN / 128) + (wave - BM / 128);
+      const int atom = (tn * BN >> 7) + (wave - A_ATOMS);
       t.sf_row = G.sfb + ((size_t)li * Nt + atom) * Kt * kAtomBytes;
       t.sf_rem = atom < Nt ? Kt * kAtomBytes : 0;
     }
+    t.sub_words = (kSubAtomA ? ((tm * BM) & 127) >> 5 : 0) | (kSubAtomB ? (((tn * BN) & 127) >> 5) << 4 : 0);
     return t;
   }
 
@@ -672,12 +685,26 @@ struct GemmKernel {
 #pragma unroll
     for (int j = 0; j < NB; ++j)
       r.b[j] = *reinterpret_cast<const u32x4*>(St + b_base[kk] + j * 32 * kRowBytes);
-    const ScaleVec<NB> sb = *reinterpret_cast<const ScaleVec<NB>*>(St + sb_base + kk * 512);
+    const int sbo = kSubAtomB ? 4 * (sub_words >> 4) : 0;
+    const ScaleVec<NB> sb = *reinterpret_cast<const ScaleVec<NB>*>(St + sb_base + kk * 512 + sbo);
 #pragma unroll
     for (int a = 0; a < (AMB + 1) / 2; ++a)
       r.sa[a] = *reinterpret_cast<const u32x4*>(St + sa_base + a * 1024 + kk * 512);
 #pragma unroll
     for (int j = 0; j < NB; ++j) r.sb[j] = sb[j];
+  }
+
+  // The word of the lane's A scale chunk that holds wave block i's scales,
+  // with this lane's two bytes (16-blocks 2h, 2h+1) in the low half: block
+  // b = 2 i + wm sits in word b % 4 of atom b / 4, shifted by the tile's
+  // sub-atom offset for 64-row tiles.
+  __device__ __forceinline__ uint32_t a_scale_word(const Raw& r, int i) const {
+    const u32x4& c = r.sa[i >> 1];
+    if constexpr (kSubAtomA) {
+      const bool upper = (sub_words & 15) != 0;  // rows 64..127 of the atom: words 2 and 3
+      return __builtin_amdgcn_perm(upper ? c[3] : c[1], upper ? c[2] : c[0], sa_sel);
+    }
+    return __builtin_amdgcn_perm(c[2 * (i & 1) + 1], c[2 * (i & 1)], sa_sel);
   }
 
   // The lane's two E4M3 scales (16-blocks 2h, 2h+1 of the half) -> f16, exactly.
@@ -687,8 +714,7 @@ struct GemmKernel {
     const int hshift = h * 16;
 #pragma unroll
     for (int i = 0; i < AMB; ++i) {
-      const u32x4& c = r.sa[i >> 1];
-      const uint32_t w = __builtin_amdgcn_perm(c[2 * (i & 1) + 1], c[2 * (i & 1)], sa_sel);
+      const uint32_t w = a_scale_word(r, i);
       s.a[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
     }
 #pragma unroll
@@ -884,10 +910,7 @@ struct GemmKernel {
   __device__ __forceinline__ void mx_scales(MxScales& s, const Raw& r, uint32_t& seen) const {
     const int hshift = h * 16;
 #pragma unroll
-    for (int i = 0; i < AMB; ++i) {
-      const u32x4& c = r.sa[i >> 1];
-      s.a[i] = e8m0_pair(__builtin_amdgcn_perm(c[2 * (i & 1) + 1], c[2 * (i & 1)], sa_sel), seen);
-    }
+    for (int i = 0; i < AMB; ++i) s.a[i] = e8m0_pair(a_scale_word(r, i), seen);
 #pragma unroll
     for (int j = 0; j < NB; ++j) s.b[j] = e8m0_pair(r.sb[j] >> hshift, seen);
   }
@@ -988,7 +1011,7 @@ struct GemmKernel {
   template <int AMB>
   __device__ __forceinline__ void mainloop_mx(f32x16 (&acc)[MB][NB], int n, int g0, Loader& ld, int kpad_g,
                                               int kpad_grp, uint32_t& seen, int pend) const {
-    static_assert(NB % 2 == 0, "two block-column parts per pass");
+    static_assert(NB % 2 == 0 || NB == 1, "two block-column parts per pass (one: the first part is empty)");
     Raw r0, r1;
     MxOps o0, o1;
     // The loader's sizes are used here, so that any reload of them from the
@@ -1193,6 +1216,7 @@ struct GemmKernel {
     while (seg.valid) {
       const TileCtx t = setup(seg.tile);
       const int n = seg.s1 - seg.s0;
+      sub_words = t.sub_words;
       f32x16 acc[MB][NB];
 #pragma unroll
       for (int i = 0; i < MB; ++i)
@@ -1483,6 +1507,7 @@ const TileConfig kConfigs[] = {
     NVFP4_TILE_CONFIG(128, 256, 64, 128),
     NVFP4_TILE_CONFIG(256, 128, 128, 64),
     NVFP4_TILE_CONFIG(128, 128, 64, 64),
+    NVFP4_TILE_CONFIG(64, 64, 32, 32),
 };
 #undef NVFP4_TILE_CONFIG
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
@@ -1643,7 +1668,11 @@ size_t workspace_bytes_for(int cfg, int grid) {
 double tile_unit(int cfg) {
   const TileConfig& tc = kConfigs[cfg];
   const double size = (double)tc.bm * tc.bn / (128.0 * 128.0);
-  const double eff = 1.0 + 0.35 * ((128.0 / tc.wm + 128.0 / tc.wn) / 2.0 - 1.0);
+  double eff = 1.0 + 0.35 * ((128.0 / tc.wm + 128.0 / tc.wn) / 2.0 - 1.0);
+  // 32x32 wave tiles dequantise 16 VALU per MFMA (64x64: 8): a stage costs
+  // about what the VALU takes, half a 64x64-wave stage for a quarter of the
+  // MFMA work
+  if (tc.wm < 64 && tc.wn < 64) eff = 2.4;
   return size * eff;
 }
 

@@ -175,7 +175,8 @@ def test_tile_configs_and_geometry():
     assert n >= 1
     for c in range(n):
         info = mm.nvfp4_tile_config_info(c)
-        assert info["bm"] % 128 == 0 and info["bn"] % 128 == 0 and info["threads"] == 256
+        # whole 128-row scale atoms, or 64 rows (half of one)
+        assert info["bm"] in (64, 128, 256) and info["bn"] in (64, 128, 256) and info["threads"] == 256
     with pytest.raises(mm.Nvfp4Error):
         mm.nvfp4_tile_config_info(n)
     shapes = synth.workload_shapes(2)
@@ -197,6 +198,10 @@ def test_tile_configs_and_geometry():
         mm.nvfp4_launch_geometry(shapes, 256, 0, 2)
     sel = mm.nvfp4_select_tile_config(synth.workload_shapes(4), 256)
     assert 0 <= sel < n
+    # the two small workloads fill more compute units with 64x64 tiles
+    small = next(c for c in range(n) if (mm.nvfp4_tile_config_info(c)["bm"], mm.nvfp4_tile_config_info(c)["bn"]) == (64, 64))
+    for idx in (0, 1):
+        assert mm.nvfp4_select_tile_config(synth.workload_shapes(idx), 256) == small
 
 
 def test_ex_entry_point_checks_before_any_hip_call():

@@ -59,7 +59,7 @@ def super_batch_shapes(seed, batches=15, per_batch=8):
     return shapes
 
 
-@pytest.mark.parametrize("cfg", [-1, 0, 1, 2, 3])
+@pytest.mark.parametrize("cfg", [-1, 0, 1, 2, 3, 4])
 def test_device_tables_match_oracle_and_host_path(cfg):
     """Small workloads and ragged edge cases: oracle parity, and bitwise
     equality with the by-value entry point (whole tiles, same configuration)."""

@@ -105,7 +105,7 @@ def test_edge_shapes(name):
 
 
 @pytest.mark.parametrize("split", [0, 1])
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
 def test_every_tile_config(cfg, split):
     """Each compiled tile configuration, with whole tiles and with stream-K."""
     if cfg >= mm.nvfp4_num_tile_configs():
@@ -119,7 +119,7 @@ def test_every_tile_config(cfg, split):
 
 
 @pytest.mark.parametrize("split", [0, 1])
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
 def test_half_atom_k(cfg, split):
     """k % 64 == 32: the last 64-K scale atom is half used and its other half
     (poisoned with NaN codes) must not count; the last stage holds 32 or 96
@@ -134,7 +134,7 @@ def test_half_atom_k(cfg, split):
 
 
 @pytest.mark.parametrize("split", [0, 1])
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
 def test_masked_row_blocks(cfg, split):
     """M tails that leave each wave 0 .. 4 active 32-row blocks in both wave rows
     (row blocks alternate between the wave rows; blocks wholly past m are

@@ -68,7 +68,7 @@ EDGE = {
 }
 
 
-@pytest.mark.parametrize("cfg", [-1, 0, 1, 2, 3])
+@pytest.mark.parametrize("cfg", [-1, 0, 1, 2, 3, 4])
 def test_pow2_small_workloads_and_edges(cfg):
     """The two small workloads with power-of-two scales, and ragged, empty,
     k = 0 and l = 2 groups whose scales span every accepted code (zero,
@@ -89,7 +89,7 @@ def test_pow2_small_workloads_and_edges(cfg):
 
 
 @pytest.mark.parametrize("split", [0, 1])
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
 def test_pow2_k_tails(cfg, split):
     """k % 128 = 32, 64 and 96 (the last stage partly past k; for k % 64 == 32
     a half-used scale atom whose padding bytes are poisoned with the E4M3 NaN
