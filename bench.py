@@ -184,7 +184,7 @@ def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None
         call(i)
         evs[i + 1].record(stream)
     torch.cuda.synchronize()
-    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]  # ms
+    per_call = [evs[i].elapsed_time(evs[i + 1]) for i in range(reps)]  # ms
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     if device_tables:
         cfg = tile_config
@@ -223,8 +223,8 @@ def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None
             t_rep = time.perf_counter()
             g.replay()
             torch.cuda.synchronize()
-            per = max(time.perf_counter() - t_rep, 1e-6)
-            for _ in range(min(20, int(min(settle_s, 0.03) / per) + 1)):
+            t_replay = max(time.perf_counter() - t_rep, 1e-6)
+            for _ in range(min(20, int(min(settle_s, 0.03) / t_replay) + 1)):
                 g.replay()
             torch.cuda.synchronize()
         ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -244,7 +244,7 @@ def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None
     return dict(
         workload=name, device_tables=device_tables, pow2=pow2, shapes=[list(s) for s in shapes], flops=flops, bytes=nbytes,
         total_ms=total_ms, wall_s=wall, ms_per_call=total_ms / steps,
-        us_median=percentile(per, 50) * 1e3, us_p10=percentile(per, 10) * 1e3, us_p90=percentile(per, 90) * 1e3,
+        us_median=percentile(per_call, 50) * 1e3, us_p10=percentile(per_call, 10) * 1e3, us_p90=percentile(per_call, 90) * 1e3,
         tflops=flops / avg_s / 1e12, gbs=nbytes / avg_s / 1e9, sets=len(sets), tile_config=geo["config"],
         tiles=geo["total_tiles"], grid=geo["grid"], split=geo["split"], graph_us_per_call=graph_us,
         settle_calls=settle_calls, settle_s=settle_wall, from_idle_ms_per_call=idle_ms,
