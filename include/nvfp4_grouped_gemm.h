@@ -32,10 +32,12 @@
  * counts as lighter - and dealt out one per workgroup per round, alternately
  * forwards and backwards) or stream-K (each workgroup takes
  * an equal share of all (tile, 128-K stage) units and stores the fp32 partial
- * sums of the tiles it shares; a second kernel, on the same stream, adds them
- * in workgroup order, so results do not depend on timing). Stream-K needs a
- * workspace of two fp32 tile-sized slots per workgroup; it holds no state
- * between calls.
+ * sums of the tiles it shares; the last contributor to arrive at a shared tile
+ * adds the partials in workgroup order, so results do not depend on timing,
+ * and no workgroup waits for another). Stream-K needs a workspace of two fp32
+ * tile-sized slots and one counter per workgroup; a small kernel on the same
+ * stream clears the counters first, so the workspace holds no state between
+ * calls.
  *
  * Ownership and threading: the caller owns every buffer, the workspace
  * included; the library allocates no device memory and makes no synchronising

@@ -371,7 +371,8 @@ struct GemmKernel {
   static constexpr int S = MB * NB * 2;
   static_assert((NS - 1) * L + S < 64, "vmcnt range (counted waits across the epilogue's stores)");
   static constexpr int DUMMY_OFF = NS * STAGE_BYTES;
-  static constexpr int LDS_BYTES = NS * STAGE_BYTES + 1024;
+  static constexpr int FLAG_OFF = DUMMY_OFF + 1024;  // stream-K: a tile's arrival count, shared by the waves
+  static constexpr int LDS_BYTES = NS * STAGE_BYTES + 1024 + 16;
   static_assert(NS >= 3 && NS <= 4 && LDS_BYTES <= 160 * 1024, "LDS stages");
   static_assert((NS - 2) * L < 64, "vmcnt range");
 
@@ -1041,12 +1042,16 @@ struct GemmKernel {
     }
   }
 
+  // This wave's 32-row blocks that hold rows below m (0 .. MB).
+  __device__ __forceinline__ int active_blocks(const TileCtx& t) const {
+    const int rows = t.M - t.row0;
+    const int nb = rows <= 0 ? 0 : (rows + 31) >> 5;  // row blocks of the tile below m
+    return nb <= wm ? 0 : min(MB, (nb - wm + 1) >> 1);
+  }
+
   __device__ __forceinline__ void mainloop_rows_mx(f32x16 (&acc)[MB][NB], const TileCtx& t, int n, int g0,
                                                    Loader& ld, int kpad_g, uint32_t& seen, int pend) const {
-    const int rows = t.M - t.row0;
-    const int nb = rows <= 0 ? 0 : (rows + 31) >> 5;
-    const int amb = nb <= wm ? 0 : min(MB, (nb - wm + 1) >> 1);
-    switch (amb) {
+    switch (active_blocks(t)) {
       case 0: mainloop_mx<0>(acc, n, g0, ld, kpad_g, t.kpad_group, seen, pend); break;
       case 1: mainloop_mx<(MB >= 1 ? 1 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group, seen, pend); break;
       case 2: mainloop_mx<(MB >= 2 ? 2 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group, seen, pend); break;
@@ -1068,11 +1073,8 @@ struct GemmKernel {
   // Dispatch on this wave's active 32-row blocks (rows below m).
   __device__ __forceinline__ void mainloop_rows(f32x16 (&acc)[MB][NB], const TileCtx& t, int n, int g0,
                                                 Loader& ld, int kpad_g, int pend) const {
-    const int rows = t.M - t.row0;
-    const int nb = rows <= 0 ? 0 : (rows + 31) >> 5;  // row blocks of the tile below m
-    const int amb = nb <= wm ? 0 : min(MB, (nb - wm + 1) >> 1);
     static_assert(MB <= 4, "active-block dispatch covers MB <= 4");
-    switch (amb) {
+    switch (active_blocks(t)) {
       case 0: mainloop<0>(acc, n, g0, ld, kpad_g, t.kpad_group, pend); break;
       case 1: mainloop<(MB >= 1 ? 1 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group, pend); break;
       case 2: mainloop<(MB >= 2 ? 2 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group, pend); break;
@@ -1165,28 +1167,140 @@ struct GemmKernel {
   }
 
 
-  // Stream-K partials. Workgroup wg owns two fp32 tile-sized slots: slot 0 for
-  // its first segment, slot 1 for its last. Each lane's 16 floats of block
-  // (i, j) are four 16-byte words at
-  // ((((wave * MB + i) * NB + j) * 4 + q) * 64 + lane) * 16 bytes of the slot.
+  // ---------------- stream-K: partials and the fold ----------------
+  // Workgroup wg owns two fp32 tile-sized slots: slot 0 for its first
+  // segment, slot 1 for its last. Each lane's 16 floats of block (i, j) are
+  // four 16-byte words at ((((wave * MB + i) * NB + j) * 4 + q) * 64 + lane) * 16
+  // bytes of the slot; only the wave's active row blocks are written. After
+  // the slots: one int32 arrival counter per workgroup, zero between calls;
+  // a split tile counts on the counter of its first contributor.
   __device__ __forceinline__ static int partial_off(int wave_, int i, int j, int q, int lane_) {
     return ((((wave_ * MB + i) * NB + j) * 4 + q) * 64 + lane_) * 16;
   }
+  // Cache-policy bit SC1 of buffer loads and stores: device scope. Such stores
+  // write through the XCD's L2, and such loads read what device-scope stores
+  // wrote, from any XCD (the L2s of the XCDs are not coherent with each other).
+  static constexpr int kDeviceScope = 16;
 
-  // This workgroup computed stages [s0, s1) of a tile, not all of it: store the
-  // fp32 partial sum; the reduction kernel adds the partials up.
-  __device__ __forceinline__ void write_partial(const f32x16 (&acc)[MB][NB], bool first_seg) const {
-    uint8_t* slot = reinterpret_cast<uint8_t*>(src.args.partials) +
-                    ((size_t)vwg * 2 + (first_seg ? 0 : 1)) * TILE_FLOATS * 4;
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(int wg, int slot) const {
+    uint8_t* p = reinterpret_cast<uint8_t*>(src.args.partials) + ((size_t)wg * 2 + slot) * (TILE_FLOATS * 4);
+    return __builtin_amdgcn_make_buffer_rsrc(p, 0, TILE_FLOATS * 4, kBufferWord3);
+  }
+  __device__ __forceinline__ int32_t* arrivals(int wg) const {
+    uint8_t* p = reinterpret_cast<uint8_t*>(src.args.partials) + (size_t)src.args.grid * 2 * (TILE_FLOATS * 4);
+    return reinterpret_cast<int32_t*>(p) + wg;
+  }
+
+  // This workgroup computed stages [s0, s1) of a tile, not all of it. It
+  // stores its partial sum with device-scope stores and waits until they have
+  // completed; then one thread adds one to the tile's arrival counter
+  // (device-scope atomic). The contributor that brings the count to the
+  // number of contributors folds: it adds every partial in contributor
+  // order, which is K order (its own from registers), rounds to fp16 and
+  // stores C, then clears the counter. No workgroup waits for another.
+  // Returns true when this workgroup stored the tile's C.
+  __device__ bool publish_partial(const f32x16 (&acc)[MB][NB], const TileCtx& t, const Segment& seg,
+                                  bool first_seg) const {
+    const int amb = active_blocks(t);
+    const __amdgpu_buffer_rsrc_t mine = slot_rsrc(vwg, first_seg ? 0 : 1);
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
+    for (int i = 0; i < MB; ++i) {
+      if (i >= amb) break;
 #pragma unroll
       for (int j = 0; j < NB; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const f32x4 v = {acc[i][j][4 * q + 0], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          *reinterpret_cast<f32x4*>(slot + partial_off(wave, i, j, q, lane)) = v;
+          const u32x4 v = {__builtin_bit_cast(uint32_t, acc_read(acc[i][j][4 * q + 0])),
+                           __builtin_bit_cast(uint32_t, acc_read(acc[i][j][4 * q + 1])),
+                           __builtin_bit_cast(uint32_t, acc_read(acc[i][j][4 * q + 2])),
+                           __builtin_bit_cast(uint32_t, acc_read(acc[i][j][4 * q + 3]))};
+          __builtin_amdgcn_raw_buffer_store_b128(v, mine, partial_off(wave, i, j, q, lane), 0, kDeviceScope);
         }
+    }
+    wait_vmem_all();  // this wave's partial is visible at device scope
+    const int64_t u_first = seg.u - seg.s0;  // the tile's first unit
+    const int c_first = owner_of_unit(u_first);
+    const int c_last = owner_of_unit(u_first + t.nk - 1);
+    int32_t* count = reinterpret_cast<int32_t*>(smem + FLAG_OFF);
+    block_sync();  // every wave's partial is
+    if (threadIdx.x == 0)
+      *count = __hip_atomic_fetch_add(arrivals(c_first), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    block_sync();
+    if (__builtin_amdgcn_readfirstlane(*count) != c_last - c_first) return false;
+    if (t.row0 + BM <= t.M && t.col0 + BN <= t.N) fold<false>(acc, t, amb, u_first, c_first, c_last);
+    else fold<true>(acc, t, amb, u_first, c_first, c_last);
+    if (threadIdx.x == 0) __hip_atomic_store(arrivals(c_first), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+  }
+
+  // The sum of all contributors' partials of the tile whose first unit is
+  // u_first, row block by row block: for each contributor in order, the
+  // block row's NB blocks are loaded at once (device-scope loads), then
+  // added. Contributor c stored the tile in slot 0 if its range starts inside
+  // the tile, else (the first contributor, whose range starts before it) in
+  // slot 1.
+  template <bool MASKED>
+  __device__ __forceinline__ void fold(const f32x16 (&acc)[MB][NB], const TileCtx& t, int amb, int64_t u_first,
+                                       int c_first, int c_last) const {
+    int lro = lr, h8 = h * 8;
+    asm volatile("" : "+v"(lro), "+v"(h8));
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      if (i >= amb) break;
+      f32x16 sum[NB];
+      for (int c = c_first; c <= c_last; ++c) {
+        f32x16 x[NB];
+        if (c == vwg) {
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) x[j][e] = acc_read(acc[i][j][e]);
+        } else {
+          const __amdgpu_buffer_rsrc_t r = slot_rsrc(c, unit_begin(c) >= u_first ? 0 : 1);
+#pragma unroll
+          for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              // (cast straight to floats: element reads of an unsigned vector
+              // cast of this builtin's result load one dword and copy it to
+              // all four elements with this compiler)
+              const f32x4 v = __builtin_bit_cast(
+                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, partial_off(wave, i, j, q, lane), 0, kDeviceScope));
+#pragma unroll
+              for (int e = 0; e < 4; ++e) x[j][4 * q + e] = v[e];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) sum[j] = c == c_first ? x[j] : sum[j] + x[j];
+      }
+      store_row_block<MASKED>(sum, t, i, lro, h8);
+    }
+  }
+
+  // C stores of this wave's row block i from the lane's 16 floats per block
+  // (the layout of the accumulators), as in epilogue_impl.
+  template <bool MASKED>
+  __device__ __forceinline__ void store_row_block(const f32x16 (&v)[NB], const TileCtx& t, int i, int lro,
+                                                  int h8) const {
+    const int col0 = t.col0 + wn * WN;
+    typedef __attribute__((address_space(1))) uint16_t gu16;
+    const int rb = row_block(wm, i) * 32;
+    gu16* crow = (gu16*)t.c + (size_t)(t.row0 + rb + lro) * t.N + col0 + h8;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const f32x16& a = v[j];
+        const auto s0 = __builtin_amdgcn_permlane32_swap(pack_f16(a[8 * p + 0], a[8 * p + 1]),
+                                                         pack_f16(a[8 * p + 4], a[8 * p + 5]), false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(pack_f16(a[8 * p + 2], a[8 * p + 3]),
+                                                         pack_f16(a[8 * p + 6], a[8 * p + 7]), false, false);
+        const int cu = j * 32 + 2 * p * 8;
+        if (!MASKED || (lro < t.M - t.row0 - rb && h8 < t.N - col0 - cu)) {
+          const u32x4 w = {s0[0], s1[0], s0[1], s1[1]};
+          *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(crow + cu) = w;
+        }
+      }
   }
 
   // Stream-K leaves the tiles of k = 0 groups (no units) to a strided pass.
@@ -1236,7 +1350,7 @@ struct GemmKernel {
       bool unmasked = false;
       if constexpr (Src::kCanSplit) {
         if (seg.s0 == 0 && seg.s1 == t.nk) unmasked = epilogue(acc, t);
-        else write_partial(acc, first_seg);
+        else publish_partial(acc, t, seg, first_seg);
       } else {
         unmasked = epilogue(acc, t);  // whole tiles only
       }
@@ -1400,78 +1514,11 @@ __global__ __launch_bounds__(kThreads, 1) void nvfp4_grouped_gemm_device_kernel(
   k.run();
 }
 
-// Stream-K reduction. Every split tile contains the start of some workgroup's
-// unit range; the first such boundary inside the tile (workgroup c_first + 1)
-// names it. Workgroup (boundary b, chunk x) reduces 16 KiB of the partial
-// layout of that tile: the partials of its contributors are added in
-// contributor order (so the result does not depend on timing), converted to
-// fp16 (RNE) and stored, masked to m and n. Loads of up to four contributors
-// are in flight before they are folded.
-constexpr int kReduceWordsPerThread = 4;
-constexpr int kReduceChunkWords = kThreads * kReduceWordsPerThread;
-
-template <int BM, int BN, int WM, int WN, int NS>
-__global__ __launch_bounds__(kThreads) void nvfp4_streamk_reduce_kernel(KernelArgs) {
-  using K = GemmKernel<BM, BN, WM, WN, NS, KernargSrc>;
-  constexpr int WORDS = K::TILE_FLOATS / 4;
-  constexpr int CHUNKS = WORDS / kReduceChunkWords;
-  static_assert(WORDS % kReduceChunkWords == 0, "chunking");
-  const KernelArgs& args = kernel_args();
-  const K k(KernargSrc{args}, nullptr);
-  const int boundary = 1 + (int)(blockIdx.x / CHUNKS);  // workgroup whose range starts inside the tile
-  const int chunk = (int)(blockIdx.x % CHUNKS);
-  const int64_t ub = k.unit_begin(boundary);
-  int stage;
-  const int tile = k.tile_of_unit(ub, &stage);
-  if (stage == 0) return;  // the boundary falls between tiles: nothing split here
-  const int64_t u_first = ub - stage;
-  const int nk = args.cls[k.class_of_tile(tile)].nk;
-  const int c_first = k.owner_of_unit(u_first);
-  const int c_last = k.owner_of_unit(u_first + nk - 1);
-  if (boundary != c_first + 1) return;  // another boundary of this tile does the work
-  const TileCtx t = k.setup(tile);
-  const uint8_t* parts = reinterpret_cast<const uint8_t*>(args.partials);
-  f32x4 sum[kReduceWordsPerThread];
-  for (int c0 = c_first; c0 <= c_last; c0 += 4) {
-    f32x4 v[4][kReduceWordsPerThread];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const int c = c0 + d;
-      if (c > c_last) break;
-      const int slot = k.tile_of_unit(k.unit_begin(c), &stage) == tile ? 0 : 1;
-      const uint8_t* base = parts + ((size_t)c * 2 + slot) * K::TILE_FLOATS * 4;
-#pragma unroll
-      for (int x = 0; x < kReduceWordsPerThread; ++x) {
-        const int w = chunk * kReduceChunkWords + x * kThreads + (int)threadIdx.x;
-        v[d][x] = *reinterpret_cast<const f32x4*>(base + (size_t)w * 16);
-      }
-    }
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      if (c0 + d > c_last) break;
-#pragma unroll
-      for (int x = 0; x < kReduceWordsPerThread; ++x) sum[x] = (c0 + d == c_first) ? v[d][x] : sum[x] + v[d][x];
-    }
-  }
-#pragma unroll
-  for (int x = 0; x < kReduceWordsPerThread; ++x) {
-    const int w = chunk * kReduceChunkWords + x * kThreads + (int)threadIdx.x;
-    // word w of the layout belongs to (wave, i, j, q, lane)
-    const int ln = w & 63;
-    int rest = w >> 6;
-    const int q = rest & 3;
-    rest >>= 2;
-    const int j = rest % K::NB;
-    rest /= K::NB;
-    const int i = rest % K::MB;
-    const int wv = rest / K::MB;
-    const int row = t.row0 + K::row_block(wv / K::WAVES_N, i) * 32 + (ln & 31);
-    const int col = t.col0 + (wv % K::WAVES_N) * WN + j * 32 + q * 8 + (ln >> 5) * 4;
-    if (row < t.M && col < t.N) {
-      const f16x4 o = {(_Float16)sum[x][0], (_Float16)sum[x][1], (_Float16)sum[x][2], (_Float16)sum[x][3]};
-      *reinterpret_cast<f16x4*>(t.c + (size_t)row * t.N + col) = o;
-    }
-  }
+// Clears the stream-K arrival counters (one int32 per workgroup) before a
+// split launch: a kernel rather than a memset, so that a captured graph
+// replays it correctly. The fold also leaves them zero.
+__global__ __launch_bounds__(kThreads) void nvfp4_clear_arrivals_kernel(int32_t* p, int n) {
+  for (int i = (int)threadIdx.x; i < n; i += kThreads) p[i] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -1484,7 +1531,6 @@ struct TileConfig {
   void (*kernel_kpad)(KernelArgs);  // some group with k % 64 == 32
   void (*kernel_mx)(KernelArgs);    // power-of-two scales
   void (*kernel_mx_kpad)(KernelArgs);
-  void (*reduce)(KernelArgs);
   void (*device_kernel)(DeviceGroupArgs);
   int64_t (*device_tiles)(const int32_t*, const uint64_t*);  // the device kernel's per-group check
   // The same computation with a three-stage LDS pipeline (any k), for
@@ -1500,7 +1546,7 @@ constexpr int kStages = 4;  // LDS pipeline depth (4 x 36 KiB for 256x256 tiles)
     nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, kStages, true>,                                  \
     nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, kStages, false, true>,                           \
     nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, kStages, true, true>,                            \
-    nvfp4_streamk_reduce_kernel<bm, bn, wm, wn, kStages>, nvfp4_grouped_gemm_device_kernel<bm, bn, wm, wn, kStages>, \
+    nvfp4_grouped_gemm_device_kernel<bm, bn, wm, wn, kStages>,                                  \
     device_group_tiles<bm, bn>, nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, 3, true> }
 const TileConfig kConfigs[] = {
     NVFP4_TILE_CONFIG(256, 256, 128, 128),
@@ -1657,13 +1703,16 @@ int build_classes(const int32_t* ps, int G, int cfg, WorkClass* out) {
   return n;
 }
 
+// Stream-K workspace: two fp32 tile slots per workgroup, then one int32
+// arrival counter per workgroup (padded to 256 bytes).
+size_t partial_bytes_for(int cfg, int grid) { return (size_t)grid * 2 * kConfigs[cfg].bm * kConfigs[cfg].bn * 4; }
 size_t workspace_bytes_for(int cfg, int grid) {
-  return (size_t)grid * 2 * kConfigs[cfg].bm * kConfigs[cfg].bn * 4;
+  return partial_bytes_for(cfg, grid) + ((size_t)grid * 4 + 255) / 256 * 256;
 }
 
 // Cost model, in units of one 128x128 tile-stage of MFMA work. Smaller wave
 // tiles dequantise more per MFMA; a tile costs a fixed prologue/epilogue on top
-// of its stages; a stream-K plan adds its partial stores and the reduction
+// of its stages; a stream-K plan adds its partial stores and the fold
 // kernel (plan_for).
 double tile_unit(int cfg) {
   const TileConfig& tc = kConfigs[cfg];
@@ -1715,16 +1764,15 @@ Plan plan_for(const int32_t* ps, int G, int cus, int cfg, int split) {
     const int nc = build_classes(ps, G, cfg, cls);
     static thread_local int32_t ranges[kMaxSplitGrid + 1];
     const double per = split_ranges(cls, nc, p.grid, ranges);
-    // Each workgroup stores up to two fp32 partial tiles, and the reduction
-    // kernel reads them back and writes C: both scale with the tile area
-    // (measured: ~25 us for 255 split 256x256 tiles on 256 CUs, ~15 us for
-    // 128x256), on top of the second launch's fixed latency (~12 us on tiny
-    // problems), in 128x128-stage units of about 0.8 us.
+    // Each workgroup stores up to two fp32 partial tiles (device-scope
+    // stores, then a wait for them) and folds about one split tile (loads
+    // the other contributors' partials); a one-workgroup kernel clears the
+    // arrival counters first. Both scale with the tile area, in 128x128
+    // tile-stage units (about 0.8 us).
     const TileConfig& tc = kConfigs[cfg];
     const double area = (double)tc.bm * tc.bn / 65536.0;
-    const double partials = 6.0 * area;   // the main kernel's partial stores
-    const double reduce_kernel = 15.0 + 30.0 * area * (p.grid - 1) / 255.0;
-    p.cost = unit * per + partials + reduce_kernel;
+    const double publish = 4.0 * area, fold = 4.0 * area, clear = 2.0;
+    p.cost = unit * per + publish + fold + clear;
     p.ws_bytes = workspace_bytes_for(cfg, p.grid);
   }
   return p;
@@ -1871,13 +1919,15 @@ int launch(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, vo
   for (int g = 0; g < G; ++g) kpad = kpad || (ps[4 * g + 2] % 64 != 0);
   void (*kernel)(KernelArgs) = mx_status ? (kpad ? tc.kernel_mx_kpad : tc.kernel_mx) : (kpad ? tc.kernel_kpad : tc.kernel);
   if (stages == 3) kernel = tc.kernel_ns3;
-  hipLaunchKernelGGL(kernel, dim3(plan.grid), dim3(kThreads), 0, st, args);
-  hipError_t e = hipGetLastError();
-  if (e == hipSuccess && plan.split && plan.grid > 1) {
-    const int chunks = tc.bm * tc.bn / 4 / kReduceChunkWords;
-    hipLaunchKernelGGL(tc.reduce, dim3((unsigned)(plan.grid - 1) * chunks), dim3(kThreads), 0, st, args);
-    e = hipGetLastError();
+  if (plan.split) {
+    int32_t* counters = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) +
+                                                   partial_bytes_for(plan.cfg, plan.grid));
+    hipLaunchKernelGGL(nvfp4_clear_arrivals_kernel, dim3(1), dim3(kThreads), 0, st, counters, plan.grid);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) { t_last_hip_error = (int)e; return NVFP4_ERR_HIP; }
   }
+  hipLaunchKernelGGL(kernel, dim3(plan.grid), dim3(kThreads), 0, st, args);
+  const hipError_t e = hipGetLastError();
   if (e != hipSuccess) { t_last_hip_error = (int)e; return NVFP4_ERR_HIP; }
   return NVFP4_OK;
 }

@@ -189,7 +189,9 @@ def test_tile_configs_and_geometry():
         assert geo["split"] == 0 and geo["workspace_bytes"] == 0
         geo = mm.nvfp4_launch_geometry(shapes, 256, c, 1)
         assert geo["split"] == 1 and geo["grid"] == min(units, 256)
-        assert geo["workspace_bytes"] == geo["grid"] * 2 * info["bm"] * info["bn"] * 4
+        # two fp32 tile slots and one int32 arrival counter per workgroup (counters padded to 256 bytes)
+        counters = -(-geo["grid"] * 4 // 256) * 256
+        assert geo["workspace_bytes"] == geo["grid"] * 2 * info["bm"] * info["bn"] * 4 + counters
         assert mm.nvfp4_workspace_bytes(shapes, 256) >= geo["workspace_bytes"]
     # empty groups own no tiles, wherever they sit
     geo = mm.nvfp4_launch_geometry([(0, 128, 64, 1), (128, 128, 64, 1), (128, 0, 64, 1)], 256, 0, 0)

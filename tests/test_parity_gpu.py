@@ -191,7 +191,7 @@ def test_streamk_plans_share_a_workspace():
     """Stream-K calls with different tile configurations (so different grids
     and slot sizes) in a row on one stream share one caller workspace: the
     slots of one call overlap those of the call before, and each call's
-    reduction must read only partials its own main kernel wrote."""
+    fold must read only partials its own workgroups wrote."""
     shapes = [(256, 256, 16384, 1), (40, 136, 64, 1)]
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     groups = synth.make_custom(shapes, seed=21)
@@ -199,6 +199,31 @@ def test_streamk_plans_share_a_workspace():
     for cfg in (0, 3, 1, 0):
         assert mm.nvfp4_launch_geometry(shapes, cus, cfg)["split"] == 1
         check(shapes, groups, tile_config=cfg, split_mode=-1, ref=ref, label=f"stream-K cfg {cfg} after others")
+
+
+@pytest.mark.parametrize("cfg", [0, 2])
+def test_streamk_workspace_reuse_across_inputs(cfg):
+    """One workspace, filled with 0xFF bytes first, serves stream-K calls on
+    two different inputs in turn. The counters start from whatever the
+    workspace held (the clear kernel zeroes them), and each call must fold
+    only partials that its own workgroups stored in that call: a partial left
+    by the call before carries the other input's values."""
+    shapes = [(300, 1024, 2048, 1), (77, 512, 4096, 1), (512, 256, 1024, 2)]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert mm.nvfp4_launch_geometry(shapes, cus, cfg, 1)["split"] == 1
+    inputs = [poison_padding(shapes, synth.make_custom(shapes, seed=s)) for s in (901, 902)]
+    refs = [O.grouped_gemm(shapes, g) for g in inputs]
+    devs = [dev.upload(shapes, g) for g in inputs]
+    ws = dev.workspace_for(shapes)
+    ws.fill_(0xFF)
+    for rep, x in enumerate((0, 1, 0, 1, 1, 0)):
+        announce(f"stream-K workspace reuse cfg {cfg} call {rep} input {x}")
+        for dd in devs[x]:
+            dd["c"].fill_(-1)
+        dev.run(shapes, devs[x], tile_config=cfg, split_mode=1, workspace=ws)
+        torch.cuda.synchronize()
+        for c, r in zip(dev.c_as_numpy(shapes, devs[x]), refs[x]):
+            assert not O.tolerance_violations(c, r["c16"], r["s"]).any(), f"call {rep} (input {x})"
 
 
 @pytest.mark.parametrize("split", [-1, 0])
@@ -271,7 +296,7 @@ def test_graph_replay_matches_eager(idx, split):
     """A call captured in a HIP graph and replayed several times, with eager
     work and synchronisation between the replays, writes exactly what the
     eager call writes. Whole tiles, and stream-K with a caller workspace (each
-    replay's reduction reads the partials of the same replay)."""
+    replay's fold reads the partials of the same replay)."""
     shapes, groups = synth.make_workload(idx)
     announce(f"graph replay workload {idx} split {split}")
     d = dev.upload(shapes, groups)
