@@ -32,12 +32,13 @@
  * counts as lighter - and dealt out one per workgroup per round, alternately
  * forwards and backwards) or stream-K (each workgroup takes
  * an equal share of all (tile, 128-K stage) units and stores the fp32 partial
- * sums of the tiles it shares; the last contributor to arrive at a shared tile
- * adds the partials in workgroup order, so results do not depend on timing,
+ * sums of the tiles it shares; the contributors of a shared tile add their
+ * partials pairwise along a fixed binary tree, each node's sum formed by the
+ * second of its two children to arrive, so results do not depend on timing,
  * and no workgroup waits for another). Stream-K needs a workspace of two fp32
- * tile-sized slots and one counter per workgroup; a small kernel on the same
- * stream clears the counters first, so the workspace holds no state between
- * calls.
+ * tile-sized slots and 80 bytes of counters per workgroup; a small kernel on
+ * the same stream clears the counters first, so the workspace holds no state
+ * between calls.
  *
  * Ownership and threading: the caller owns every buffer, the workspace
  * included; the library allocates no device memory and makes no synchronising
@@ -117,18 +118,19 @@ int nvfp4_grouped_gemm_ex(const int32_t* problem_sizes, const uint64_t* ptrs_abc
  * library's code object holds on each device it runs on (until the process
  * ends). The call allocates nothing.
  *   tile_config, split_mode  as nvfp4_grouped_gemm_ex. With split_mode -1 the
- *                  heuristic considers only stream-K plans whose partials
- *                  (two fp32 tiles per workgroup) fit NVFP4_SCRATCH_BYTES;
+ *                  heuristic considers only stream-K plans whose workspace
+ *                  (two fp32 tiles and 80 bytes of counters per workgroup)
+ *                  fits NVFP4_SCRATCH_BYTES (32 MiB of partials plus 64 KiB);
  *                  split_mode 1 with a plan that needs more returns
  *                  NVFP4_ERR_WORKSPACE and launches nothing.
  * Every call on a device shares that device's array: calls that may overlap
  * in time on one device (other streams, other threads) race and must not be
  * issued. Nothing in the array needs clearing (a call writes every partial it
- * reads). The device's array address is looked up once per device, on the
+ * reads, and clears its counters first). The device's array address is looked up once per device, on the
  * first call with that device current. Returns as nvfp4_grouped_gemm_ex
  * (NVFP4_ERR_HIP if the lookup fails).
  */
-#define NVFP4_SCRATCH_BYTES ((size_t)32 << 20)
+#define NVFP4_SCRATCH_BYTES (((size_t)32 << 20) + 65536)
 int nvfp4_grouped_gemm_scratch(const int32_t* problem_sizes, const uint64_t* ptrs_abc,
                                const uint64_t* ptrs_sfa_sfb, int num_groups, int tile_config,
                                int split_mode, void* stream);
@@ -228,6 +230,20 @@ int nvfp4_grouped_gemm_pow2(const int32_t* problem_sizes, const uint64_t* ptrs_a
  * an argument is NULL or tile_config unknown).
  */
 int64_t nvfp4_device_group_tiles(const int32_t* size, const uint64_t* ptrs, int tile_config);
+
+/*
+ * nvfp4_split_plan - how a stream-K call (split mode 1, configuration `cfg`,
+ * -1 = heuristic) on `num_cus` compute units divides the work (host only, no
+ * HIP call). Tiles are numbered class by class, heaviest first (a group's
+ * last tile row, mostly past m, forms a lighter class), and (tile, 128-K
+ * stage) units tile by tile. The first *whole_tiles tiles (whole rounds of
+ * one tile per workgroup) are dealt out whole; workgroup w (in XCD-major
+ * order) then takes units [unit_ranges[w], unit_ranges[w + 1]) of the rest, a
+ * range that may be empty. unit_ranges needs max_ranges >= grid + 1 entries
+ * (else only *whole_tiles is written). Returns the grid size, or an error.
+ */
+int nvfp4_split_plan(const int32_t* problem_sizes, int num_groups, int num_cus, int cfg, int32_t* whole_tiles,
+                     int32_t* unit_ranges, int max_ranges);
 
 /*
  * nvfp4_workspace_bytes - workspace that covers every plan the library may

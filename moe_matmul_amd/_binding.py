@@ -18,7 +18,7 @@ NVFP4_ERR_HIP = -3
 NVFP4_ERR_CONFIG = -4
 NVFP4_ERR_WORKSPACE = -5
 NVFP4_MAX_GROUPS = 8
-NVFP4_SCRATCH_BYTES = 32 << 20
+NVFP4_SCRATCH_BYTES = (32 << 20) + 65536
 NVFP4_MAX_DEVICE_GROUPS = 512
 
 _lib = None
@@ -66,6 +66,7 @@ def load_library() -> ctypes.CDLL:
                                                      ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]),
         "nvfp4_device_group_tiles": (ctypes.c_int64, [i32p, u64p, ctypes.c_int]),
         "nvfp4_workspace_bytes": (ctypes.c_size_t, [i32p, ctypes.c_int, ctypes.c_int]),
+        "nvfp4_split_plan": (ctypes.c_int, [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, i32p, i32p, ctypes.c_int]),
         "nvfp4_sf_bytes": (ctypes.c_size_t, [ctypes.c_int, ctypes.c_int, ctypes.c_int]),
         "nvfp4_last_hip_error": (ctypes.c_int, []),
         "nvfp4_error_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -269,6 +270,20 @@ def nvfp4_device_group_tiles(size, ptrs, tile_config=-1) -> int:
 def nvfp4_workspace_bytes(problem_sizes, num_cus: int, num_groups=None) -> int:
     ps, g = _sizes(problem_sizes)
     return int(load_library().nvfp4_workspace_bytes(ps, _groups(num_groups, ps, g), int(num_cus)))
+
+
+def nvfp4_split_plan(problem_sizes, num_cus: int, cfg: int = -1, num_groups=None):
+    """How a stream-K call divides the work: (whole_tiles, unit_ranges), the
+    tiles dealt out whole first and each workgroup's range of the other
+    tiles' (tile, stage) units (unit_ranges[w] .. unit_ranges[w + 1])."""
+    ps, g = _sizes(problem_sizes)
+    g = _groups(num_groups, ps, g)
+    whole = ctypes.c_int32()
+    ranges = (ctypes.c_int32 * 1025)()
+    rc = load_library().nvfp4_split_plan(ps, g, int(num_cus), int(cfg), ctypes.byref(whole), ranges, 1025)
+    if rc < 0:
+        raise Nvfp4Error(rc, "nvfp4_split_plan")
+    return whole.value, list(ranges[: rc + 1])
 
 
 def nvfp4_sf_bytes(rows: int, k: int, l: int = 1) -> int:

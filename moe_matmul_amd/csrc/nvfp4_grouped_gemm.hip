@@ -86,6 +86,9 @@ constexpr int kRasterWidth = 8;           // n-tiles per raster super-column
 // first, so that the whole-tile walk below hands out big tiles first.
 constexpr int kMaxClasses = 2 * kMaxGroups;
 constexpr int kMaxSplitGrid = 512;  // stream-K workgroups (unit ranges passed by value)
+// stream-K fold tree levels (contributors of one tile <= kMaxSplitGrid = 2^(kFoldLevels - 1))
+constexpr int kFoldLevels = 10;
+static_assert(kMaxSplitGrid <= (1 << (kFoldLevels - 1)), "fold tree depth");
 
 struct ClassArgs {
   const uint8_t* a;  // the group's tensors and sizes
@@ -106,10 +109,14 @@ struct KernelArgs {
   int32_t num_classes;
   int32_t split;        // 0: whole tiles strided over the grid; 1: stream-K over units
   int32_t grid;         // workgroups of the main kernel
+  // split: tiles [0, whole_tiles) - whole rounds of `grid` tiles - are dealt
+  // out whole first (as without split), the units of the rest by range
+  int32_t whole_tiles;
   float* partials;      // split: two fp32 tile-sized slots per workgroup
-  // split: workgroup w takes units [wg_unit[w], wg_unit[w + 1]), every range
-  // non-empty; the host sizes the ranges to equal modelled cost, since a stage
-  // of a tile that is mostly past m costs less than a full one.
+  // split: workgroup w takes units [wg_unit[w], wg_unit[w + 1]) of the tiles
+  // from whole_tiles on (a range may be empty); the host sizes the ranges so
+  // that every workgroup's modelled cost, its whole tiles included, comes out
+  // equal (a stage of a tile that is mostly past m costs less than a full one).
   int32_t wg_unit[kMaxSplitGrid + 1];
   // power-of-two-scale kernels: set to 1 when a used scale is not zero or a
   // positive power of two
@@ -214,6 +221,7 @@ struct Segment {
   int tile, s0, s1;
   int64_t u;  // stream-K: first work unit of the segment; whole tiles: the round
   bool valid;
+  bool sk;    // a stream-K segment (of a unit range)
 };
 
 __device__ __forceinline__ int search_prefix(const int32_t* prefix, int count, int64_t x) {
@@ -226,13 +234,15 @@ __device__ __forceinline__ int search_prefix(const int32_t* prefix, int count, i
 }
 
 // Where a kernel finds its work: the by-value argument block (up to eight
-// groups, split into cost-ordered classes by the host; whole tiles or
-// stream-K) ...
+// groups, split into cost-ordered classes by the host) - whole tiles, or with
+// SPLIT whole rounds and stream-K (separate instantiations, so that the
+// whole-tile kernels carry none of the stream-K code and its registers) ...
+template <bool SPLIT>
 struct KernargSrc {
-  static constexpr bool kCanSplit = true;
+  static constexpr bool kCanSplit = SPLIT;
   const KernelArgs& args;
   __device__ __forceinline__ int grid() const { return args.grid; }
-  __device__ __forceinline__ bool split() const { return args.split != 0; }
+  __device__ __forceinline__ bool split() const { return SPLIT && args.split != 0; }
   __device__ __forceinline__ int total_tiles() const { return args.tile_prefix[args.num_classes]; }
   __device__ __forceinline__ int class_of_tile(int tile) const {
     return search_prefix(args.tile_prefix, args.num_classes, tile);
@@ -423,7 +433,7 @@ struct GemmKernel {
     return x * q + (x < r ? x : r) + b / kXcds;
   }
 
-  __device__ GemmKernel(const Src& s, uint8_t* sm) : src(s), smem(sm) {
+  __device__ __forceinline__ GemmKernel(const Src& s, uint8_t* sm) : src(s), smem(sm) {
     const int tid = threadIdx.x;
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -471,6 +481,7 @@ struct GemmKernel {
 
   __device__ __forceinline__ void locate(Segment& s, int64_t u, int64_t u_end) const {
     s.u = u;
+    s.sk = true;
     s.valid = u < u_end;
     if (!s.valid) return;
     int stage;
@@ -481,8 +492,9 @@ struct GemmKernel {
   }
 
   __device__ __forceinline__ void first_segment(Segment& s) const {
+    s.sk = false;
     if constexpr (Src::kCanSplit) {
-      if (src.split()) {
+      if (src.split() && src.args.whole_tiles == 0) {
         locate(s, unit_begin(vwg), unit_begin(vwg + 1));
         return;
       }
@@ -496,8 +508,13 @@ struct GemmKernel {
 
   __device__ __forceinline__ void next_segment(Segment& s) const {
     if constexpr (Src::kCanSplit) {
-      if (src.split()) {
+      if (s.sk) {
         locate(s, s.u + (s.s1 - s.s0), unit_begin(vwg + 1));
+        return;
+      }
+      // after the whole rounds, this workgroup's unit range
+      if (src.split() && (int)s.u + 1 >= src.args.whole_tiles / src.grid()) {
+        locate(s, unit_begin(vwg), unit_begin(vwg + 1));
         return;
       }
     }
@@ -1168,139 +1185,189 @@ struct GemmKernel {
 
 
   // ---------------- stream-K: partials and the fold ----------------
-  // Workgroup wg owns two fp32 tile-sized slots: slot 0 for its first
-  // segment, slot 1 for its last. Each lane's 16 floats of block (i, j) are
-  // four 16-byte words at ((((wave * MB + i) * NB + j) * 4 + q) * 64 + lane) * 16
-  // bytes of the slot; only the wave's active row blocks are written. After
-  // the slots: one int32 arrival counter per workgroup, zero between calls;
-  // a split tile counts on the counter of its first contributor.
-  __device__ __forceinline__ static int partial_off(int wave_, int i, int j, int q, int lane_) {
-    return ((((wave_ * MB + i) * NB + j) * 4 + q) * 64 + lane_) * 16;
+  // Workgroup wg owns two fp32 tile-sized slots: slot 0 for the segment that
+  // starts its range, slot 1 for its last. Accumulator element e of block
+  // (i, j) of a lane is float ((((wave * MB + i) * NB + j) * 16 + e) * 64 + lane)
+  // of the slot, so that the 64 lanes' accesses to one element are 256
+  // contiguous bytes; only the wave's active row blocks are written. After
+  // the slots: arrival counters, kFoldLevels per slot, zero between calls.
+  __device__ __forceinline__ int partial_index(int i, int j) const {
+    return (((wave * MB + i) * NB + j) * 16) * 64 + lane;
   }
-  // Cache-policy bit SC1 of buffer loads and stores: device scope. Such stores
-  // write through the XCD's L2, and such loads read what device-scope stores
-  // wrote, from any XCD (the L2s of the XCDs are not coherent with each other).
-  static constexpr int kDeviceScope = 16;
-
-  __device__ __forceinline__ __amdgpu_buffer_rsrc_t slot_rsrc(int wg, int slot) const {
-    uint8_t* p = reinterpret_cast<uint8_t*>(src.args.partials) + ((size_t)wg * 2 + slot) * (TILE_FLOATS * 4);
-    return __builtin_amdgcn_make_buffer_rsrc(p, 0, TILE_FLOATS * 4, kBufferWord3);
+  // Partials are stored and loaded element by element as relaxed atomics of
+  // device scope (global_store/global_load with cache-policy bit SC1): such
+  // stores write through the XCD's L2, and such loads read what they wrote,
+  // from any XCD (the L2s of the XCDs are not coherent with each other).
+  __device__ __forceinline__ float* slot_ptr(int wg, int slot) const {
+    return src.args.partials + ((size_t)wg * 2 + slot) * TILE_FLOATS;
   }
-  __device__ __forceinline__ int32_t* arrivals(int wg) const {
+  __device__ __forceinline__ int32_t* arrivals(int wg, int slot, int level) const {
     uint8_t* p = reinterpret_cast<uint8_t*>(src.args.partials) + (size_t)src.args.grid * 2 * (TILE_FLOATS * 4);
-    return reinterpret_cast<int32_t*>(p) + wg;
+    return reinterpret_cast<int32_t*>(p) + ((wg * 2 + slot) * kFoldLevels + level);
   }
 
-  // This workgroup computed stages [s0, s1) of a tile, not all of it. It
-  // stores its partial sum with device-scope stores and waits until they have
-  // completed; then one thread adds one to the tile's arrival counter
-  // (device-scope atomic). The contributor that brings the count to the
-  // number of contributors folds: it adds every partial in contributor
-  // order, which is K order (its own from registers), rounds to fp16 and
-  // stores C, then clears the counter. No workgroup waits for another.
+  // The contributors of a split tile are the workgroups in [c_first, c_last]
+  // with non-empty ranges (ranges are empty only after whole rounds), ranked
+  // in workgroup order, which is K order. Contributor c's partial of the tile
+  // is in its slot 0 if its range starts inside the tile (or at its first
+  // unit u_first), else in slot 1.
+  __device__ __forceinline__ bool has_units(int c) const { return unit_begin(c + 1) > unit_begin(c); }
+  __device__ __forceinline__ int contributor(int c_first, int c_last, int rank) const {
+    if (src.args.whole_tiles == 0) return c_first + rank;
+    for (int c = c_first; c < c_last; ++c)
+      if (has_units(c) && rank-- == 0) return c;
+    return c_last;
+  }
+  __device__ __forceinline__ int slot_of(int c, int64_t u_first) const { return unit_begin(c) >= u_first ? 0 : 1; }
+
+  // This workgroup computed stages [s0, s1) of a tile, not all of it: the
+  // tile's C contributors fold their partials along a fixed binary tree over
+  // their ranks. Node (L, j) covers ranks [j 2^L, (j + 1) 2^L); its sum is
+  // (left child) + (right child) and sits in the slot of its first rank.
+  // Each contributor stores its partial (device-scope stores) and waits until
+  // they have completed; then, level by level, one thread adds one to the
+  // counter of its node (device-scope atomic, skipped where the node has no
+  // right child). The first to arrive stops there; the second loads both
+  // children (its own from registers at the first level), adds them, and
+  // either stores the sum to the node's slot and goes on up, or - at the
+  // root - rounds to fp16 and stores C. The order of every addition is fixed
+  // by the tree, so the result does not depend on timing, and no workgroup
+  // ever waits for another. Each node's counter is cleared by its folder.
   // Returns true when this workgroup stored the tile's C.
-  __device__ bool publish_partial(const f32x16 (&acc)[MB][NB], const TileCtx& t, const Segment& seg,
-                                  bool first_seg) const {
+  __device__ __forceinline__ bool publish_partial(const f32x16 (&acc)[MB][NB], const TileCtx& t,
+                                                  const Segment& seg) const {
     const int amb = active_blocks(t);
-    const __amdgpu_buffer_rsrc_t mine = slot_rsrc(vwg, first_seg ? 0 : 1);
+    float* mine = slot_ptr(vwg, seg.u == unit_begin(vwg) ? 0 : 1);
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
       if (i >= amb) break;
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const u32x4 v = {__builtin_bit_cast(uint32_t, acc_read(acc[i][j][4 * q + 0])),
-                           __builtin_bit_cast(uint32_t, acc_read(acc[i][j][4 * q + 1])),
-                           __builtin_bit_cast(uint32_t, acc_read(acc[i][j][4 * q + 2])),
-                           __builtin_bit_cast(uint32_t, acc_read(acc[i][j][4 * q + 3]))};
-          __builtin_amdgcn_raw_buffer_store_b128(v, mine, partial_off(wave, i, j, q, lane), 0, kDeviceScope);
-        }
+      for (int j = 0; j < NB; ++j) {
+        float x[16];
+        acc_block(acc, i, j, x);
+        store_block(mine, i, j, x);
+      }
     }
     wait_vmem_all();  // this wave's partial is visible at device scope
     const int64_t u_first = seg.u - seg.s0;  // the tile's first unit
     const int c_first = owner_of_unit(u_first);
     const int c_last = owner_of_unit(u_first + t.nk - 1);
-    int32_t* count = reinterpret_cast<int32_t*>(smem + FLAG_OFF);
-    block_sync();  // every wave's partial is
-    if (threadIdx.x == 0)
-      *count = __hip_atomic_fetch_add(arrivals(c_first), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    block_sync();
-    if (__builtin_amdgcn_readfirstlane(*count) != c_last - c_first) return false;
-    if (t.row0 + BM <= t.M && t.col0 + BN <= t.N) fold<false>(acc, t, amb, u_first, c_first, c_last);
-    else fold<true>(acc, t, amb, u_first, c_first, c_last);
-    if (threadIdx.x == 0) __hip_atomic_store(arrivals(c_first), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return true;
+    int count = c_last - c_first + 1, me = vwg - c_first;
+    if (src.args.whole_tiles != 0) {
+      count = me = 0;
+      for (int c = c_first; c <= c_last; ++c) {
+        me += c < vwg && has_units(c);
+        count += has_units(c);
+      }
+    }
+    const bool masked = !(t.row0 + BM <= t.M && t.col0 + BN <= t.N);
+    int32_t* flag = reinterpret_cast<int32_t*>(smem + FLAG_OFF);
+    for (int level = 1; (1 << (level - 1)) < count; ++level) {
+      const int left = (me >> level) << level, right = left + (1 << (level - 1));  // first ranks of the children
+      if (right >= count) continue;  // no right child: the node's sum is the left child's, in the same slot
+      const int wl = contributor(c_first, c_last, left), wr = contributor(c_first, c_last, right);
+      const int sl = slot_of(wl, u_first), sr = slot_of(wr, u_first);
+      block_sync();  // every wave's stores (partial, or the sum of the level below) have completed
+      if (threadIdx.x == 0)
+        *flag = __hip_atomic_fetch_add(arrivals(wl, sl, level), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      block_sync();
+      if (__builtin_amdgcn_readfirstlane(*flag) == 0) return false;  // the other child's folder goes on
+      const bool root = (1 << level) >= count;
+      // at the first level this workgroup's own child is its partial, still in registers
+      const int own = level == 1 ? (me == left ? 0 : 1) : -1;
+      if (root && masked) fold_node<true, true>(acc, t, amb, own, wl, sl, wr, sr);
+      else if (root) fold_node<true, false>(acc, t, amb, own, wl, sl, wr, sr);
+      else fold_node<false, false>(acc, t, amb, own, wl, sl, wr, sr);
+      if (threadIdx.x == 0) __hip_atomic_store(arrivals(wl, sl, level), 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (root) return true;
+      wait_vmem_all();  // the node's sum is visible at device scope
+    }
+    return false;  // (not reached: the root always has a right child)
   }
 
-  // The sum of all contributors' partials of the tile whose first unit is
-  // u_first, row block by row block: for each contributor in order, the
-  // block row's NB blocks are loaded at once (device-scope loads), then
-  // added. Contributor c stored the tile in slot 0 if its range starts inside
-  // the tile, else (the first contributor, whose range starts before it) in
-  // slot 1.
-  template <bool MASKED>
-  __device__ __forceinline__ void fold(const f32x16 (&acc)[MB][NB], const TileCtx& t, int amb, int64_t u_first,
-                                       int c_first, int c_last) const {
+  // The lane's 16 floats of block (i, j) of a partial slot, and of the
+  // accumulators.
+  __device__ __forceinline__ void load_block(const float* p, int i, int j, float (&x)[16]) const {
+    const float* b = p + partial_index(i, j);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) x[e] = __hip_atomic_load(b + e * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __device__ __forceinline__ void store_block(float* p, int i, int j, const float (&x)[16]) const {
+    float* b = p + partial_index(i, j);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) __hip_atomic_store(b + e * 64, x[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __device__ __forceinline__ static void acc_block(const f32x16 (&acc)[MB][NB], int i, int j, float (&x)[16]) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) x[e] = acc_read(acc[i][j][e]);
+  }
+
+  // Node sum = left child + right child, two blocks of a row block at a
+  // time: each child's values are loaded (device-scope; own = 0 or 1 takes
+  // that child from the accumulators instead), then added; at the root the
+  // sum is rounded and stored to C, elsewhere it is stored (device-scope) to
+  // the left child's slot, whose values were just read.
+  template <bool ROOT, bool MASKED>
+  __device__ __forceinline__ void fold_node(const f32x16 (&acc)[MB][NB], const TileCtx& t, int amb, int own, int wl,
+                                            int sl, int wr, int sr) const {
     int lro = lr, h8 = h * 8;
     asm volatile("" : "+v"(lro), "+v"(h8));
+    float* pl = slot_ptr(wl, sl);
+    const float* pr = slot_ptr(wr, sr);
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
       if (i >= amb) break;
-      f32x16 sum[NB];
-      for (int c = c_first; c <= c_last; ++c) {
-        f32x16 x[NB];
-        if (c == vwg) {
-#pragma unroll
-          for (int j = 0; j < NB; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) x[j][e] = acc_read(acc[i][j][e]);
-        } else {
-          const __amdgpu_buffer_rsrc_t r = slot_rsrc(c, unit_begin(c) >= u_first ? 0 : 1);
-#pragma unroll
-          for (int j = 0; j < NB; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              // (cast straight to floats: element reads of an unsigned vector
-              // cast of this builtin's result load one dword and copy it to
-              // all four elements with this compiler)
-              const f32x4 v = __builtin_bit_cast(
-                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, partial_off(wave, i, j, q, lane), 0, kDeviceScope));
-#pragma unroll
-              for (int e = 0; e < 4; ++e) x[j][4 * q + e] = v[e];
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < NB; ++j) sum[j] = c == c_first ? x[j] : sum[j] + x[j];
-      }
-      store_row_block<MASKED>(sum, t, i, lro, h8);
+      fold_blocks<ROOT, MASKED, 0>(acc, t, i, own, pl, pr, lro, h8);
+      if constexpr (NB > 2) fold_blocks<ROOT, MASKED, 2>(acc, t, i, own, pl, pr, lro, h8);
     }
   }
 
-  // C stores of this wave's row block i from the lane's 16 floats per block
-  // (the layout of the accumulators), as in epilogue_impl.
+  template <bool ROOT, bool MASKED, int J0>
+  __device__ __forceinline__ void fold_blocks(const f32x16 (&acc)[MB][NB], const TileCtx& t, int i, int own, float* pl,
+                                              const float* pr, int lro, int h8) const {
+    constexpr int JB = NB < 2 ? NB : 2;
+    float sum[JB][16], y[JB][16];
+#pragma unroll
+    for (int j = 0; j < JB; ++j) {
+      if (own == 0) acc_block(acc, i, J0 + j, sum[j]);
+      else load_block(pl, i, J0 + j, sum[j]);
+      if (own == 1) acc_block(acc, i, J0 + j, y[j]);
+      else load_block(pr, i, J0 + j, y[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < JB; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sum[j][e] += y[j][e];
+    if constexpr (ROOT) {
+#pragma unroll
+      for (int j = 0; j < JB; ++j) store_block_c<MASKED>(sum[j], t, i, J0 + j, lro, h8);
+    } else {
+#pragma unroll
+      for (int j = 0; j < JB; ++j) store_block(pl, i, J0 + j, sum[j]);
+    }
+  }
+
+  // C stores of block (i, j) of this wave from the lane's 16 floats (the
+  // layout of the accumulators), as in epilogue_impl.
   template <bool MASKED>
-  __device__ __forceinline__ void store_row_block(const f32x16 (&v)[NB], const TileCtx& t, int i, int lro,
-                                                  int h8) const {
+  __device__ __forceinline__ void store_block_c(const float (&a)[16], const TileCtx& t, int i, int j, int lro,
+                                                int h8) const {
     const int col0 = t.col0 + wn * WN;
     typedef __attribute__((address_space(1))) uint16_t gu16;
     const int rb = row_block(wm, i) * 32;
     gu16* crow = (gu16*)t.c + (size_t)(t.row0 + rb + lro) * t.N + col0 + h8;
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const f32x16& a = v[j];
-        const auto s0 = __builtin_amdgcn_permlane32_swap(pack_f16(a[8 * p + 0], a[8 * p + 1]),
-                                                         pack_f16(a[8 * p + 4], a[8 * p + 5]), false, false);
-        const auto s1 = __builtin_amdgcn_permlane32_swap(pack_f16(a[8 * p + 2], a[8 * p + 3]),
-                                                         pack_f16(a[8 * p + 6], a[8 * p + 7]), false, false);
-        const int cu = j * 32 + 2 * p * 8;
-        if (!MASKED || (lro < t.M - t.row0 - rb && h8 < t.N - col0 - cu)) {
-          const u32x4 w = {s0[0], s1[0], s0[1], s1[1]};
-          *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(crow + cu) = w;
-        }
+    for (int p = 0; p < 2; ++p) {
+      const auto s0 = __builtin_amdgcn_permlane32_swap(pack_f16(a[8 * p + 0], a[8 * p + 1]),
+                                                       pack_f16(a[8 * p + 4], a[8 * p + 5]), false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(pack_f16(a[8 * p + 2], a[8 * p + 3]),
+                                                       pack_f16(a[8 * p + 6], a[8 * p + 7]), false, false);
+      const int cu = j * 32 + 2 * p * 8;
+      if (!MASKED || (lro < t.M - t.row0 - rb && h8 < t.N - col0 - cu)) {
+        const u32x4 w = {s0[0], s1[0], s0[1], s1[1]};
+        *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(crow + cu) = w;
       }
+    }
   }
 
   // Stream-K leaves the tiles of k = 0 groups (no units) to a strided pass.
@@ -1314,7 +1381,7 @@ struct GemmKernel {
     for (int gi = 0; gi < args.num_classes; ++gi) {
       if (args.cls[gi].nk != 0) continue;
       for (int tile = args.tile_prefix[gi] + vwg; tile < args.tile_prefix[gi + 1]; tile += args.grid)
-        epilogue(zero, setup(tile));
+        if (tile >= args.whole_tiles) epilogue(zero, setup(tile));  // (earlier ones were dealt out whole)
     }
   }
 
@@ -1324,7 +1391,6 @@ struct GemmKernel {
     for (int b = 0; b < NS; ++b) issue_all(ld);  // every buffer is free
     Segment seg;
     first_segment(seg);
-    bool first_seg = true;
     int g0 = 0;
     int pend = kPendPrologue;
     while (seg.valid) {
@@ -1350,7 +1416,7 @@ struct GemmKernel {
       bool unmasked = false;
       if constexpr (Src::kCanSplit) {
         if (seg.s0 == 0 && seg.s1 == t.nk) unmasked = epilogue(acc, t);
-        else publish_partial(acc, t, seg, first_seg);
+        else publish_partial(acc, t, seg);
       } else {
         unmasked = epilogue(acc, t);  // whole tiles only
       }
@@ -1358,7 +1424,6 @@ struct GemmKernel {
       // after any earlier stores, iff it ran at least NS stages
       pend = (kOverlapStores && unmasked && n >= NS) ? kPendStores : kPendUnknown;
       g0 += n;
-      first_seg = false;
       next_segment(seg);
     }
     if constexpr (Src::kCanSplit) {
@@ -1379,11 +1444,11 @@ __device__ __forceinline__ const KernelArgs& kernel_args() {
 // Stage layout in LDS (bytes): [A: BM rows x 64][B: BN rows x 64]
 // [scale atoms: (BM + BN) / 128 atom rows x 2 k-groups x 512]; A and B rows are
 // swizzled by lds_off, the scale atoms are stored as in global memory.
-template <int BM, int BN, int WM, int WN, int NS, bool KPAD, bool MX = false>
+template <int BM, int BN, int WM, int WN, int NS, bool KPAD, bool MX = false, bool SPLIT = false>
 __global__ __launch_bounds__(kThreads, 1) void nvfp4_grouped_gemm_kernel(KernelArgs) {
-  using K = GemmKernel<BM, BN, WM, WN, NS, KernargSrc, KPAD, MX>;
+  using K = GemmKernel<BM, BN, WM, WN, NS, KernargSrc<SPLIT>, KPAD, MX>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[K::LDS_BYTES];
-  const K k(KernargSrc{kernel_args()}, smem);
+  const K k(KernargSrc<SPLIT>{kernel_args()}, smem);
   k.run();
 }
 
@@ -1514,8 +1579,7 @@ __global__ __launch_bounds__(kThreads, 1) void nvfp4_grouped_gemm_device_kernel(
   k.run();
 }
 
-// Clears the stream-K arrival counters (one int32 per workgroup) before a
-// split launch: a kernel rather than a memset, so that a captured graph
+// Clears the stream-K arrival counters before a split launch: a kernel rather than a memset, so that a captured graph
 // replays it correctly. The fold also leaves them zero.
 __global__ __launch_bounds__(kThreads) void nvfp4_clear_arrivals_kernel(int32_t* p, int n) {
   for (int i = (int)threadIdx.x; i < n; i += kThreads) p[i] = 0;
@@ -1527,27 +1591,28 @@ __global__ __launch_bounds__(kThreads) void nvfp4_clear_arrivals_kernel(int32_t*
 
 struct TileConfig {
   int bm, bn, wm, wn;
-  void (*kernel)(KernelArgs);       // k % 64 == 0 in every group
-  void (*kernel_kpad)(KernelArgs);  // some group with k % 64 == 32
-  void (*kernel_mx)(KernelArgs);    // power-of-two scales
-  void (*kernel_mx_kpad)(KernelArgs);
+  // [stream-K][power-of-two scales][some group with k % 64 == 32]
+  void (*kernel[2][2][2])(KernelArgs);
   void (*device_kernel)(DeviceGroupArgs);
   int64_t (*device_tiles)(const int32_t*, const uint64_t*);  // the device kernel's per-group check
-  // The same computation with a three-stage LDS pipeline (any k), for
-  // verification: each LDS buffer is then rewritten one stage sooner after
-  // its last reads, so a missing wait or barrier shows up as a difference.
+  // The same computation with a three-stage LDS pipeline (any k, whole tiles
+  // or stream-K), for verification: each LDS buffer is then rewritten one
+  // stage sooner after its last reads, so a missing wait or barrier shows up
+  // as a difference.
   void (*kernel_ns3)(KernelArgs);
 };
 
 constexpr int kStages = 4;  // LDS pipeline depth (4 x 36 KiB for 256x256 tiles)
 
-#define NVFP4_TILE_CONFIG(bm, bn, wm, wn)                                                       \
-  { bm, bn, wm, wn, nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, kStages, false>,              \
-    nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, kStages, true>,                                  \
-    nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, kStages, false, true>,                           \
-    nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, kStages, true, true>,                            \
-    nvfp4_grouped_gemm_device_kernel<bm, bn, wm, wn, kStages>,                                  \
-    device_group_tiles<bm, bn>, nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, 3, true> }
+#define NVFP4_KERNEL(bm, bn, wm, wn, kpad, mx, split) nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, kStages, kpad, mx, split>
+#define NVFP4_TILE_CONFIG(bm, bn, wm, wn)                                                                       \
+  { bm, bn, wm, wn,                                                                                         \
+    {{{NVFP4_KERNEL(bm, bn, wm, wn, false, false, false), NVFP4_KERNEL(bm, bn, wm, wn, true, false, false)},   \
+      {NVFP4_KERNEL(bm, bn, wm, wn, false, true, false), NVFP4_KERNEL(bm, bn, wm, wn, true, true, false)}},    \
+     {{NVFP4_KERNEL(bm, bn, wm, wn, false, false, true), NVFP4_KERNEL(bm, bn, wm, wn, true, false, true)},     \
+      {NVFP4_KERNEL(bm, bn, wm, wn, false, true, true), NVFP4_KERNEL(bm, bn, wm, wn, true, true, true)}}},     \
+    nvfp4_grouped_gemm_device_kernel<bm, bn, wm, wn, kStages>, device_group_tiles<bm, bn>,                     \
+    nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, 3, true, false, true> }
 const TileConfig kConfigs[] = {
     NVFP4_TILE_CONFIG(256, 256, 128, 128),
     NVFP4_TILE_CONFIG(128, 256, 64, 128),
@@ -1556,6 +1621,7 @@ const TileConfig kConfigs[] = {
     NVFP4_TILE_CONFIG(64, 64, 32, 32),
 };
 #undef NVFP4_TILE_CONFIG
+#undef NVFP4_KERNEL
 constexpr int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 // 256x256 tiles for the device-table entry point: the largest wave tiles
 // dequantise least per MFMA, and a many-group launch has tiles enough to
@@ -1589,6 +1655,7 @@ int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 struct Plan {
   int cfg;        // tile configuration
   int split;      // 0: whole tiles strided over the grid, 1: stream-K
+  int rounds;     // stream-K: whole rounds of `grid` tiles before the unit ranges
   int grid;       // persistent workgroups
   int64_t tiles;  // output tiles
   int64_t units;  // (tile, 128-K stage) units
@@ -1626,6 +1693,7 @@ struct WorkClass {
   int64_t tiles;  // tiles_m * tiles_n * l
   int nk;         // stages per tile
   double cost;    // modelled time per tile, in full tile-stages
+  double fill;    // share of a full tile's row blocks that hold rows below m (sizes its stream-K partial)
 };
 
 // The work classes of a call for tile configuration cfg, heaviest per tile
@@ -1634,49 +1702,140 @@ double tile_overhead_stages() { return 1.5; }  // epilogue and pipeline fill per
 
 int build_classes(const int32_t* ps, int G, int cfg, WorkClass* out);
 
-// Stream-K ranges: ranges[w] .. ranges[w + 1] are the units of workgroup w,
-// cut so that every workgroup gets the same modelled cost (a unit of class c
-// costs cls[c].cost / nk) and at least one unit. Needs 1 <= grid <= units.
-// Returns the largest modelled cost of one range, in full tile-stages.
-double split_ranges(const WorkClass* cls, int nc, int grid, int32_t* ranges) {
-  // piecewise-linear cumulative cost over the units, one piece per class
-  double cost_at[kMaxClasses + 1];
-  int64_t unit_at[kMaxClasses + 1];
-  cost_at[0] = 0.0;
+// Stream-K after `rounds` whole rounds: the first rounds * grid tiles (in
+// class order) are dealt out whole by the kernel's snake walk; the units of
+// the remaining tiles are cut into ranges[w] .. ranges[w + 1] for workgroup
+// w (contiguous in workgroup order, possibly empty) so that every
+// workgroup's modelled cost, its whole tiles included, comes out equal (the
+// remaining cost is water-filled over the workgroups' whole-tile loads). A
+// unit of class c costs cls[c].cost / nk. pub and fold are the modelled costs
+// of storing and of folding one full-sized partial tile; a partial's size
+// scales with its class's fill. Returns the modelled makespan in full
+// tile-stages. Needs 1 <= grid <= kMaxSplitGrid and rounds * grid <= tiles.
+// Modelled stream-K costs, in full tile-stages of the configuration, for a
+// partial of fill f (its share of a full tile's row blocks): storing it
+// (device-scope stores, then a wait for them) and folding a tile with C
+// contributors along the fold tree (the root's folder goes through
+// ceil(log2 C) levels, each but the first loading two children and storing
+// a sum). Fitted to per-workgroup timestamps on 256x256 and 256x128 tiles
+// (256x256, f = 1: ~6 us to store, ~8 us more to fold with C = 2, against a
+// ~2.2 us stage). The one-workgroup kernel that clears the counters first is
+// counted in 128x128 tile-stage units.
+double partial_store_stages(double f) { return 1.0 + 1.7 * f; }
+double fold_stages(double f, int contributors) {
+  int levels = 0;
+  while ((1 << levels) < contributors) ++levels;
+  return (0.3 + 3.3 * f) * (1.0 + 1.3 * (levels - 1));
+}
+constexpr double kClearKernelUnits = 4.0;
+
+// Stream-K after `rounds` whole rounds: the first rounds * grid tiles (in
+// class order) are dealt out whole by the kernel's snake walk; the units of
+// the remaining tiles are cut into ranges[w] .. ranges[w + 1] for workgroup
+// w (contiguous in workgroup order, possibly empty) so that every
+// workgroup's whole tiles plus units (a unit of class c costs
+// cls[c].cost / nk) come out equal: the remaining cost is water-filled over
+// the whole-tile loads. The partials' stores and folds are left out of the
+// cuts (which contributor folds depends on timing: cutting around a
+// predicted folder measured worse) and added to the returned makespan
+// estimate, in full tile-stages: a range's first segment may be the tail of
+// a tile begun by an earlier workgroup (it stores a partial), and its last
+// the head of a tile that later workgroups finish, whose fold it usually
+// does. Needs 1 <= grid <= kMaxSplitGrid and rounds * grid <= tiles.
+double hybrid_ranges(const WorkClass* cls, int nc, int grid, int rounds, int32_t* ranges) {
+  double load[kMaxSplitGrid], over[kMaxSplitGrid];
+  for (int w = 0; w < grid; ++w) load[w] = over[w] = 0.0;
+  int64_t unit_at[kMaxClasses + 1], tile_at[kMaxClasses + 1];
   unit_at[0] = 0;
+  tile_at[0] = 0;
   for (int c = 0; c < nc; ++c) {
-    const int64_t n = cls[c].nk ? cls[c].tiles * cls[c].nk : 0;
-    unit_at[c + 1] = unit_at[c] + n;
-    cost_at[c + 1] = cost_at[c] + (n ? cls[c].cost * cls[c].tiles : 0.0);
+    unit_at[c + 1] = unit_at[c] + cls[c].tiles * cls[c].nk;
+    tile_at[c + 1] = tile_at[c] + cls[c].tiles;
+  }
+  // the whole rounds, as the kernel walks them
+  const int64_t whole = (int64_t)rounds * grid;
+  int64_t u0 = 0;  // first unit after the whole tiles
+  for (int c = 0; c < nc; ++c) {
+    const int64_t n = std::min(cls[c].tiles, std::max<int64_t>(whole - tile_at[c], 0));
+    for (int64_t i = 0; i < n; ++i) {
+      const int64_t t = tile_at[c] + i, r = t / grid, pos = t % grid;
+      load[(r & 1) ? grid - 1 - pos : pos] += cls[c].cost;
+    }
+    u0 += n * cls[c].nk;
   }
   const int64_t units = unit_at[nc];
-  const double total = cost_at[nc];
-  auto cost_of = [&](int64_t u) {  // cost of units [0, u)
-    int c = 0;
-    while (c < nc - 1 && unit_at[c + 1] <= u) ++c;
-    const int64_t n = unit_at[c + 1] - unit_at[c];
-    return n ? cost_at[c] + (cost_at[c + 1] - cost_at[c]) * (double)(u - unit_at[c]) / (double)n : cost_at[c];
+  auto cost_to = [&](int64_t u) {  // cost of units [u0, u)
+    double x = 0.0;
+    for (int c = 0; c < nc; ++c) {
+      const int64_t lo = std::max(unit_at[c], u0), hi = std::min(unit_at[c + 1], u);
+      if (hi > lo) x += (double)(hi - lo) * cls[c].cost / cls[c].nk;
+    }
+    return x;
   };
-  ranges[0] = 0;
-  int c = 0;
-  for (int w = 1; w < grid; ++w) {
-    const double x = total * w / grid;
-    while (c < nc - 1 && cost_at[c + 1] <= x) ++c;
-    const int64_t n = unit_at[c + 1] - unit_at[c];
-    const double span = cost_at[c + 1] - cost_at[c];
-    int64_t u = unit_at[c] + (n && span > 0.0 ? (int64_t)std::llround((x - cost_at[c]) / span * (double)n) : 0);
-    // strictly increasing, leaving one unit for every later workgroup
-    u = std::max<int64_t>(u, (int64_t)ranges[w - 1] + 1);
-    u = std::min<int64_t>(u, units - (grid - w));
-    ranges[w] = (int32_t)u;
+  auto unit_of_cost = [&](double target) {  // inverse of cost_to, to the nearest unit
+    double x = 0.0;
+    for (int c = 0; c < nc; ++c) {
+      const int64_t lo = std::max(unit_at[c], u0), hi = unit_at[c + 1];
+      if (hi <= lo) continue;
+      const double per = cls[c].cost / cls[c].nk, span = (double)(hi - lo) * per;
+      if (x + span >= target) return lo + (int64_t)std::llround((target - x) / per);
+      x += span;
+    }
+    return units;
+  };
+  auto locate_unit = [&](int64_t u, int* c, int* stage) {
+    int k = 0;
+    while (k < nc - 1 && unit_at[k + 1] <= u) ++k;
+    *c = k;
+    const int64_t local = u - unit_at[k];
+    *stage = (int)(local % cls[k].nk);
+    return tile_at[k] + local / cls[k].nk;
+  };
+  const double total = cost_to(units);
+  {
+    // water level: the sum over w of max(0, level - load[w]) is total
+    double base[kMaxSplitGrid];
+    for (int w = 0; w < grid; ++w) base[w] = load[w];
+    std::sort(base, base + grid);
+    double level = base[grid - 1] + total / grid, acc = 0.0;
+    for (int i = 0; i < grid; ++i) {
+      acc += base[i];
+      const double lv = (total + acc) / (i + 1);  // the level with the i + 1 lowest under it
+      if (i + 1 == grid || lv <= base[i + 1]) {
+        level = lv;
+        break;
+      }
+    }
+    ranges[0] = (int32_t)u0;
+    double target = 0.0;
+    for (int w = 1; w < grid; ++w) {
+      target += std::max(0.0, level - load[w - 1]);
+      // without whole rounds every workgroup gets at least one unit (grid <= units)
+      const int64_t lo = ranges[w - 1] + (rounds == 0 ? 1 : 0), hi = units - (rounds == 0 ? grid - w : 0);
+      ranges[w] = (int32_t)std::min<int64_t>(std::max<int64_t>(unit_of_cost(target), lo), hi);
+    }
+    ranges[grid] = (int32_t)units;
+    // the partials of these cuts
+    for (int w = 0; w < grid; ++w) {
+      over[w] = 0.0;
+      const int64_t a = ranges[w], b = ranges[w + 1];
+      if (b <= a) continue;
+      int ca, cb, sa, sb;
+      const int64_t ta = locate_unit(a, &ca, &sa), tb = locate_unit(b - 1, &cb, &sb);
+      const bool tail = sa > 0, head = sb + 1 < cls[cb].nk;  // first segment begun earlier; last unfinished
+      if (tail) over[w] += partial_store_stages(cls[ca].fill);
+      if (head && !(tail && ta == tb)) {
+        // contributors of tile tb: this one and the later non-empty ranges that start inside it
+        const int64_t end = b - 1 - sb + cls[cb].nk;
+        int contributors = 1;
+        for (int v = w + 1; v < grid && ranges[v] < end; ++v) contributors += ranges[v + 1] > ranges[v];
+        over[w] += partial_store_stages(cls[cb].fill) + fold_stages(cls[cb].fill, contributors);
+      }
+    }
   }
-  ranges[grid] = (int32_t)units;
-  double worst = 0.0, prev = 0.0;
-  for (int w = 1; w <= grid; ++w) {
-    const double at = cost_of(ranges[w]);
-    worst = std::max(worst, at - prev);
-    prev = at;
-  }
+  double worst = 0.0;
+  for (int w = 0; w < grid; ++w)
+    worst = std::max(worst, load[w] + over[w] + cost_to(ranges[w + 1]) - cost_to(ranges[w]));
   return worst;
 }
 
@@ -1695,25 +1854,27 @@ int build_classes(const int32_t* ps, int G, int cfg, WorkClass* out) {
     const int body_rows = split_tail ? tiles_m - 1 : tiles_m;
     const int body_amb = tiles_m == 1 ? tail_amb : mb;  // a one-row group is all tail
     out[n++] = WorkClass{g, 0, body_rows, body_rows * tiles_n * l, nk,
-                         nk * stage_fraction(body_amb, mb) + tile_overhead_stages()};
+                         nk * stage_fraction(body_amb, mb) + tile_overhead_stages(), (double)body_amb / mb};
     if (split_tail)
-      out[n++] = WorkClass{g, tiles_m - 1, 1, tiles_n * l, nk, nk * stage_fraction(tail_amb, mb) + tile_overhead_stages()};
+      out[n++] = WorkClass{g, tiles_m - 1, 1, tiles_n * l, nk, nk * stage_fraction(tail_amb, mb) + tile_overhead_stages(),
+                           (double)tail_amb / mb};
   }
   std::stable_sort(out, out + n, [](const WorkClass& x, const WorkClass& y) { return x.cost > y.cost; });
   return n;
 }
 
-// Stream-K workspace: two fp32 tile slots per workgroup, then one int32
-// arrival counter per workgroup (padded to 256 bytes).
+// Stream-K workspace: two fp32 tile slots per workgroup, then the fold
+// tree's arrival counters, kFoldLevels int32 per slot (padded to 256 bytes).
 size_t partial_bytes_for(int cfg, int grid) { return (size_t)grid * 2 * kConfigs[cfg].bm * kConfigs[cfg].bn * 4; }
+int counter_count(int grid) { return grid * 2 * kFoldLevels; }
 size_t workspace_bytes_for(int cfg, int grid) {
-  return partial_bytes_for(cfg, grid) + ((size_t)grid * 4 + 255) / 256 * 256;
+  return partial_bytes_for(cfg, grid) + ((size_t)counter_count(grid) * 4 + 255) / 256 * 256;
 }
 
 // Cost model, in units of one 128x128 tile-stage of MFMA work. Smaller wave
 // tiles dequantise more per MFMA; a tile costs a fixed prologue/epilogue on top
-// of its stages; a stream-K plan adds its partial stores and the fold
-// kernel (plan_for).
+// of its stages; a stream-K plan adds its partial stores and folds and the
+// kernel that clears its counters (plan_for).
 double tile_unit(int cfg) {
   const TileConfig& tc = kConfigs[cfg];
   const double size = (double)tc.bm * tc.bn / (128.0 * 128.0);
@@ -1762,17 +1923,20 @@ Plan plan_for(const int32_t* ps, int G, int cus, int cfg, int split) {
     p.grid = (int)(units < cap ? units : cap);
     WorkClass cls[kMaxClasses];
     const int nc = build_classes(ps, G, cfg, cls);
-    static thread_local int32_t ranges[kMaxSplitGrid + 1];
-    const double per = split_ranges(cls, nc, p.grid, ranges);
-    // Each workgroup stores up to two fp32 partial tiles (device-scope
-    // stores, then a wait for them) and folds about one split tile (loads
-    // the other contributors' partials); a one-workgroup kernel clears the
-    // arrival counters first. Both scale with the tile area, in 128x128
-    // tile-stage units (about 0.8 us).
-    const TileConfig& tc = kConfigs[cfg];
-    const double area = (double)tc.bm * tc.bn / 65536.0;
-    const double publish = 4.0 * area, fold = 4.0 * area, clear = 2.0;
-    p.cost = unit * per + publish + fold + clear;
+    int32_t ranges[kMaxSplitGrid + 1];
+    // whole rounds first (up to four), then the water-filled unit ranges
+    // (no units, e.g. every group empty or of k = 0: nothing to plan)
+    const int64_t max_rounds = p.grid > 0 ? std::min<int64_t>(tiles / p.grid, 4) : -1;
+    double best = 0.0;
+    p.rounds = 0;
+    for (int r = 0; r <= max_rounds; ++r) {
+      const double m = hybrid_ranges(cls, nc, p.grid, r, ranges);
+      if (r == 0 || m < best) {
+        best = m;
+        p.rounds = r;
+      }
+    }
+    p.cost = unit * best + kClearKernelUnits;
     p.ws_bytes = workspace_bytes_for(cfg, p.grid);
   }
   return p;
@@ -1911,18 +2075,19 @@ int launch(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, vo
   args.status = mx_status;
   if (plan.split) {
     args.partials = reinterpret_cast<float*>(workspace);
-    split_ranges(cls, nc, plan.grid, args.wg_unit);
+    args.whole_tiles = plan.rounds * plan.grid;
+    hybrid_ranges(cls, nc, plan.grid, plan.rounds, args.wg_unit);
   }
   if (tiles == 0 || plan.grid == 0) return NVFP4_OK;
   const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   bool kpad = false;
   for (int g = 0; g < G; ++g) kpad = kpad || (ps[4 * g + 2] % 64 != 0);
-  void (*kernel)(KernelArgs) = mx_status ? (kpad ? tc.kernel_mx_kpad : tc.kernel_mx) : (kpad ? tc.kernel_kpad : tc.kernel);
+  void (*kernel)(KernelArgs) = tc.kernel[plan.split ? 1 : 0][mx_status ? 1 : 0][kpad ? 1 : 0];
   if (stages == 3) kernel = tc.kernel_ns3;
   if (plan.split) {
     int32_t* counters = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) +
                                                    partial_bytes_for(plan.cfg, plan.grid));
-    hipLaunchKernelGGL(nvfp4_clear_arrivals_kernel, dim3(1), dim3(kThreads), 0, st, counters, plan.grid);
+    hipLaunchKernelGGL(nvfp4_clear_arrivals_kernel, dim3(1), dim3(kThreads), 0, st, counters, counter_count(plan.grid));
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) { t_last_hip_error = (int)e; return NVFP4_ERR_HIP; }
   }
@@ -2048,6 +2213,21 @@ int nvfp4_launch_geometry(const int32_t* ps, int G, int num_cus, int cfg, int sp
   if (split_used) *split_used = p.split;
   if (workspace_bytes) *workspace_bytes = p.ws_bytes;
   return p.cfg;
+}
+
+int nvfp4_split_plan(const int32_t* ps, int G, int num_cus, int cfg, int32_t* whole_tiles, int32_t* unit_ranges,
+                     int max_ranges) {
+  if (sizes_ok(ps, G) != NVFP4_OK || num_cus < 1) return NVFP4_ERR_INVALID;
+  if (cfg < -1 || cfg >= kNumConfigs) return NVFP4_ERR_CONFIG;
+  const Plan p = cached_plan(ps, G, num_cus, cfg, 1, SIZE_MAX);
+  if (!p.split) return NVFP4_ERR_INVALID;  // nothing to split (no units)
+  if (whole_tiles) *whole_tiles = p.rounds * p.grid;
+  if (unit_ranges && max_ranges >= p.grid + 1) {
+    WorkClass cls[kMaxClasses];
+    const int nc = build_classes(ps, G, p.cfg, cls);
+    hybrid_ranges(cls, nc, p.grid, p.rounds, unit_ranges);
+  }
+  return p.grid;
 }
 
 size_t nvfp4_workspace_bytes(const int32_t* ps, int G, int num_cus) {

@@ -189,8 +189,8 @@ def test_tile_configs_and_geometry():
         assert geo["split"] == 0 and geo["workspace_bytes"] == 0
         geo = mm.nvfp4_launch_geometry(shapes, 256, c, 1)
         assert geo["split"] == 1 and geo["grid"] == min(units, 256)
-        # two fp32 tile slots and one int32 arrival counter per workgroup (counters padded to 256 bytes)
-        counters = -(-geo["grid"] * 4 // 256) * 256
+        # two fp32 tile slots and 10 int32 fold-tree counters per slot per workgroup (padded to 256 bytes)
+        counters = -(-geo["grid"] * 2 * 10 * 4 // 256) * 256
         assert geo["workspace_bytes"] == geo["grid"] * 2 * info["bm"] * info["bn"] * 4 + counters
         assert mm.nvfp4_workspace_bytes(shapes, 256) >= geo["workspace_bytes"]
     # empty groups own no tiles, wherever they sit
@@ -204,6 +204,35 @@ def test_tile_configs_and_geometry():
     small = next(c for c in range(n) if (mm.nvfp4_tile_config_info(c)["bm"], mm.nvfp4_tile_config_info(c)["bn"]) == (64, 64))
     for idx in (0, 1):
         assert mm.nvfp4_select_tile_config(synth.workload_shapes(idx), 256) == small
+
+
+def test_split_plan_covers_every_unit_once():
+    """Stream-K plans: whole rounds of one tile per workgroup, then contiguous
+    (possibly empty) unit ranges in workgroup order that cover exactly the
+    units of the remaining tiles."""
+    for idx in (1, 2, 3, 4):
+        shapes = synth.workload_shapes(idx)
+        for cfg in range(mm.nvfp4_num_tile_configs()):
+            info = mm.nvfp4_tile_config_info(cfg)
+            tiles = sum(-(-m // info["bm"]) * -(-n // info["bn"]) * l for (m, n, k, l) in shapes)
+            units = sum(-(-m // info["bm"]) * -(-n // info["bn"]) * l * -(-k // 128) for (m, n, k, l) in shapes)
+            whole, r = mm.nvfp4_split_plan(shapes, 256, cfg)
+            grid = len(r) - 1
+            assert grid == mm.nvfp4_launch_geometry(shapes, 256, cfg, 1)["grid"] == min(units, 256)
+            assert whole % grid == 0 and 0 <= whole <= tiles
+            # the whole tiles hold r[0] units: whole * nk when every group has the same k
+            nks = [-(-k // 128) for (m, n, k, l) in shapes]
+            assert min(nks) * whole <= r[0] <= max(nks) * whole and r[-1] == units
+            if len(set(nks)) == 1:
+                assert r[0] == whole * nks[0]
+            assert all(a <= b for a, b in zip(r, r[1:]))
+            if whole == 0:
+                assert all(a < b for a, b in zip(r, r[1:]))  # without whole rounds no range is empty
+    # a long K on few tiles: no whole round, one unit (128-K stage) per workgroup
+    whole, r = mm.nvfp4_split_plan([(256, 256, 16384, 1), (40, 136, 64, 1)], 256, 0)
+    assert whole == 0 and r == list(range(130))  # 128 + 1 units on 129 workgroups
+    with pytest.raises(mm.Nvfp4Error):
+        mm.nvfp4_split_plan([(0, 128, 256, 1)], 256, 0)  # no units to split
 
 
 def test_ex_entry_point_checks_before_any_hip_call():
