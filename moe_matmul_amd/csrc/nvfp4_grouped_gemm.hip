@@ -1793,23 +1793,38 @@ double hybrid_ranges(const WorkClass* cls, int nc, int grid, int rounds, int32_t
   };
   const double total = cost_to(units);
   {
-    // water level: the sum over w of max(0, level - load[w]) is total
-    double base[kMaxSplitGrid];
-    for (int w = 0; w < grid; ++w) base[w] = load[w];
-    std::sort(base, base + grid);
-    double level = base[grid - 1] + total / grid, acc = 0.0;
-    for (int i = 0; i < grid; ++i) {
-      acc += base[i];
-      const double lv = (total + acc) / (i + 1);  // the level with the i + 1 lowest under it
-      if (i + 1 == grid || lv <= base[i + 1]) {
-        level = lv;
-        break;
-      }
+    // water level: the sum over w of max(0, level - load[w]) is total. After
+    // whole rounds a workgroup gets at least about a quarter of a tile's
+    // stages or nothing: slivers of a few units would spread one tile over
+    // many workgroups, whose partials then pass through a deep fold tree
+    // (measured: 14 one-unit ranges of one tile, folds of up to 45 us).
+    int order[kMaxSplitGrid];
+    for (int w = 0; w < grid; ++w) order[w] = w;
+    std::stable_sort(order, order + grid, [&](int x, int y) { return load[x] < load[y]; });
+    const int64_t sk_tiles = tile_at[nc] - whole;
+    const double min_amount =
+        rounds == 0 || units == u0 ? 0.0
+                                   : total / (double)(units - u0) *
+                                         std::max<double>(2.0, std::floor((double)(units - u0) / sk_tiles / 4.0));
+    // the k lowest-loaded workgroups share the rest: k as large as the level
+    // allows (each of them below it) and, after whole rounds, as leaves the
+    // k-th at least min_amount
+    double level = 0.0, acc = 0.0;
+    int k = 0;
+    for (int i = 1; i <= grid; ++i) {
+      acc += load[order[i - 1]];
+      const double lv = (total + acc) / i;
+      if (i > 1 && (lv < load[order[i - 1]] || lv - load[order[i - 1]] < min_amount)) break;
+      level = lv;
+      k = i;
     }
+    double amount[kMaxSplitGrid];
+    for (int w = 0; w < grid; ++w) amount[w] = 0.0;
+    for (int r = 0; r < k; ++r) amount[order[r]] = std::max(0.0, level - load[order[r]]);
     ranges[0] = (int32_t)u0;
     double target = 0.0;
     for (int w = 1; w < grid; ++w) {
-      target += std::max(0.0, level - load[w - 1]);
+      target += amount[w - 1];
       // without whole rounds every workgroup gets at least one unit (grid <= units)
       const int64_t lo = ranges[w - 1] + (rounds == 0 ? 1 : 0), hi = units - (rounds == 0 ? grid - w : 0);
       ranges[w] = (int32_t)std::min<int64_t>(std::max<int64_t>(unit_of_cost(target), lo), hi);
