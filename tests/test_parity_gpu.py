@@ -226,6 +226,41 @@ def test_streamk_workspace_reuse_across_inputs(cfg):
             assert not O.tolerance_violations(c, r["c16"], r["s"]).any(), f"call {rep} (input {x})"
 
 
+def test_streamk_random_shapes_every_config():
+    """Random group shapes (empty groups, ragged m, n and k, k % 64 = 32,
+    batches) on every tile configuration with stream-K forced, through one
+    workspace filled with 0xFF first: every result within the oracle's
+    tolerance, and a repeat bitwise identical (the fold tree fixes the order
+    of every addition)."""
+    rng = np.random.default_rng(2024)
+    ws = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    ws.fill_(0xFF)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for case in range(30):
+        shapes = [(int(rng.choice([0, 1, 7, 33, 64, 100, 128, 200, 255, 256, 300, 400])),
+                   int(rng.choice([8, 64, 136, 256, 264, 512])),
+                   int(rng.choice([32, 64, 96, 128, 256, 512, 1024, 2048, 4096])),
+                   int(rng.choice([1, 1, 1, 2]))) for _ in range(int(rng.integers(1, 9)))]
+        groups = synth.make_custom(shapes, seed=int(rng.integers(1 << 30)))
+        ref = O.grouped_gemm(shapes, groups)
+        for cfg in range(mm.nvfp4_num_tile_configs()):
+            if mm.nvfp4_launch_geometry(shapes, cus, cfg, 1)["workspace_bytes"] > ws.numel():
+                continue
+            announce(f"stream-K random case {case} cfg {cfg} shapes={shapes}")
+            d = dev.upload(shapes, groups)
+            outs = []
+            for _ in range(2):
+                for dd in d:
+                    dd["c"].fill_(-1)
+                dev.run(shapes, d, tile_config=cfg, split_mode=1, workspace=ws)
+                torch.cuda.synchronize()
+                outs.append([c.copy() for c in dev.c_as_numpy(shapes, d)])
+            for (m, n, k, l), a, b, r in zip(shapes, outs[0], outs[1], ref):
+                if m and n:
+                    assert not O.tolerance_violations(a, r["c16"], r["s"]).any(), (case, cfg, (m, n, k, l))
+                    assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), (case, cfg, (m, n, k, l))
+
+
 @pytest.mark.parametrize("split", [-1, 0])
 def test_max_k(split):
     """The largest K the library accepts (2^22): fp32 accumulation over 4M
