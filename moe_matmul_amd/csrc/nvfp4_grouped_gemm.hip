@@ -692,81 +692,113 @@ struct GemmKernel {
   // no dequantisation and no MFMAs. A wave with AMB = 0 still issues its share
   // of the loads and joins every barrier.
 
-  // ds_reads of one half stage (kk) from LDS buffer buf.
-  template <int AMB>
-  __device__ __forceinline__ void read_half(Raw& r, int buf, int kk) const {
+  // Per-lane LDS offsets of a wave's operands: its first A and B chunk for
+  // each half, its B scale words, and the selector of its A scale bytes.
+  // The normal layout is the wave's (wm, wn) tile; the wide one (tiles of one
+  // row block, see mainloop_rows) gives each wave row block 0 and a quarter
+  // of the tile's columns.
+  struct Bases {
+    int a[2], b[2], sb;
+    uint32_t sel;
+  };
+  __device__ __forceinline__ Bases normal_bases() const {
+    return Bases{{a_base[0], a_base[1]}, {b_base[0], b_base[1]}, sb_base, sa_sel};
+  }
+  static constexpr int WIDE_COLS = BN / 4;
+  static constexpr int NBW = WIDE_COLS / 32;  // block columns of a wave in the wide layout
+  __device__ __forceinline__ Bases wide_bases() const {
+    Bases b;
+    const int c0 = wave * WIDE_COLS;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      b.a[kk] = lds_off(lr, kk * 2 + h);
+      b.b[kk] = A_BYTES + lds_off(c0 + lr, kk * 2 + h);
+    }
+    b.sb = A_BYTES + B_BYTES + (A_ATOMS + (c0 >> 7)) * 1024 + lr * 16 + ((c0 & 127) >> 5) * 4;
+    b.sel = (uint32_t)(2 * h) | ((uint32_t)(2 * h + 1) << 8) | 0x0C0C0000u;
+    return b;
+  }
+
+  // ds_reads of one half stage (kk) from LDS buffer buf (NBX block columns).
+  template <int AMB, int NBX = NB>
+  __device__ __forceinline__ void read_half(Raw& r, int buf, int kk, const Bases& bs) const {
     if (AMB == 0) return;
     const uint8_t* St = smem + buf * STAGE_BYTES;
 #pragma unroll
     for (int i = 0; i < AMB; ++i)
-      r.a[i] = *reinterpret_cast<const u32x4*>(St + a_base[kk] + i * WAVES_M * 32 * kRowBytes);
+      r.a[i] = *reinterpret_cast<const u32x4*>(St + bs.a[kk] + i * WAVES_M * 32 * kRowBytes);
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
-      r.b[j] = *reinterpret_cast<const u32x4*>(St + b_base[kk] + j * 32 * kRowBytes);
+    for (int j = 0; j < NBX; ++j)
+      r.b[j] = *reinterpret_cast<const u32x4*>(St + bs.b[kk] + j * 32 * kRowBytes);
     const int sbo = kSubAtomB ? 4 * (sub_words >> 4) : 0;
-    const ScaleVec<NB> sb = *reinterpret_cast<const ScaleVec<NB>*>(St + sb_base + kk * 512 + sbo);
+    const ScaleVec<NBX> sb = *reinterpret_cast<const ScaleVec<NBX>*>(St + bs.sb + kk * 512 + sbo);
 #pragma unroll
     for (int a = 0; a < (AMB + 1) / 2; ++a)
       r.sa[a] = *reinterpret_cast<const u32x4*>(St + sa_base + a * 1024 + kk * 512);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) r.sb[j] = sb[j];
+    for (int j = 0; j < NBX; ++j) r.sb[j] = sb[j];
+  }
+  template <int AMB>
+  __device__ __forceinline__ void read_half(Raw& r, int buf, int kk) const {
+    read_half<AMB, NB>(r, buf, kk, normal_bases());
   }
 
   // The word of the lane's A scale chunk that holds wave block i's scales,
   // with this lane's two bytes (16-blocks 2h, 2h+1) in the low half: block
   // b = 2 i + wm sits in word b % 4 of atom b / 4, shifted by the tile's
   // sub-atom offset for 64-row tiles.
-  __device__ __forceinline__ uint32_t a_scale_word(const Raw& r, int i) const {
+  __device__ __forceinline__ uint32_t a_scale_word(const Raw& r, int i, uint32_t sel) const {
     const u32x4& c = r.sa[i >> 1];
     if constexpr (kSubAtomA) {
       const bool upper = (sub_words & 15) != 0;  // rows 64..127 of the atom: words 2 and 3
-      return __builtin_amdgcn_perm(upper ? c[3] : c[1], upper ? c[2] : c[0], sa_sel);
+      return __builtin_amdgcn_perm(upper ? c[3] : c[1], upper ? c[2] : c[0], sel);
     }
-    return __builtin_amdgcn_perm(c[2 * (i & 1) + 1], c[2 * (i & 1)], sa_sel);
+    return __builtin_amdgcn_perm(c[2 * (i & 1) + 1], c[2 * (i & 1)], sel);
   }
+  __device__ __forceinline__ uint32_t a_scale_word(const Raw& r, int i) const { return a_scale_word(r, i, sa_sel); }
 
   // The lane's two E4M3 scales (16-blocks 2h, 2h+1 of the half) -> f16, exactly.
-  template <int AMB>
-  __device__ __forceinline__ void convert_scales(Scales& s, const Raw& r) const {
+  template <int AMB, int NBX = NB>
+  __device__ __forceinline__ void convert_scales(Scales& s, const Raw& r, uint32_t sel) const {
     if (AMB == 0) return;
     const int hshift = h * 16;
 #pragma unroll
     for (int i = 0; i < AMB; ++i) {
-      const uint32_t w = a_scale_word(r, i);
+      const uint32_t w = a_scale_word(r, i, sel);
       s.a[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
     }
 #pragma unroll
-    for (int j = 0; j < NB; ++j) s.b[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sb[j] >> hshift, 1.0f, false);
+    for (int j = 0; j < NBX; ++j) s.b[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sb[j] >> hshift, 1.0f, false);
   }
 
   // Operand fragments of substep S (K elements 8S..8S+7 of the lane's 32).
-  template <int S, int AMB>
+  template <int S, int AMB, int NBX = NB>
   __device__ __forceinline__ void dequant(Frags& f, const Raw& r, const Scales& s) const {
     if (AMB == 0) return;
 #pragma unroll
     for (int i = 0; i < AMB; ++i) f.a[i] = dequant8(r.a[i][S], s.a[i][S >> 1]);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) f.b[j] = dequant8(r.b[j][S], s.b[j][S >> 1]);
+    for (int j = 0; j < NBX; ++j) f.b[j] = dequant8(r.b[j][S], s.b[j][S >> 1]);
   }
 
-  template <int AMB>
+  template <int AMB, int NBX = NB>
   __device__ __forceinline__ static void mfmas(f32x16 (&acc)[MB][NB], const Frags& f) {
 #pragma unroll
     for (int i = 0; i < AMB; ++i)
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
+      for (int j = 0; j < NBX; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
   }
 
   // Keeps the fragments and scales of the next substep computed before this
   // point: without it the compiler sinks their conversion past the barrier,
   // next to their first use, where it cannot overlap any MFMA.
-  template <int AMB>
+  template <int AMB, int NBX = NB>
   __device__ __forceinline__ static void pin(const Frags& f, const Scales& s) {
 #pragma unroll
     for (int i = 0; i < AMB; ++i) asm volatile("" ::"v"(f.a[i]), "v"(s.a[i]));
 #pragma unroll
-    for (int j = 0; j < (AMB ? NB : 0); ++j) asm volatile("" ::"v"(f.b[j]), "v"(s.b[j]));
+    for (int j = 0; j < (AMB ? NBX : 0); ++j) asm volatile("" ::"v"(f.b[j]), "v"(s.b[j]));
   }
 
   // One substep, in a scheduling region of its own: the MFMAs of `use`
@@ -777,21 +809,21 @@ struct GemmKernel {
   // own, so each step hands the memory pipeline a few loads while its MFMAs
   // run (issued all at once, a stage's loads stall every wave behind the
   // address unit).
-  template <int NEXT_S, bool CONVERT, int AMB, int U0 = 0, int U1 = 0>
+  template <int NEXT_S, bool CONVERT, int AMB, int U0 = 0, int U1 = 0, int NBX = NB>
   __device__ __forceinline__ void step(f32x16 (&acc)[MB][NB], const Frags& use, Frags& fill, const Raw& src,
-                                       Scales& ssrc, const StageIssue* si = nullptr) const {
+                                       Scales& ssrc, uint32_t sel, const StageIssue* si = nullptr) const {
     if constexpr (U0 < U1) {
       dma_range<U0, U1>(*si);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (AMB == 0) return;
-    constexpr int VALU = (AMB + NB) * 8 + (CONVERT ? 2 * (AMB + NB) : 0);
-    constexpr int PER = (VALU + AMB * NB - 1) / (AMB * NB > 0 ? AMB * NB : 1);
-    if (CONVERT) convert_scales<AMB>(ssrc, src);
-    dequant<NEXT_S, AMB>(fill, src, ssrc);
-    mfmas<AMB>(acc, use);
+    constexpr int VALU = (AMB + NBX) * 8 + (CONVERT ? 2 * (AMB + NBX) : 0);
+    constexpr int PER = (VALU + AMB * NBX - 1) / (AMB * NBX > 0 ? AMB * NBX : 1);
+    if (CONVERT) convert_scales<AMB, NBX>(ssrc, src, sel);
+    dequant<NEXT_S, AMB, NBX>(fill, src, ssrc);
+    mfmas<AMB, NBX>(acc, use);
 #pragma unroll
-    for (int q = 0; q < AMB * NB; ++q) {
+    for (int q = 0; q < AMB * NBX; ++q) {
       __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedVALU, PER, 0);
     }
@@ -852,9 +884,9 @@ struct GemmKernel {
   // stages after g + 1 are exactly NS - 2 (plus the epilogue's stores, see
   // wait_next_stage). With KPAD, global stage kpad_g (or none, -1) is a
   // tile's last stage with a half-used scale atom in 64-K group kpad_grp.
-  template <int AMB>
+  template <int AMB, int NBX = NB>
   __device__ __forceinline__ void mainloop(f32x16 (&acc)[MB][NB], int n, int g0, Loader& ld, int kpad_g,
-                                           int kpad_grp, int pend) const {
+                                           int kpad_grp, int pend, const Bases& bs) const {
     // split of a stage's L loads over the four steps of a half stage
     constexpr int U1 = (L + 3) / 4, U2 = U1 + (L - U1 + 2) / 3, U3 = U2 + (L - U2 + 1) / 2;
     Raw r0, r1;
@@ -863,19 +895,19 @@ struct GemmKernel {
     wait_first_stage(pend);
     if (KPAD && g0 == kpad_g) zero_half_atom((uint32_t)g0 % NS, kpad_grp);
     block_sync();
-    read_half<AMB>(r0, (uint32_t)g0 % NS, 0);
-    convert_scales<AMB>(s0, r0);
-    dequant<0, AMB>(f0, r0, s0);
+    read_half<AMB, NBX>(r0, (uint32_t)g0 % NS, 0, bs);
+    convert_scales<AMB, NBX>(s0, r0, bs.sel);
+    dequant<0, AMB, NBX>(f0, r0, s0);
     for (int kt = 0; kt < n; ++kt) {
       const int g = g0 + kt;
       // ---- first half (K 0..63 of the stage): raw data in r0 ----
-      read_half<AMB>(r1, (uint32_t)g % NS, 1);
-      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, AMB + NB + 1 + (AMB + 1) / 2, 0);
-      step<1, false, AMB>(acc, f0, f1, r0, s0);
-      step<2, false, AMB>(acc, f1, f0, r0, s0);
-      step<3, false, AMB>(acc, f0, f1, r0, s0);
-      step<0, true, AMB>(acc, f1, f0, r1, s1);
-      pin<AMB>(f0, s1);
+      read_half<AMB, NBX>(r1, (uint32_t)g % NS, 1, bs);
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, AMB + NBX + 1 + (AMB + 1) / 2, 0);
+      step<1, false, AMB, 0, 0, NBX>(acc, f0, f1, r0, s0, bs.sel);
+      step<2, false, AMB, 0, 0, NBX>(acc, f1, f0, r0, s0, bs.sel);
+      step<3, false, AMB, 0, 0, NBX>(acc, f0, f1, r0, s0, bs.sel);
+      step<0, true, AMB, 0, 0, NBX>(acc, f1, f0, r1, s1, bs.sel);
+      pin<AMB, NBX>(f0, s1);
       // ---- second half: raw data in r1. Stage g+1 must have landed before its
       // first half is read; every wave is done with stage g's buffer here, so
       // stage g + NS can take it.
@@ -883,13 +915,13 @@ struct GemmKernel {
       if (KPAD && g + 1 == kpad_g) zero_half_atom((uint32_t)(g + 1) % NS, kpad_grp);
       block_sync();
       const StageIssue si = prep_issue(ld);
-      read_half<AMB>(r0, (uint32_t)(g + 1) % NS, 0);  // unused after the last stage
-      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, AMB + NB + 1 + (AMB + 1) / 2, 0);
-      step<1, false, AMB, 0, U1>(acc, f0, f1, r1, s1, &si);
-      step<2, false, AMB, U1, U2>(acc, f1, f0, r1, s1, &si);
-      step<3, false, AMB, U2, U3>(acc, f0, f1, r1, s1, &si);
-      step<0, true, AMB, U3, L>(acc, f1, f0, r0, s0, &si);
-      pin<AMB>(f0, s0);
+      read_half<AMB, NBX>(r0, (uint32_t)(g + 1) % NS, 0, bs);  // unused after the last stage
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, AMB + NBX + 1 + (AMB + 1) / 2, 0);
+      step<1, false, AMB, 0, U1, NBX>(acc, f0, f1, r1, s1, bs.sel, &si);
+      step<2, false, AMB, U1, U2, NBX>(acc, f1, f0, r1, s1, bs.sel, &si);
+      step<3, false, AMB, U2, U3, NBX>(acc, f0, f1, r1, s1, bs.sel, &si);
+      step<0, true, AMB, U3, L, NBX>(acc, f1, f0, r0, s0, bs.sel, &si);
+      pin<AMB, NBX>(f0, s0);
       advance(ld);
     }
   }
@@ -1091,14 +1123,30 @@ struct GemmKernel {
   __device__ __forceinline__ void mainloop_rows(f32x16 (&acc)[MB][NB], const TileCtx& t, int n, int g0,
                                                 Loader& ld, int kpad_g, int pend) const {
     static_assert(MB <= 4, "active-block dispatch covers MB <= 4");
+    if constexpr (kWide) {
+      if (wide(t)) {
+        mainloop<1, NBW>(acc, n, g0, ld, kpad_g, t.kpad_group, pend, wide_bases());
+        return;
+      }
+    }
+    const Bases bs = normal_bases();
     switch (active_blocks(t)) {
-      case 0: mainloop<0>(acc, n, g0, ld, kpad_g, t.kpad_group, pend); break;
-      case 1: mainloop<(MB >= 1 ? 1 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group, pend); break;
-      case 2: mainloop<(MB >= 2 ? 2 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group, pend); break;
-      case 3: mainloop<(MB >= 3 ? 3 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group, pend); break;
-      default: mainloop<MB>(acc, n, g0, ld, kpad_g, t.kpad_group, pend); break;
+      case 0: mainloop<0>(acc, n, g0, ld, kpad_g, t.kpad_group, pend, bs); break;
+      case 1: mainloop<(MB >= 1 ? 1 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group, pend, bs); break;
+      case 2: mainloop<(MB >= 2 ? 2 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group, pend, bs); break;
+      case 3: mainloop<(MB >= 3 ? 3 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group, pend, bs); break;
+      default: mainloop<MB>(acc, n, g0, ld, kpad_g, t.kpad_group, pend, bs); break;
     }
   }
+
+  // Tiles with at most 32 rows below m (a light group's only tile, or the
+  // last of a ragged one) leave one wave row idle in the (wm, wn) layout:
+  // there the four waves instead sit side by side along n, each on row
+  // block 0 and a quarter of the columns (NBW blocks), so that all of them
+  // do MFMAs. Whole-tile f16 kernels only (the stream-K fold and the MX
+  // mainloop keep the wave-tile layout of their accumulators).
+  static constexpr bool kWide = !Src::kCanSplit && !MX && NBW >= 1;
+  __device__ __forceinline__ bool wide(const TileCtx& t) const { return kWide && t.M - t.row0 <= 32; }
 
   // ---------------- output ----------------
   // fp32 -> fp16 (RNE), 16-byte stores masked to m and n. A lane holds runs
@@ -1135,6 +1183,12 @@ struct GemmKernel {
   // Returns true for an unmasked epilogue: every wave then issued exactly S
   // stores (see kPendStores).
   __device__ __forceinline__ bool epilogue(const f32x16 (&acc)[MB][NB], const TileCtx& t) const {
+    if constexpr (kWide) {
+      if (wide(t)) {
+        epilogue_wide(acc, t);
+        return false;
+      }
+    }
     // Tiles wholly inside m and n (all but the edges) store without masks,
     // i.e. without an exec-mask branch around every store.
     if (t.row0 + BM <= t.M && t.col0 + BN <= t.N) {
@@ -1143,6 +1197,32 @@ struct GemmKernel {
     }
     epilogue_impl<true>(acc, t);
     return false;
+  }
+
+  // The wide layout's output: block j of a wave is columns
+  // wave * WIDE_COLS + 32 j .. +31 of the tile's first 32 rows.
+  __device__ __forceinline__ void epilogue_wide(const f32x16 (&acc)[MB][NB], const TileCtx& t) const {
+    int lro = lr, h8 = h * 8;
+    asm volatile("" : "+v"(lro), "+v"(h8));
+    const int col0 = t.col0 + wave * WIDE_COLS;
+    typedef __attribute__((address_space(1))) uint16_t gu16;
+    gu16* crow = (gu16*)t.c + (size_t)(t.row0 + lro) * t.N + col0 + h8;
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        float a[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = acc_read(acc[0][j][8 * p + e]);
+        const auto s0 = __builtin_amdgcn_permlane32_swap(pack_f16(a[0], a[1]), pack_f16(a[4], a[5]), false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(pack_f16(a[2], a[3]), pack_f16(a[6], a[7]), false, false);
+        const int cu = j * 32 + 2 * p * 8;
+        if (lro < t.M - t.row0 && h8 < t.N - col0 - cu) {
+          const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+          *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(crow + cu) = v;
+        }
+      }
+    }
   }
 
   template <bool MASKED>

@@ -452,3 +452,33 @@ def test_three_stage_pipeline_half_atom_k():
             for a, b, r in zip(*outs, ref):
                 assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), (cfg, split)
                 assert not O.tolerance_violations(b, r["c16"], r["s"]).any()
+
+
+def test_one_row_block_tiles_every_config():
+    """Tiles with at most 32 rows below m (the whole-tile kernels then put
+    the four waves side by side along n on that one row block): against the
+    oracle, and bitwise against the three-stage kernels, which keep the
+    two-by-two wave layout for every tile. m tails of 1 .. 32 rows on every
+    tile height, n tails that leave some waves' columns wholly past n, and a
+    half-used last scale atom."""
+    shapes = [(1, 136, 384, 1), (17, 264, 256, 1), (32, 512, 384, 1), (133, 40, 384, 1), (160, 328, 256, 2),
+              (280, 264, 384, 1), (288, 72, 96, 1), (257, 520, 160, 1)]
+    groups = poison_padding(shapes, synth.make_custom(shapes, seed=4141))
+    d = dev.upload(shapes, groups, c_guard=GUARD)
+    abc, sf = dev.pointer_tables(d)
+    ws = dev.workspace_for(shapes)
+    ref = O.grouped_gemm(shapes, groups)
+    for cfg in range(mm.nvfp4_num_tile_configs()):
+        outs = []
+        for stages in (4, 3):
+            announce(f"one-row-block tiles cfg {cfg} stages {stages}")
+            for dd in d:
+                dd["c"].fill_(-1)
+            mm.nvfp4_grouped_gemm_stages(shapes, abc, sf, len(shapes), ws.data_ptr(), ws.numel(), cfg, 0,
+                                         stages, torch.cuda.current_stream())
+            torch.cuda.synchronize()
+            assert dev.guards_intact(d), "store outside C"
+            outs.append([c.copy() for c in dev.c_as_numpy(shapes, d)])
+        for shape, a, b, r in zip(shapes, *outs, ref):
+            assert not O.tolerance_violations(a, r["c16"], r["s"]).any(), (cfg, shape)
+            assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), (cfg, shape)
