@@ -1776,22 +1776,12 @@ struct WorkClass {
   double fill;    // share of a full tile's row blocks that hold rows below m (sizes its stream-K partial)
 };
 
-// The work classes of a call for tile configuration cfg, heaviest per tile
-// first (stable: groups keep their order among equals). Returns the count.
 double tile_overhead_stages() { return 1.5; }  // epilogue and pipeline fill per tile
 
+// The work classes of a call for tile configuration cfg, heaviest per tile
+// first (stable: groups keep their order among equals). Returns the count.
 int build_classes(const int32_t* ps, int G, int cfg, WorkClass* out);
 
-// Stream-K after `rounds` whole rounds: the first rounds * grid tiles (in
-// class order) are dealt out whole by the kernel's snake walk; the units of
-// the remaining tiles are cut into ranges[w] .. ranges[w + 1] for workgroup
-// w (contiguous in workgroup order, possibly empty) so that every
-// workgroup's modelled cost, its whole tiles included, comes out equal (the
-// remaining cost is water-filled over the workgroups' whole-tile loads). A
-// unit of class c costs cls[c].cost / nk. pub and fold are the modelled costs
-// of storing and of folding one full-sized partial tile; a partial's size
-// scales with its class's fill. Returns the modelled makespan in full
-// tile-stages. Needs 1 <= grid <= kMaxSplitGrid and rounds * grid <= tiles.
 // Modelled stream-K costs, in full tile-stages of the configuration, for a
 // partial of fill f (its share of a full tile's row blocks): storing it
 // (device-scope stores, then a wait for them) and folding a tile with C
