@@ -30,7 +30,8 @@
 //  * v_mfma_f32_32x32x16_f16 with B as the first operand, so each lane ends up
 //    holding four consecutive columns of one output row. A wave skips the
 //    LDS reads, dequantisation and MFMAs of its 32-row blocks that lie wholly
-//    past m (ragged M of the expert groups).
+//    past m (ragged M of the expert groups); in a tile with a single row
+//    block below m the four waves sit side by side along n instead.
 //  * Inside each 64-K group the K order fed to the MFMA is permuted so that a
 //    lane reads 32 consecutive FP4 codes (16 bytes) of its row: lane half h
 //    takes K elements [32h, 32h+32) in four steps of 8. A and B use the same
@@ -38,8 +39,10 @@
 //    16-block, so one scale covers it.
 //  * Epilogue: fp32 -> fp16 (RNE) fused; a lane-half swap gives each lane 8
 //    consecutive columns, stored as 16 bytes, masked to m and n.
-//    Tiles split by stream-K store fp32 partials; a second kernel adds them in
-//    a fixed order and writes fp16.
+//    Tiles split by stream-K store fp32 partials, and their contributors fold
+//    them in the same kernel along a fixed binary tree (the second to arrive
+//    at a node adds; no workgroup waits for another), so results do not
+//    depend on timing.
 //  * Scales that are all zero or powers of two (an MX-compatible special case
 //    of the pages' MX/NV FP4 block-scaled MMA) have their own mainloop: the
 //    packed codes go to v_mfma_scale_f32_32x32x64_f8f6f4 as E2M1 with E8M0
