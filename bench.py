@@ -33,6 +33,8 @@ PEAK_F16_TFLOPS = 2500.0  # MI355X dense f16/bf16 MFMA (published)
 PEAK_FP4_TFLOPS = 10100.0  # MI355X dense fp4 MFMA (published)
 PEAK_HBM_GBS = 8000.0
 COLD_BYTES = 1 << 30
+# Per-workload rows time at least this much back-to-back work (see time_workload).
+PER_CONFIG_MIN_TIMED_MS = 2.0
 
 
 def log(*a):
@@ -86,16 +88,19 @@ def settle(call, seconds):
 
 
 def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None, device_tables=False,
-                  super_batch=False, pow2=False, settle_s=0.0, from_idle=False):
+                  super_batch=False, pow2=False, settle_s=0.0, from_idle=False, min_timed_ms=0.0):
     """Times the grouped GEMM on workload ``idx``. ``device_tables``: through
     nvfp4_grouped_gemm_device (group tables in device memory); ``super_batch``:
     the groups of 15 calls of the workload in one launch (device tables);
     ``pow2``: the workload with power-of-two scales through
     nvfp4_grouped_gemm_pow2 (its status word checked afterwards).
     ``settle_s``: seconds of back-to-back calls before the warm-up steps (see
-    settle). ``from_idle``: also time ``steps`` calls after only the warm-up
-    steps, straight after the input set-up (before the settle), as a run
-    without the settle would."""
+    settle). ``min_timed_ms``: time at least that much work, more than
+    ``steps`` calls if need be (the per-call time is estimated from the
+    settle): 20 calls of a few microseconds are a window of the same order as
+    the latencies around it. ``from_idle``: also time ``steps`` calls after
+    only the warm-up steps, straight after the input set-up (before the
+    settle), as a run without the settle would."""
     import torch
 
     import moe_matmul_amd as mm
@@ -160,6 +165,10 @@ def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None
     settle_t0 = time.perf_counter()
     settle_calls = settle(call, settle_s)
     settle_wall = time.perf_counter() - settle_t0
+    timed_steps = steps
+    if min_timed_ms > 0 and settle_calls > 0:
+        per_call_s = settle_wall / settle_calls
+        timed_steps = min(max(steps, -(-int(min_timed_ms * 1e-3 * 1e6) // max(int(per_call_s * 1e6), 1))), 5000)
     for i in range(warmup):
         call(i)
     torch.cuda.synchronize()
@@ -168,7 +177,7 @@ def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
-    for i in range(steps):
+    for i in range(timed_steps):
         call(i)
     end.record(stream)
     torch.cuda.synchronize()
@@ -197,7 +206,7 @@ def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None
     else:
         # without a workspace (split_mode None: nvfp4_grouped_gemm_config) the library plans whole tiles
         geo = mm.nvfp4_launch_geometry(shapes, cus, tile_config, 0 if split_mode is None else split_mode)
-    avg_s = total_ms / steps / 1e3
+    avg_s = total_ms / timed_steps / 1e3
     # The same calls replayed from a captured HIP graph: GPU time per call
     # without host launch overhead (what matters for the microsecond-sized
     # workloads).
@@ -243,7 +252,7 @@ def time_workload(idx, steps, warmup, tile_config=-1, cold=True, split_mode=None
             raise RuntimeError(f"{name}: the power-of-two entry point reported a scale outside its set")
     return dict(
         workload=name, device_tables=device_tables, pow2=pow2, shapes=[list(s) for s in shapes], flops=flops, bytes=nbytes,
-        total_ms=total_ms, wall_s=wall, ms_per_call=total_ms / steps,
+        total_ms=total_ms, wall_s=wall, ms_per_call=total_ms / timed_steps, timed_steps=timed_steps,
         us_median=percentile(per_call, 50) * 1e3, us_p10=percentile(per_call, 10) * 1e3, us_p90=percentile(per_call, 90) * 1e3,
         tflops=flops / avg_s / 1e12, gbs=nbytes / avg_s / 1e9, sets=len(sets), tile_config=geo["config"],
         tiles=geo["total_tiles"], grid=geo["grid"], split=geo["split"], graph_us_per_call=graph_us,
@@ -263,6 +272,7 @@ def config_row(idx, r):
         "workload": r["workload"], "index": idx, "shapes_mnkl": r["shapes"],
         "us_per_call": {"timed_mean": round(r["ms_per_call"] * 1e3, 2), "median": round(r["us_median"], 2),
                         "graph_replay": None if r["graph_us_per_call"] is None else round(r["graph_us_per_call"], 2)},
+        "timed_calls": r["timed_steps"],
         "tflops": round(r["tflops"], 2), "algorithmic_gbs": round(r["gbs"], 1),
         "roofline": {"bound": bound, "frac": round(max(t_mfma, t_hbm) / t, 4),
                      "mfma_frac": round(t_mfma / t, 4), "hbm_frac": round(t_hbm / t, 4),
@@ -463,9 +473,11 @@ def main():
             if i == args.workload:
                 r = head
             else:
-                r = time_workload(i, args.steps, args.warmup, -1, cold=True, settle_s=args.settle)
+                r = time_workload(i, args.steps, args.warmup, -1, cold=True, settle_s=args.settle,
+                                  min_timed_ms=PER_CONFIG_MIN_TIMED_MS)
             rows.append(config_row(i, r))
-            log(f"[bench] workload {i} {r['workload']}: {r['ms_per_call'] * 1e3:.2f} us/call (median "
+            log(f"[bench] workload {i} {r['workload']}: {r['ms_per_call'] * 1e3:.2f} us/call over "
+                f"{r['timed_steps']} calls (median "
                 f"{r['us_median']:.2f}, graph replay {fmt_us(r['graph_us_per_call'])}), {r['tflops']:.1f} TFLOP/s, "
                 f"{rows[-1]['roofline']['bound']}-bound, frac {rows[-1]['roofline']['frac']:.3f}")
         details["per_config"] = rows
