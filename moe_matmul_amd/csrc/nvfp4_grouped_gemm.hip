@@ -385,7 +385,13 @@ struct GemmKernel {
   static_assert((NS - 1) * L + S < 64, "vmcnt range (counted waits across the epilogue's stores)");
   static constexpr int DUMMY_OFF = NS * STAGE_BYTES;
   static constexpr int FLAG_OFF = DUMMY_OFF + 1024;  // stream-K: a tile's arrival count, shared by the waves
-  static constexpr int LDS_BYTES = NS * STAGE_BYTES + 1024 + 16;
+  // Light tiles of the whole-tile 256x128 kernels split K over the waves
+  // (mainloop_ks) and add the partials through 16 LDS slots of 64 lanes x 8
+  // floats after the stages.
+  static constexpr bool kKS = !Src::kCanSplit && !MX && BM == 256 && BN == 128 && WM == 128 && WN == 64;
+  static constexpr int EX_OFF = FLAG_OFF + 16;
+  static constexpr int EX_BYTES = kKS ? 16 * 2048 : 0;
+  static constexpr int LDS_BYTES = NS * STAGE_BYTES + 1024 + 16 + EX_BYTES;
   static_assert(NS >= 3 && NS <= 4 && LDS_BYTES <= 160 * 1024, "LDS stages");
   static_assert((NS - 2) * L < 64, "vmcnt range");
 
@@ -929,6 +935,241 @@ struct GemmKernel {
     }
   }
 
+  // ---------------- light tiles of the 256x128 kernel: the waves split K ----------------
+  // A tile with at most four 32-row blocks below m (at most 128 of its 256
+  // rows) would leave the two-by-two layout dequantising every B fragment
+  // twice for few rows. Here the four waves split the K range instead: with
+  // KS = 4 (one or two row blocks) wave w takes two of the eight 16-K
+  // substeps of every stage (half w / 2, substeps 2 (w % 2) and 2 (w % 2) + 1)
+  // for all rows and all 128 columns; with KS = 2 (three or four row blocks)
+  // wave w takes half w % 2 of every stage for the 64 columns w / 2. Each
+  // wave dequantises its fragments for a quarter of the substeps, 80-192 VALU
+  // per stage against 128-256 in the layouts above. At the end of the tile the
+  // KS partial sums of each output block are added through LDS, in the order
+  // of their K parts, so the result is deterministic; wave w then stores the
+  // 32 columns 32 w .. 32 w + 31. The accumulator array holds the partials:
+  // block (i, j) (row block i, the wave's column block j) is
+  // acc[ks_ai(i, j)][ks_aj(i, j)].
+  template <int KS>
+  __device__ __forceinline__ static constexpr int ks_ai(int i, int j) { return KS == 4 ? 2 * i + (j >> 1) : i; }
+  template <int KS>
+  __device__ __forceinline__ static constexpr int ks_aj(int i, int j) { return KS == 4 ? (j & 1) : j; }
+  __device__ __forceinline__ bool ks_tile(const TileCtx& t) const { return kKS && t.M - t.row0 <= 128; }
+
+  // A wave's operands for its P substeps of a stage: P dwords of each of its
+  // R A chunks and NBK B chunks, and the scale words.
+  template <int R, int NBK, int P>
+  struct KsRaw {
+    typedef uint32_t chunk __attribute__((ext_vector_type(P)));
+    chunk a[R];
+    chunk b[NBK];
+    uint32_t sa[R];
+    uint32_t sb[NBK];
+  };
+  template <int R, int NBK>
+  struct KsScales {
+    f16x2 a[R];
+    f16x2 b[NBK];
+  };
+  template <int R, int NBK>
+  struct KsFrags {
+    f16x8 a[R];
+    f16x8 b[NBK];
+  };
+  // Per-lane LDS offsets of a wave's first A and B chunk (8 bytes into the
+  // chunk for the second substep pair of KS = 4), of the A scale chunk (row
+  // block i: word i) and of its B scale words, inside a stage; and the shift
+  // that brings the lane's scale bytes (two 16-blocks, or the one of KS = 4)
+  // to the bottom of a scale word.
+  struct KsBases {
+    int a, b, sa, sb, shift;
+  };
+  template <int KS>
+  __device__ __forceinline__ KsBases ks_bases() const {
+    const int kpart = wave % KS, npart = wave / KS;
+    const int kk = KS == 2 ? kpart : kpart >> 1;
+    const int sub = KS == 4 ? (kpart & 1) : 0;
+    const int c0 = npart * (BN * KS / 4);
+    KsBases b;
+    b.a = lds_off(lr, kk * 2 + h) + sub * 8;
+    b.b = A_BYTES + lds_off(c0 + lr, kk * 2 + h) + sub * 8;
+    b.sa = A_BYTES + B_BYTES + lr * 16 + kk * 512;
+    b.sb = A_BYTES + B_BYTES + (A_ATOMS + (c0 >> 7)) * 1024 + lr * 16 + ((c0 & 127) >> 5) * 4 + kk * 512;
+    b.shift = h * 16 + sub * 8;
+    return b;
+  }
+  template <int R, int NBK, int P>
+  __device__ __forceinline__ void ks_read(KsRaw<R, NBK, P>& r, int buf, const KsBases& bs) const {
+    typedef typename KsRaw<R, NBK, P>::chunk chunk;
+    const uint8_t* St = smem + buf * STAGE_BYTES;
+#pragma unroll
+    for (int i = 0; i < R; ++i) r.a[i] = *reinterpret_cast<const chunk*>(St + bs.a + i * 32 * kRowBytes);
+#pragma unroll
+    for (int j = 0; j < NBK; ++j) r.b[j] = *reinterpret_cast<const chunk*>(St + bs.b + j * 32 * kRowBytes);
+    const u32x4 ca = *reinterpret_cast<const u32x4*>(St + bs.sa);
+#pragma unroll
+    for (int i = 0; i < R; ++i) r.sa[i] = ca[i];
+    const ScaleVec<NBK> cb = *reinterpret_cast<const ScaleVec<NBK>*>(St + bs.sb);
+#pragma unroll
+    for (int j = 0; j < NBK; ++j) r.sb[j] = cb[j];
+  }
+  template <int R, int NBK, int P>
+  __device__ __forceinline__ static void ks_convert(KsScales<R, NBK>& s, const KsRaw<R, NBK, P>& r, int shift) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) s.a[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sa[i] >> shift, 1.0f, false);
+#pragma unroll
+    for (int j = 0; j < NBK; ++j) s.b[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sb[j] >> shift, 1.0f, false);
+  }
+  // Substep PS of the wave's P: dword PS of each chunk, under the scale of its
+  // 16-block (P = 2: the wave's one 16-block).
+  template <int PS, int R, int NBK, int P>
+  __device__ __forceinline__ static void ks_dequant(KsFrags<R, NBK>& f, const KsRaw<R, NBK, P>& r,
+                                                    const KsScales<R, NBK>& s) {
+    constexpr int SI = P == 4 ? (PS >> 1) : 0;
+#pragma unroll
+    for (int i = 0; i < R; ++i) f.a[i] = dequant8(r.a[i][PS], s.a[i][SI]);
+#pragma unroll
+    for (int j = 0; j < NBK; ++j) f.b[j] = dequant8(r.b[j][PS], s.b[j][SI]);
+  }
+  template <int KS, int R, int NBK>
+  __device__ __forceinline__ static void ks_mfmas(f32x16 (&acc)[MB][NB], const KsFrags<R, NBK>& f) {
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int j = 0; j < NBK; ++j) {
+        f32x16& c = acc[ks_ai<KS>(i, j)][ks_aj<KS>(i, j)];
+        c = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[j], f.a[i], c, 0, 0, 0);
+      }
+  }
+  template <int R, int NBK>
+  __device__ __forceinline__ static void ks_pin(const KsFrags<R, NBK>& f, const KsScales<R, NBK>& s) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) asm volatile("" ::"v"(f.a[i]), "v"(s.a[i]));
+#pragma unroll
+    for (int j = 0; j < NBK; ++j) asm volatile("" ::"v"(f.b[j]), "v"(s.b[j]));
+  }
+  // One substep (as step): the MFMAs of `use` with the dequantisation of the
+  // wave's substep NEXT of `src` into `fill` (and, with CONVERT, first the
+  // conversion of src's scales), after direct loads U0 .. U1-1.
+  template <int KS, int NEXT, bool CONVERT, int U0, int U1, int R, int NBK, int P>
+  __device__ __forceinline__ void ks_step(f32x16 (&acc)[MB][NB], const KsFrags<R, NBK>& use, KsFrags<R, NBK>& fill,
+                                          const KsRaw<R, NBK, P>& src, KsScales<R, NBK>& ssrc, int shift,
+                                          const StageIssue* si) const {
+    if constexpr (U0 < U1) {
+      dma_range<U0, U1>(*si);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    constexpr int VALU = (R + NBK) * 8 + (CONVERT ? 2 * (R + NBK) : 0);
+    constexpr int PER = (VALU + R * NBK - 1) / (R * NBK);
+    if (CONVERT) ks_convert(ssrc, src, shift);
+    ks_dequant<NEXT>(fill, src, ssrc);
+    ks_mfmas<KS>(acc, use);
+#pragma unroll
+    for (int q = 0; q < R * NBK; ++q) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedVALU, PER, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Stage g of a segment (iteration kt) from the raw operands r, whose
+  // substep 0 is dequantised in f0. All but the last of the wave's substeps
+  // run before the mid-stage barrier, so r is free by then and takes stage
+  // g + 1 (no second register set, no copies); the last substep's MFMAs then
+  // cover the reads, the stage's direct loads and stage g + 1's first
+  // dequantisation into f0. The same waits, barrier and loads per stage as
+  // mainloop.
+  template <int KS, int R, int NBK, int P>
+  __device__ __forceinline__ void ks_stage(f32x16 (&acc)[MB][NB], KsRaw<R, NBK, P>& r, KsScales<R, NBK>& s,
+                                           KsFrags<R, NBK>& f0, KsFrags<R, NBK>& f1, const KsBases& bs, int g, int kt,
+                                           Loader& ld, int kpad_g, int kpad_grp, int pend) const {
+    constexpr int DS = R + NBK + 2;  // LDS reads of a stage
+    if constexpr (P == 4) {
+      ks_step<KS, 1, false, 0, 0>(acc, f0, f1, r, s, bs.shift, nullptr);
+      ks_step<KS, 2, false, 0, 0>(acc, f1, f0, r, s, bs.shift, nullptr);
+      ks_step<KS, 3, false, 0, 0>(acc, f0, f1, r, s, bs.shift, nullptr);
+    } else {
+      ks_step<KS, 1, false, 0, 0>(acc, f0, f1, r, s, bs.shift, nullptr);
+    }
+    ks_pin(f1, s);
+    wait_next_stage(pend, kt);
+    if (KPAD && g + 1 == kpad_g) zero_half_atom((uint32_t)(g + 1) % NS, kpad_grp);
+    block_sync();
+    const StageIssue si = prep_issue(ld);
+    ks_read(r, (uint32_t)(g + 1) % NS, bs);  // unused after the last stage
+    __builtin_amdgcn_sched_group_barrier(kSchedDSRead, DS, 0);
+    ks_step<KS, 0, true, 0, L>(acc, f1, f0, r, s, bs.shift, &si);
+    ks_pin(f0, s);
+    advance(ld);
+  }
+  // n stages of a light tile's segment (as mainloop), R row blocks below m.
+  template <int R, int KS>
+  __device__ __forceinline__ void mainloop_ks(f32x16 (&acc)[MB][NB], int n, int g0, Loader& ld, int kpad_g,
+                                              int kpad_grp, int pend) const {
+    constexpr int NBK = BN * KS / 4 / 32, P = 8 / KS;
+    const KsBases bs = ks_bases<KS>();
+    KsRaw<R, NBK, P> r;
+    KsScales<R, NBK> s;
+    KsFrags<R, NBK> f0, f1;
+    wait_first_stage(pend);
+    if (KPAD && g0 == kpad_g) zero_half_atom((uint32_t)g0 % NS, kpad_grp);
+    block_sync();
+    ks_read(r, (uint32_t)g0 % NS, bs);
+    ks_convert(s, r, bs.shift);
+    ks_dequant<0>(f0, r, s);
+    for (int kt = 0; kt < n; ++kt) ks_stage<KS>(acc, r, s, f0, f1, bs, g0 + kt, kt, ld, kpad_g, kpad_grp, pend);
+  }
+
+  // The end of a light tile: for each row block i and each half p of the
+  // lane's 16 accumulator elements (one 16-column store run pair), every wave
+  // writes its partials into LDS slot (o, kp) - o the wave that stores the
+  // block, kp the writer's K part - and after a barrier each wave adds the KS
+  // partials of its own block in K-part order and stores them. Two barriers
+  // per round; the slots lie past the stages (which already hold the next
+  // tile's loads).
+  template <int R, int KS>
+  __device__ __forceinline__ void epilogue_ks(const f32x16 (&acc)[MB][NB], const TileCtx& t) const {
+    constexpr int NBK = BN * KS / 4 / 32;
+    const int kpart = wave % KS, npart = wave / KS;
+    int lro = lr, h8 = h * 8;
+    asm volatile("" : "+v"(lro), "+v"(h8));
+    const int col0 = t.col0 + wave * 32;  // this wave's 32 output columns
+    typedef __attribute__((address_space(1))) uint16_t gu16;
+    gu16* crow = (gu16*)t.c + (size_t)(t.row0 + lro) * t.N + col0 + h8;
+    // slot (o, kp) holds 2 x 64 lanes x 16 bytes at EX_OFF + (o * 4 + kp) * 2048
+    f32x4* wr = reinterpret_cast<f32x4*>(smem + EX_OFF) + ((npart * NBK) * 4 + kpart) * 128 + lane;
+    const f32x4* rd = reinterpret_cast<const f32x4*>(smem + EX_OFF) + wave * 4 * 128 + lane;
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        // the wave's local column block j is stored by wave npart * NBK + j
+#pragma unroll
+        for (int j = 0; j < NBK; ++j) {
+          const f32x16& c = acc[ks_ai<KS>(i, j)][ks_aj<KS>(i, j)];
+          wr[j * 4 * 128] = f32x4{c[8 * p + 0], c[8 * p + 1], c[8 * p + 2], c[8 * p + 3]};
+          wr[j * 4 * 128 + 64] = f32x4{c[8 * p + 4], c[8 * p + 5], c[8 * p + 6], c[8 * p + 7]};
+        }
+        block_sync();
+        f32x4 sum0 = rd[0], sum1 = rd[64];
+#pragma unroll
+        for (int kp = 1; kp < KS; ++kp) {
+          sum0 += rd[kp * 128];
+          sum1 += rd[kp * 128 + 64];
+        }
+        const auto s0 = __builtin_amdgcn_permlane32_swap(pack_f16(sum0[0], sum0[1]), pack_f16(sum1[0], sum1[1]), false,
+                                                         false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(pack_f16(sum0[2], sum0[3]), pack_f16(sum1[2], sum1[3]), false,
+                                                         false);
+        const int cu = 2 * p * 8;
+        if (lro < t.M - t.row0 - i * 32 && h8 < t.N - col0 - cu) {
+          const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+          *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(crow + (size_t)i * 32 * t.N + cu) = v;
+        }
+        block_sync();  // the slots are rewritten next round
+      }
+    }
+  }
+
   // ---------------- power-of-two scales: FP4 MFMA with E8M0 scales ----------------
   // v_mfma_scale_f32_32x32x64_f8f6f4 with E2M1 operands: lane l of an operand
   // holds 32 codes (four dwords, low nibble first) of row l % 32 at K
@@ -1126,6 +1367,17 @@ struct GemmKernel {
   __device__ __forceinline__ void mainloop_rows(f32x16 (&acc)[MB][NB], const TileCtx& t, int n, int g0,
                                                 Loader& ld, int kpad_g, int pend) const {
     static_assert(MB <= 4, "active-block dispatch covers MB <= 4");
+    if constexpr (kKS) {
+      if (ks_tile(t)) {
+        switch ((t.M - t.row0 + 31) >> 5) {
+          case 1: mainloop_ks<1, 4>(acc, n, g0, ld, kpad_g, t.kpad_group, pend); break;
+          case 2: mainloop_ks<2, 4>(acc, n, g0, ld, kpad_g, t.kpad_group, pend); break;
+          case 3: mainloop_ks<3, 2>(acc, n, g0, ld, kpad_g, t.kpad_group, pend); break;
+          default: mainloop_ks<4, 2>(acc, n, g0, ld, kpad_g, t.kpad_group, pend); break;
+        }
+        return;
+      }
+    }
     if constexpr (kWide) {
       if (wide(t)) {
         mainloop<1, NBW>(acc, n, g0, ld, kpad_g, t.kpad_group, pend, wide_bases());
@@ -1148,7 +1400,7 @@ struct GemmKernel {
   // block 0 and a quarter of the columns (NBW blocks), so that all of them
   // do MFMAs. Whole-tile f16 kernels only (the stream-K fold and the MX
   // mainloop keep the wave-tile layout of their accumulators).
-  static constexpr bool kWide = !Src::kCanSplit && !MX && NBW >= 1;
+  static constexpr bool kWide = !Src::kCanSplit && !MX && NBW >= 1 && !kKS;
   __device__ __forceinline__ bool wide(const TileCtx& t) const { return kWide && t.M - t.row0 <= 32; }
 
   // ---------------- output ----------------
@@ -1186,6 +1438,17 @@ struct GemmKernel {
   // Returns true for an unmasked epilogue: every wave then issued exactly S
   // stores (see kPendStores).
   __device__ __forceinline__ bool epilogue(const f32x16 (&acc)[MB][NB], const TileCtx& t) const {
+    if constexpr (kKS) {
+      if (ks_tile(t)) {
+        switch ((t.M - t.row0 + 31) >> 5) {
+          case 1: epilogue_ks<1, 4>(acc, t); break;
+          case 2: epilogue_ks<2, 4>(acc, t); break;
+          case 3: epilogue_ks<3, 2>(acc, t); break;
+          default: epilogue_ks<4, 2>(acc, t); break;
+        }
+        return false;
+      }
+    }
     if constexpr (kWide) {
       if (wide(t)) {
         epilogue_wide(acc, t);
@@ -1678,11 +1941,10 @@ struct TileConfig {
   void (*kernel[2][2][2])(KernelArgs);
   void (*device_kernel)(DeviceGroupArgs);
   int64_t (*device_tiles)(const int32_t*, const uint64_t*);  // the device kernel's per-group check
-  // The same computation with a three-stage LDS pipeline (any k, whole tiles
-  // or stream-K), for verification: each LDS buffer is then rewritten one
-  // stage sooner after its last reads, so a missing wait or barrier shows up
-  // as a difference.
-  void (*kernel_ns3)(KernelArgs);
+  // The same computation with a three-stage LDS pipeline (any k; [stream-K]),
+  // for verification: each LDS buffer is then rewritten one stage sooner after
+  // its last reads, so a missing wait or barrier shows up as a difference.
+  void (*kernel_ns3[2])(KernelArgs);
 };
 
 constexpr int kStages = 4;  // LDS pipeline depth (4 x 36 KiB for 256x256 tiles)
@@ -1695,7 +1957,8 @@ constexpr int kStages = 4;  // LDS pipeline depth (4 x 36 KiB for 256x256 tiles)
      {{NVFP4_KERNEL(bm, bn, wm, wn, false, false, true), NVFP4_KERNEL(bm, bn, wm, wn, true, false, true)},     \
       {NVFP4_KERNEL(bm, bn, wm, wn, false, true, true), NVFP4_KERNEL(bm, bn, wm, wn, true, true, true)}}},     \
     nvfp4_grouped_gemm_device_kernel<bm, bn, wm, wn, kStages>, device_group_tiles<bm, bn>,                     \
-    nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, 3, true, false, true> }
+    {nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, 3, true, false, false>,                                       \
+     nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, 3, true, false, true>} }
 const TileConfig kConfigs[] = {
     NVFP4_TILE_CONFIG(256, 256, 128, 128),
     NVFP4_TILE_CONFIG(128, 256, 64, 128),
@@ -2171,7 +2434,7 @@ int launch(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, vo
   bool kpad = false;
   for (int g = 0; g < G; ++g) kpad = kpad || (ps[4 * g + 2] % 64 != 0);
   void (*kernel)(KernelArgs) = tc.kernel[plan.split ? 1 : 0][mx_status ? 1 : 0][kpad ? 1 : 0];
-  if (stages == 3) kernel = tc.kernel_ns3;
+  if (stages == 3) kernel = tc.kernel_ns3[plan.split ? 1 : 0];
   if (plan.split) {
     int32_t* counters = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) +
                                                    partial_bytes_for(plan.cfg, plan.grid));
