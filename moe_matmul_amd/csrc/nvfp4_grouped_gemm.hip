@@ -352,7 +352,7 @@ struct DeviceSrc {
 // calls without such groups use the one without. MX: the mainloop for scales
 // that are all zero or positive powers of two (FP4 MFMA with E8M0 scales, no
 // dequantisation).
-template <int BM, int BN, int WM, int WN, int NS, class Src, bool KPAD = false, bool MX = false>
+template <int BM, int BN, int WM, int WN, int NS, class Src, bool KPAD = false, bool MX = false, bool KS2R_ALL = false>
 struct GemmKernel {
   static constexpr int MB = WM / 32;
   static constexpr int NB = WN / 32;
@@ -385,12 +385,17 @@ struct GemmKernel {
   static_assert((NS - 1) * L + S < 64, "vmcnt range (counted waits across the epilogue's stores)");
   static constexpr int DUMMY_OFF = NS * STAGE_BYTES;
   static constexpr int FLAG_OFF = DUMMY_OFF + 1024;  // stream-K: a tile's arrival count, shared by the waves
-  // Light tiles of the whole-tile 256x128 kernels split K over the waves
-  // (mainloop_ks) and add the partials through 16 LDS slots of 64 lanes x 8
-  // floats after the stages.
+  // The whole-tile f16 256x128 kernels split K over the waves (mainloop_ks)
+  // and add the partials through 16 LDS slots of 64 lanes x 8 floats after
+  // the stages; their accumulators are 4 x 4 blocks (128x128 per wave at most).
   static constexpr bool kKS = !Src::kCanSplit && !MX && BM == 256 && BN == 128 && WM == 128 && WN == 64;
   static constexpr int EX_OFF = FLAG_OFF + 16;
   static constexpr int EX_BYTES = kKS ? 16 * 2048 : 0;
+  // KS2R_ALL: every tile in a K-split mode (fuller ones in KS2R, 128x128
+  // wave tiles: 4 x 4 accumulator blocks); else only tiles of at most four row
+  // blocks, and 4 x 2 accumulator blocks as in the two-by-two layout.
+  static constexpr bool kKS2R = kKS && KS2R_ALL;
+  static constexpr int ACC_M = kKS ? 4 : MB, ACC_N = kKS2R ? 4 : NB;
   static constexpr int LDS_BYTES = NS * STAGE_BYTES + 1024 + 16 + EX_BYTES;
   static_assert(NS >= 3 && NS <= 4 && LDS_BYTES <= 160 * 1024, "LDS stages");
   static_assert((NS - 2) * L < 64, "vmcnt range");
@@ -791,7 +796,7 @@ struct GemmKernel {
   }
 
   template <int AMB, int NBX = NB>
-  __device__ __forceinline__ static void mfmas(f32x16 (&acc)[MB][NB], const Frags& f) {
+  __device__ __forceinline__ static void mfmas(f32x16 (&acc)[ACC_M][ACC_N], const Frags& f) {
 #pragma unroll
     for (int i = 0; i < AMB; ++i)
 #pragma unroll
@@ -819,7 +824,7 @@ struct GemmKernel {
   // run (issued all at once, a stage's loads stall every wave behind the
   // address unit).
   template <int NEXT_S, bool CONVERT, int AMB, int U0 = 0, int U1 = 0, int NBX = NB>
-  __device__ __forceinline__ void step(f32x16 (&acc)[MB][NB], const Frags& use, Frags& fill, const Raw& src,
+  __device__ __forceinline__ void step(f32x16 (&acc)[ACC_M][ACC_N], const Frags& use, Frags& fill, const Raw& src,
                                        Scales& ssrc, uint32_t sel, const StageIssue* si = nullptr) const {
     if constexpr (U0 < U1) {
       dma_range<U0, U1>(*si);
@@ -894,7 +899,7 @@ struct GemmKernel {
   // wait_next_stage). With KPAD, global stage kpad_g (or none, -1) is a
   // tile's last stage with a half-used scale atom in 64-K group kpad_grp.
   template <int AMB, int NBX = NB>
-  __device__ __forceinline__ void mainloop(f32x16 (&acc)[MB][NB], int n, int g0, Loader& ld, int kpad_g,
+  __device__ __forceinline__ void mainloop(f32x16 (&acc)[ACC_M][ACC_N], int n, int g0, Loader& ld, int kpad_g,
                                            int kpad_grp, int pend, const Bases& bs) const {
     // split of a stage's L loads over the four steps of a half stage
     constexpr int U1 = (L + 3) / 4, U2 = U1 + (L - U1 + 2) / 3, U3 = U2 + (L - U2 + 1) / 2;
@@ -935,26 +940,50 @@ struct GemmKernel {
     }
   }
 
-  // ---------------- light tiles of the 256x128 kernel: the waves split K ----------------
-  // A tile with at most four 32-row blocks below m (at most 128 of its 256
-  // rows) would leave the two-by-two layout dequantising every B fragment
-  // twice for few rows. Here the four waves split the K range instead: with
-  // KS = 4 (one or two row blocks) wave w takes two of the eight 16-K
-  // substeps of every stage (half w / 2, substeps 2 (w % 2) and 2 (w % 2) + 1)
-  // for all rows and all 128 columns; with KS = 2 (three or four row blocks)
-  // wave w takes half w % 2 of every stage for the 64 columns w / 2. Each
-  // wave dequantises its fragments for a quarter of the substeps, 80-192 VALU
-  // per stage against 128-256 in the layouts above. At the end of the tile the
-  // KS partial sums of each output block are added through LDS, in the order
-  // of their K parts, so the result is deterministic; wave w then stores the
-  // 32 columns 32 w .. 32 w + 31. The accumulator array holds the partials:
-  // block (i, j) (row block i, the wave's column block j) is
-  // acc[ks_ai(i, j)][ks_aj(i, j)].
-  template <int KS>
-  __device__ __forceinline__ static constexpr int ks_ai(int i, int j) { return KS == 4 ? 2 * i + (j >> 1) : i; }
-  template <int KS>
-  __device__ __forceinline__ static constexpr int ks_aj(int i, int j) { return KS == 4 ? (j & 1) : j; }
-  __device__ __forceinline__ bool ks_tile(const TileCtx& t) const { return kKS && t.M - t.row0 <= 128; }
+  // ---------------- the 256x128 whole-tile kernels: the waves split K ----------------
+  // In the two-by-two layout each wave dequantises its 4 A and 2 B fragments
+  // for every 16-K substep: 6 VALU per MFMA, and light tiles dequantise every
+  // B fragment twice for few rows. Here the four waves split the K range of
+  // every stage instead, in one of three modes by the tile's row blocks below
+  // m (r):
+  //  * KS4 (r <= 2): wave w takes substeps 2 (w % 2), 2 (w % 2) + 1 of half
+  //    w / 2 of every stage, for all r row blocks and all 4 column blocks;
+  //  * KS2C (r = 3, 4): wave w takes half w % 2 of every stage, for all r row
+  //    blocks and the 2 column blocks 2 (w / 2), 2 (w / 2) + 1;
+  //  * KS2R (r >= 5): wave w takes half w % 2 of every stage, for row blocks
+  //    w / 2, w / 2 + 2, ... (as in the two-by-two layout) and all 4 column
+  //    blocks: 128x128 wave tiles, 4 VALU per MFMA.
+  // Per stage a wave dequantises 80-256 VALU where the two-by-two layout
+  // needs 128-384, for the same MFMAs. At the end of the tile the partials of
+  // each 32x32 block are added through LDS, in the order of their K parts, so
+  // results are deterministic (and differ from the other layouts' in the last
+  // bits only). The accumulators are acc[i][j] for the wave's row block i and
+  // column block j.
+  enum { KS4 = 0, KS2C = 1, KS2R = 2 };
+  template <int MODE>
+  struct KsShape {
+    static constexpr int KS = MODE == KS4 ? 4 : 2;
+    static constexpr int P = 8 / KS;                  // substeps per stage per wave
+    static constexpr int NBK = MODE == KS2C ? 2 : 4;  // column blocks per wave
+  };
+  __device__ __forceinline__ bool ks_tile(const TileCtx& t) const { return kKS && (kKS2R || t.M - t.row0 <= 128); }
+  // Block (i, j) of a wave's partials (NBK column blocks): with 4 x 2
+  // accumulator blocks, KS4's four column blocks of row block i (i < 2) take
+  // acc[2 i][0..1] and acc[2 i + 1][0..1].
+  template <int NBK>
+  __device__ __forceinline__ static f32x16& acc_at(f32x16 (&acc)[ACC_M][ACC_N], int i, int j) {
+    if constexpr (NBK <= ACC_N) return acc[i][j];
+    else return acc[2 * i + (j >> 1)][j & 1];
+  }
+  template <int NBK>
+  __device__ __forceinline__ static const f32x16& acc_at(const f32x16 (&acc)[ACC_M][ACC_N], int i, int j) {
+    if constexpr (NBK <= ACC_N) return acc[i][j];
+    else return acc[2 * i + (j >> 1)][j & 1];
+  }
+  __device__ __forceinline__ int ks_rows(const TileCtx& t) const {
+    const int rows = t.M - t.row0;
+    return rows >= BM ? BM / 32 : (rows + 31) >> 5;
+  }
 
   // A wave's operands for its P substeps of a stage: P dwords of each of its
   // R A chunks and NBK B chunks, and the scale words.
@@ -977,38 +1006,52 @@ struct GemmKernel {
     f16x8 b[NBK];
   };
   // Per-lane LDS offsets of a wave's first A and B chunk (8 bytes into the
-  // chunk for the second substep pair of KS = 4), of the A scale chunk (row
-  // block i: word i) and of its B scale words, inside a stage; and the shift
-  // that brings the lane's scale bytes (two 16-blocks, or the one of KS = 4)
-  // to the bottom of a scale word.
+  // chunk for the second substep pair of KS4), of its A scale chunk(s) and B
+  // scale words inside a stage; the shift that brings the lane's scale bytes
+  // (two 16-blocks, or KS4's one) to the bottom of a word; and, for KS2R, the
+  // wave's word in each A scale chunk (row blocks rpart + 2i sit in atom
+  // i / 2, word rpart + 2 (i % 2)).
   struct KsBases {
-    int a, b, sa, sb, shift;
+    int a, b, sa, sb, shift, rpart;
   };
-  template <int KS>
+  template <int MODE>
   __device__ __forceinline__ KsBases ks_bases() const {
+    constexpr int KS = KsShape<MODE>::KS;
     const int kpart = wave % KS, npart = wave / KS;
     const int kk = KS == 2 ? kpart : kpart >> 1;
     const int sub = KS == 4 ? (kpart & 1) : 0;
-    const int c0 = npart * (BN * KS / 4);
+    const int c0 = MODE == KS2C ? npart * 64 : 0;
+    const int r0 = MODE == KS2R ? npart * 32 : 0;
     KsBases b;
-    b.a = lds_off(lr, kk * 2 + h) + sub * 8;
+    b.a = lds_off(r0 + lr, kk * 2 + h) + sub * 8;
     b.b = A_BYTES + lds_off(c0 + lr, kk * 2 + h) + sub * 8;
     b.sa = A_BYTES + B_BYTES + lr * 16 + kk * 512;
     b.sb = A_BYTES + B_BYTES + (A_ATOMS + (c0 >> 7)) * 1024 + lr * 16 + ((c0 & 127) >> 5) * 4 + kk * 512;
     b.shift = h * 16 + sub * 8;
+    b.rpart = MODE == KS2R ? npart : 0;
     return b;
   }
-  template <int R, int NBK, int P>
+  template <int MODE, int R, int NBK, int P>
   __device__ __forceinline__ void ks_read(KsRaw<R, NBK, P>& r, int buf, const KsBases& bs) const {
     typedef typename KsRaw<R, NBK, P>::chunk chunk;
+    constexpr int AS = MODE == KS2R ? 64 : 32;  // rows between the wave's A blocks
     const uint8_t* St = smem + buf * STAGE_BYTES;
 #pragma unroll
-    for (int i = 0; i < R; ++i) r.a[i] = *reinterpret_cast<const chunk*>(St + bs.a + i * 32 * kRowBytes);
+    for (int i = 0; i < R; ++i) r.a[i] = *reinterpret_cast<const chunk*>(St + bs.a + i * AS * kRowBytes);
 #pragma unroll
     for (int j = 0; j < NBK; ++j) r.b[j] = *reinterpret_cast<const chunk*>(St + bs.b + j * 32 * kRowBytes);
-    const u32x4 ca = *reinterpret_cast<const u32x4*>(St + bs.sa);
+    if constexpr (MODE == KS2R) {
 #pragma unroll
-    for (int i = 0; i < R; ++i) r.sa[i] = ca[i];
+      for (int a = 0; a < (R + 1) / 2; ++a) {
+        const u32x4 c = *reinterpret_cast<const u32x4*>(St + bs.sa + a * 1024);
+        r.sa[2 * a] = bs.rpart ? c[1] : c[0];
+        if (2 * a + 1 < R) r.sa[2 * a + 1] = bs.rpart ? c[3] : c[2];
+      }
+    } else {
+      const u32x4 c = *reinterpret_cast<const u32x4*>(St + bs.sa);
+#pragma unroll
+      for (int i = 0; i < R; ++i) r.sa[i] = c[i];
+    }
     const ScaleVec<NBK> cb = *reinterpret_cast<const ScaleVec<NBK>*>(St + bs.sb);
 #pragma unroll
     for (int j = 0; j < NBK; ++j) r.sb[j] = cb[j];
@@ -1031,13 +1074,13 @@ struct GemmKernel {
 #pragma unroll
     for (int j = 0; j < NBK; ++j) f.b[j] = dequant8(r.b[j][PS], s.b[j][SI]);
   }
-  template <int KS, int R, int NBK>
-  __device__ __forceinline__ static void ks_mfmas(f32x16 (&acc)[MB][NB], const KsFrags<R, NBK>& f) {
+  template <int R, int NBK>
+  __device__ __forceinline__ static void ks_mfmas(f32x16 (&acc)[ACC_M][ACC_N], const KsFrags<R, NBK>& f) {
 #pragma unroll
     for (int i = 0; i < R; ++i)
 #pragma unroll
       for (int j = 0; j < NBK; ++j) {
-        f32x16& c = acc[ks_ai<KS>(i, j)][ks_aj<KS>(i, j)];
+        f32x16& c = acc_at<NBK>(acc, i, j);
         c = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.b[j], f.a[i], c, 0, 0, 0);
       }
   }
@@ -1051,19 +1094,20 @@ struct GemmKernel {
   // One substep (as step): the MFMAs of `use` with the dequantisation of the
   // wave's substep NEXT of `src` into `fill` (and, with CONVERT, first the
   // conversion of src's scales), after direct loads U0 .. U1-1.
-  template <int KS, int NEXT, bool CONVERT, int U0, int U1, int R, int NBK, int P>
-  __device__ __forceinline__ void ks_step(f32x16 (&acc)[MB][NB], const KsFrags<R, NBK>& use, KsFrags<R, NBK>& fill,
-                                          const KsRaw<R, NBK, P>& src, KsScales<R, NBK>& ssrc, int shift,
-                                          const StageIssue* si) const {
+  template <int NEXT, bool CONVERT, int U0, int U1, int R, int NBK, int P>
+  __device__ __forceinline__ void ks_step(f32x16 (&acc)[ACC_M][ACC_N], const KsFrags<R, NBK>& use,
+                                          KsFrags<R, NBK>& fill, const KsRaw<R, NBK, P>& src, KsScales<R, NBK>& ssrc,
+                                          int shift, const StageIssue* si) const {
     if constexpr (U0 < U1) {
       dma_range<U0, U1>(*si);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (R == 0) return;
     constexpr int VALU = (R + NBK) * 8 + (CONVERT ? 2 * (R + NBK) : 0);
-    constexpr int PER = (VALU + R * NBK - 1) / (R * NBK);
+    constexpr int PER = R > 0 ? (VALU + R * NBK - 1) / (R * NBK) : 0;
     if (CONVERT) ks_convert(ssrc, src, shift);
     ks_dequant<NEXT>(fill, src, ssrc);
-    ks_mfmas<KS>(acc, use);
+    ks_mfmas(acc, use);
 #pragma unroll
     for (int q = 0; q < R * NBK; ++q) {
       __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
@@ -1078,64 +1122,86 @@ struct GemmKernel {
   // cover the reads, the stage's direct loads and stage g + 1's first
   // dequantisation into f0. The same waits, barrier and loads per stage as
   // mainloop.
-  template <int KS, int R, int NBK, int P>
-  __device__ __forceinline__ void ks_stage(f32x16 (&acc)[MB][NB], KsRaw<R, NBK, P>& r, KsScales<R, NBK>& s,
+  template <int MODE, int R, int NBK, int P>
+  __device__ __forceinline__ void ks_stage(f32x16 (&acc)[ACC_M][ACC_N], KsRaw<R, NBK, P>& r, KsScales<R, NBK>& s,
                                            KsFrags<R, NBK>& f0, KsFrags<R, NBK>& f1, const KsBases& bs, int g, int kt,
                                            Loader& ld, int kpad_g, int kpad_grp, int pend) const {
-    constexpr int DS = R + NBK + 2;  // LDS reads of a stage
     if constexpr (P == 4) {
-      ks_step<KS, 1, false, 0, 0>(acc, f0, f1, r, s, bs.shift, nullptr);
-      ks_step<KS, 2, false, 0, 0>(acc, f1, f0, r, s, bs.shift, nullptr);
-      ks_step<KS, 3, false, 0, 0>(acc, f0, f1, r, s, bs.shift, nullptr);
+      ks_step<1, false, 0, 0>(acc, f0, f1, r, s, bs.shift, nullptr);
+      ks_step<2, false, 0, 0>(acc, f1, f0, r, s, bs.shift, nullptr);
+      ks_step<3, false, 0, 0>(acc, f0, f1, r, s, bs.shift, nullptr);
     } else {
-      ks_step<KS, 1, false, 0, 0>(acc, f0, f1, r, s, bs.shift, nullptr);
+      ks_step<1, false, 0, 0>(acc, f0, f1, r, s, bs.shift, nullptr);
     }
     ks_pin(f1, s);
     wait_next_stage(pend, kt);
     if (KPAD && g + 1 == kpad_g) zero_half_atom((uint32_t)(g + 1) % NS, kpad_grp);
     block_sync();
     const StageIssue si = prep_issue(ld);
-    ks_read(r, (uint32_t)(g + 1) % NS, bs);  // unused after the last stage
-    __builtin_amdgcn_sched_group_barrier(kSchedDSRead, DS, 0);
-    ks_step<KS, 0, true, 0, L>(acc, f1, f0, r, s, bs.shift, &si);
+    if constexpr (R > 0) {
+      ks_read<MODE>(r, (uint32_t)(g + 1) % NS, bs);  // unused after the last stage
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, R + NBK + 1 + (MODE == KS2R ? (R + 1) / 2 : 1), 0);
+    }
+    ks_step<0, true, 0, L>(acc, f1, f0, r, s, bs.shift, &si);
     ks_pin(f0, s);
     advance(ld);
   }
-  // n stages of a light tile's segment (as mainloop), R row blocks below m.
-  template <int R, int KS>
-  __device__ __forceinline__ void mainloop_ks(f32x16 (&acc)[MB][NB], int n, int g0, Loader& ld, int kpad_g,
+  // n stages of a segment in mode MODE, R row blocks for this wave (0: it
+  // only issues its loads and meets the barriers).
+  template <int MODE, int R>
+  __device__ __forceinline__ void mainloop_ks(f32x16 (&acc)[ACC_M][ACC_N], int n, int g0, Loader& ld, int kpad_g,
                                               int kpad_grp, int pend) const {
-    constexpr int NBK = BN * KS / 4 / 32, P = 8 / KS;
-    const KsBases bs = ks_bases<KS>();
+    constexpr int NBK = KsShape<MODE>::NBK, P = KsShape<MODE>::P;
+    const KsBases bs = ks_bases<MODE>();
     KsRaw<R, NBK, P> r;
     KsScales<R, NBK> s;
     KsFrags<R, NBK> f0, f1;
     wait_first_stage(pend);
     if (KPAD && g0 == kpad_g) zero_half_atom((uint32_t)g0 % NS, kpad_grp);
     block_sync();
-    ks_read(r, (uint32_t)g0 % NS, bs);
-    ks_convert(s, r, bs.shift);
-    ks_dequant<0>(f0, r, s);
-    for (int kt = 0; kt < n; ++kt) ks_stage<KS>(acc, r, s, f0, f1, bs, g0 + kt, kt, ld, kpad_g, kpad_grp, pend);
+    if constexpr (R > 0) {
+      ks_read<MODE>(r, (uint32_t)g0 % NS, bs);
+      ks_convert(s, r, bs.shift);
+      ks_dequant<0>(f0, r, s);
+    }
+    for (int kt = 0; kt < n; ++kt) ks_stage<MODE>(acc, r, s, f0, f1, bs, g0 + kt, kt, ld, kpad_g, kpad_grp, pend);
+  }
+  // Mode and this wave's row blocks for a tile with r row blocks below m.
+  __device__ __forceinline__ void mainloop_ks_rows(f32x16 (&acc)[ACC_M][ACC_N], int r, int n, int g0, Loader& ld,
+                                                   int kpad_g, int kpad_grp, int pend) const {
+    switch (r) {
+      case 1: mainloop_ks<KS4, 1>(acc, n, g0, ld, kpad_g, kpad_grp, pend); return;
+      case 2: mainloop_ks<KS4, 2>(acc, n, g0, ld, kpad_g, kpad_grp, pend); return;
+      case 3: mainloop_ks<KS2C, 3>(acc, n, g0, ld, kpad_g, kpad_grp, pend); return;
+      case 4: mainloop_ks<KS2C, 4>(acc, n, g0, ld, kpad_g, kpad_grp, pend); return;
+      default: break;
+    }
+    if constexpr (kKS2R) {
+      switch ((r - wave / 2 + 1) >> 1) {  // KS2R: row blocks w / 2, w / 2 + 2, ... below m
+        case 2: mainloop_ks<KS2R, 2>(acc, n, g0, ld, kpad_g, kpad_grp, pend); return;
+        case 3: mainloop_ks<KS2R, 3>(acc, n, g0, ld, kpad_g, kpad_grp, pend); return;
+        default: mainloop_ks<KS2R, 4>(acc, n, g0, ld, kpad_g, kpad_grp, pend); return;
+      }
+    }
   }
 
-  // The end of a light tile: for each row block i and each half p of the
-  // lane's 16 accumulator elements (one 16-column store run pair), every wave
-  // writes its partials into LDS slot (o, kp) - o the wave that stores the
-  // block, kp the writer's K part - and after a barrier each wave adds the KS
-  // partials of its own block in K-part order and stores them. Two barriers
-  // per round; the slots lie past the stages (which already hold the next
-  // tile's loads).
-  template <int R, int KS>
-  __device__ __forceinline__ void epilogue_ks(const f32x16 (&acc)[MB][NB], const TileCtx& t) const {
-    constexpr int NBK = BN * KS / 4 / 32;
+  // The end of a tile in modes KS4 and KS2C: for each row block i and each
+  // half p of the lane's 16 accumulator elements (one 16-column store run
+  // pair), every wave writes its partials into LDS slot (o, kp) - o the wave
+  // that stores the block (wave o stores columns 32 o .. 32 o + 31), kp the
+  // writer's K part - and after a barrier each wave adds the KS partials of
+  // its own block in K-part order and stores them. Two barriers per round;
+  // the slots lie past the stages (which already hold the next tile's loads).
+  template <int MODE, int R>
+  __device__ __forceinline__ void epilogue_ks(const f32x16 (&acc)[ACC_M][ACC_N], const TileCtx& t) const {
+    constexpr int KS = KsShape<MODE>::KS, NBK = KsShape<MODE>::NBK;
     const int kpart = wave % KS, npart = wave / KS;
     int lro = lr, h8 = h * 8;
     asm volatile("" : "+v"(lro), "+v"(h8));
-    const int col0 = t.col0 + wave * 32;  // this wave's 32 output columns
+    const int col0 = t.col0 + wave * 32;
     typedef __attribute__((address_space(1))) uint16_t gu16;
     gu16* crow = (gu16*)t.c + (size_t)(t.row0 + lro) * t.N + col0 + h8;
-    // slot (o, kp) holds 2 x 64 lanes x 16 bytes at EX_OFF + (o * 4 + kp) * 2048
+    // slot (o, kp): 2 x 64 lanes x 16 bytes at EX_OFF + (o * 4 + kp) * 2048
     f32x4* wr = reinterpret_cast<f32x4*>(smem + EX_OFF) + ((npart * NBK) * 4 + kpart) * 128 + lane;
     const f32x4* rd = reinterpret_cast<const f32x4*>(smem + EX_OFF) + wave * 4 * 128 + lane;
 #pragma unroll
@@ -1145,9 +1211,8 @@ struct GemmKernel {
         // the wave's local column block j is stored by wave npart * NBK + j
 #pragma unroll
         for (int j = 0; j < NBK; ++j) {
-          const f32x16& c = acc[ks_ai<KS>(i, j)][ks_aj<KS>(i, j)];
-          wr[j * 4 * 128] = f32x4{c[8 * p + 0], c[8 * p + 1], c[8 * p + 2], c[8 * p + 3]};
-          wr[j * 4 * 128 + 64] = f32x4{c[8 * p + 4], c[8 * p + 5], c[8 * p + 6], c[8 * p + 7]};
+          wr[j * 4 * 128] = acc_quad(acc_at<NBK>(acc, i, j), 8 * p);
+          wr[j * 4 * 128 + 64] = acc_quad(acc_at<NBK>(acc, i, j), 8 * p + 4);
         }
         block_sync();
         f32x4 sum0 = rd[0], sum1 = rd[64];
@@ -1156,16 +1221,92 @@ struct GemmKernel {
           sum0 += rd[kp * 128];
           sum1 += rd[kp * 128 + 64];
         }
-        const auto s0 = __builtin_amdgcn_permlane32_swap(pack_f16(sum0[0], sum0[1]), pack_f16(sum1[0], sum1[1]), false,
-                                                         false);
-        const auto s1 = __builtin_amdgcn_permlane32_swap(pack_f16(sum0[2], sum0[3]), pack_f16(sum1[2], sum1[3]), false,
-                                                         false);
-        const int cu = 2 * p * 8;
-        if (lro < t.M - t.row0 - i * 32 && h8 < t.N - col0 - cu) {
-          const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
-          *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(crow + (size_t)i * 32 * t.N + cu) = v;
-        }
+        store_run(sum0, sum1, crow + (size_t)i * 32 * t.N + 16 * p,
+                  lro < t.M - t.row0 - i * 32 && h8 < t.N - col0 - 16 * p);
         block_sync();  // the slots are rewritten next round
+      }
+    }
+  }
+  // The end of a KS2R tile: the waves of K parts 0 and 1 with the same row
+  // blocks pair up; wave kp stores column blocks 2 kp, 2 kp + 1 of them. Per
+  // round (one row block of the wave, four for every wave, so the barriers
+  // match) each wave writes its partials of its partner's two column blocks
+  // (2 halves each) into the partner's four slots, and adds the partner's
+  // into its own in K-part order.
+  template <int R>
+  __device__ __forceinline__ void epilogue_ks2r(const f32x16 (&acc)[ACC_M][ACC_N], const TileCtx& t) const {
+    const int kpart = wave & 1, rpart = wave >> 1;
+    int lro = lr, h8 = h * 8;
+    asm volatile("" : "+v"(lro), "+v"(h8));
+    const int col0 = t.col0 + kpart * 64;
+    typedef __attribute__((address_space(1))) uint16_t gu16;
+    gu16* crow = (gu16*)t.c + (size_t)(t.row0 + rpart * 32 + lro) * t.N + col0 + h8;
+    f32x4* wr = reinterpret_cast<f32x4*>(smem + EX_OFF) + (wave ^ 1) * 4 * 128 + lane;
+    const f32x4* rd = reinterpret_cast<const f32x4*>(smem + EX_OFF) + wave * 4 * 128 + lane;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i < R) {
+        // slot q = jl * 2 + p of the partner: its column block 2 (1 - kpart) + jl, half p
+#pragma unroll
+        for (int jl = 0; jl < 2; ++jl)
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            // (values, not a reference, are selected: a reference picked at
+            // run time would put the accumulators in memory)
+            const f32x4 q0 = kpart ? acc_quad(acc[i][jl], 8 * p) : acc_quad(acc[i][2 + jl], 8 * p);
+            const f32x4 q1 = kpart ? acc_quad(acc[i][jl], 8 * p + 4) : acc_quad(acc[i][2 + jl], 8 * p + 4);
+            wr[(jl * 2 + p) * 128] = q0;
+            wr[(jl * 2 + p) * 128 + 64] = q1;
+          }
+      }
+      block_sync();
+      if (i < R) {
+        const int rb = rpart + 2 * i;
+#pragma unroll
+        for (int jl = 0; jl < 2; ++jl)
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            const f32x4 o0 = rd[(jl * 2 + p) * 128], o1 = rd[(jl * 2 + p) * 128 + 64];
+            const f32x4 m0 = kpart ? acc_quad(acc[i][2 + jl], 8 * p) : acc_quad(acc[i][jl], 8 * p);
+            const f32x4 m1 = kpart ? acc_quad(acc[i][2 + jl], 8 * p + 4) : acc_quad(acc[i][jl], 8 * p + 4);
+            // K part 0's partial first
+            const f32x4 sum0 = kpart ? o0 + m0 : m0 + o0, sum1 = kpart ? o1 + m1 : m1 + o1;
+            const int cu = jl * 32 + 16 * p;
+            store_run(sum0, sum1, crow + (size_t)i * 64 * t.N + cu,
+                      lro < t.M - t.row0 - rb * 32 && h8 < t.N - col0 - cu);
+          }
+      }
+      block_sync();
+    }
+  }
+  __device__ __forceinline__ static f32x4 acc_quad(const f32x16& c, int e) {
+    return f32x4{acc_read(c[e]), acc_read(c[e + 1]), acc_read(c[e + 2]), acc_read(c[e + 3])};
+  }
+  // One lane's run pair of a block row (elements 8p .. 8p + 7 as two quads)
+  // to 8 consecutive fp16 columns, as in epilogue_impl.
+  __device__ __forceinline__ static void store_run(const f32x4& q0, const f32x4& q1,
+                                                   __attribute__((address_space(1))) uint16_t* dst, bool ok) {
+    const auto s0 = __builtin_amdgcn_permlane32_swap(pack_f16(q0[0], q0[1]), pack_f16(q1[0], q1[1]), false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(pack_f16(q0[2], q0[3]), pack_f16(q1[2], q1[3]), false, false);
+    if (ok) {
+      const u32x4 v = {s0[0], s1[0], s0[1], s1[1]};
+      *reinterpret_cast<__attribute__((address_space(1))) u32x4*>(dst) = v;
+    }
+  }
+  __device__ __forceinline__ void epilogue_ks_rows(const f32x16 (&acc)[ACC_M][ACC_N], const TileCtx& t) const {
+    const int r = ks_rows(t);
+    switch (r) {
+      case 1: epilogue_ks<KS4, 1>(acc, t); return;
+      case 2: epilogue_ks<KS4, 2>(acc, t); return;
+      case 3: epilogue_ks<KS2C, 3>(acc, t); return;
+      case 4: epilogue_ks<KS2C, 4>(acc, t); return;
+      default: break;
+    }
+    if constexpr (kKS2R) {
+      switch ((r - wave / 2 + 1) >> 1) {
+        case 2: epilogue_ks2r<2>(acc, t); return;
+        case 3: epilogue_ks2r<3>(acc, t); return;
+        default: epilogue_ks2r<4>(acc, t); return;
       }
     }
   }
@@ -1241,7 +1382,7 @@ struct GemmKernel {
   // of their own, as in the f16 steps); the VALU work `work` emits (VALU
   // instructions, about) is spread between the MFMAs.
   template <int P, int J0, int J1, int AMB, int U0, int U1, int VALU, class Work>
-  __device__ __forceinline__ void mx_sub(f32x16 (&acc)[MB][NB], const u32x4 (&ta)[MB], const Raw& r,
+  __device__ __forceinline__ void mx_sub(f32x16 (&acc)[ACC_M][ACC_N], const u32x4 (&ta)[MB], const Raw& r,
                                          const MxScales& s, const StageIssue* si, Work&& work) const {
     if constexpr (U0 < U1) {
       dma_range<U0, U1>(*si);
@@ -1276,7 +1417,7 @@ struct GemmKernel {
   // issued before this half), so that after the barrier its MFMAs start at
   // once.
   template <int AMB, bool ISSUE>
-  __device__ __forceinline__ void mx_half(f32x16 (&acc)[MB][NB], const Raw& cur, const MxOps& o, const Raw& nxt,
+  __device__ __forceinline__ void mx_half(f32x16 (&acc)[ACC_M][ACC_N], const Raw& cur, const MxOps& o, const Raw& nxt,
                                           MxOps& no, uint32_t& seen, const StageIssue* si) const {
     constexpr int U1 = ISSUE ? (L + 3) / 4 : 0, U2 = ISSUE ? U1 + (L - U1 + 2) / 3 : 0;
     constexpr int U3 = ISSUE ? U2 + (L - U2 + 1) / 2 : 0, U4 = ISSUE ? L : 0;
@@ -1303,7 +1444,7 @@ struct GemmKernel {
   // The MX counterpart of mainloop: the same stages, waits, barriers and
   // direct loads; a half stage's raw chunks feed the MFMAs directly.
   template <int AMB>
-  __device__ __forceinline__ void mainloop_mx(f32x16 (&acc)[MB][NB], int n, int g0, Loader& ld, int kpad_g,
+  __device__ __forceinline__ void mainloop_mx(f32x16 (&acc)[ACC_M][ACC_N], int n, int g0, Loader& ld, int kpad_g,
                                               int kpad_grp, uint32_t& seen, int pend) const {
     static_assert(NB % 2 == 0 || NB == 1, "two block-column parts per pass (one: the first part is empty)");
     Raw r0, r1;
@@ -1342,7 +1483,7 @@ struct GemmKernel {
     return nb <= wm ? 0 : min(MB, (nb - wm + 1) >> 1);
   }
 
-  __device__ __forceinline__ void mainloop_rows_mx(f32x16 (&acc)[MB][NB], const TileCtx& t, int n, int g0,
+  __device__ __forceinline__ void mainloop_rows_mx(f32x16 (&acc)[ACC_M][ACC_N], const TileCtx& t, int n, int g0,
                                                    Loader& ld, int kpad_g, uint32_t& seen, int pend) const {
     switch (active_blocks(t)) {
       case 0: mainloop_mx<0>(acc, n, g0, ld, kpad_g, t.kpad_group, seen, pend); break;
@@ -1364,33 +1505,28 @@ struct GemmKernel {
   }
 
   // Dispatch on this wave's active 32-row blocks (rows below m).
-  __device__ __forceinline__ void mainloop_rows(f32x16 (&acc)[MB][NB], const TileCtx& t, int n, int g0,
+  __device__ __forceinline__ void mainloop_rows(f32x16 (&acc)[ACC_M][ACC_N], const TileCtx& t, int n, int g0,
                                                 Loader& ld, int kpad_g, int pend) const {
     static_assert(MB <= 4, "active-block dispatch covers MB <= 4");
-    if constexpr (kKS) {
-      if (ks_tile(t)) {
-        switch ((t.M - t.row0 + 31) >> 5) {
-          case 1: mainloop_ks<1, 4>(acc, n, g0, ld, kpad_g, t.kpad_group, pend); break;
-          case 2: mainloop_ks<2, 4>(acc, n, g0, ld, kpad_g, t.kpad_group, pend); break;
-          case 3: mainloop_ks<3, 2>(acc, n, g0, ld, kpad_g, t.kpad_group, pend); break;
-          default: mainloop_ks<4, 2>(acc, n, g0, ld, kpad_g, t.kpad_group, pend); break;
+    if constexpr (kKS2R) {
+      mainloop_ks_rows(acc, ks_rows(t), n, g0, ld, kpad_g, t.kpad_group, pend);
+    } else if (kKS && ks_tile(t)) {
+      if constexpr (kKS) mainloop_ks_rows(acc, ks_rows(t), n, g0, ld, kpad_g, t.kpad_group, pend);
+    } else {
+      if constexpr (kWide) {
+        if (wide(t)) {
+          mainloop<1, NBW>(acc, n, g0, ld, kpad_g, t.kpad_group, pend, wide_bases());
+          return;
         }
-        return;
       }
-    }
-    if constexpr (kWide) {
-      if (wide(t)) {
-        mainloop<1, NBW>(acc, n, g0, ld, kpad_g, t.kpad_group, pend, wide_bases());
-        return;
+      const Bases bs = normal_bases();
+      switch (active_blocks(t)) {
+        case 0: mainloop<0>(acc, n, g0, ld, kpad_g, t.kpad_group, pend, bs); break;
+        case 1: mainloop<(MB >= 1 ? 1 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group, pend, bs); break;
+        case 2: mainloop<(MB >= 2 ? 2 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group, pend, bs); break;
+        case 3: mainloop<(MB >= 3 ? 3 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group, pend, bs); break;
+        default: mainloop<MB>(acc, n, g0, ld, kpad_g, t.kpad_group, pend, bs); break;
       }
-    }
-    const Bases bs = normal_bases();
-    switch (active_blocks(t)) {
-      case 0: mainloop<0>(acc, n, g0, ld, kpad_g, t.kpad_group, pend, bs); break;
-      case 1: mainloop<(MB >= 1 ? 1 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group, pend, bs); break;
-      case 2: mainloop<(MB >= 2 ? 2 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group, pend, bs); break;
-      case 3: mainloop<(MB >= 3 ? 3 : MB)>(acc, n, g0, ld, kpad_g, t.kpad_group, pend, bs); break;
-      default: mainloop<MB>(acc, n, g0, ld, kpad_g, t.kpad_group, pend, bs); break;
     }
   }
 
@@ -1419,55 +1555,52 @@ struct GemmKernel {
   // mainloop, which do not hold them all, and spills; they are kept in AGPRs
   // (pin_acc) and each element is read where the epilogue needs it. Smaller
   // wave tiles fit in VGPRs and are left to the compiler.
-  static constexpr bool kAccInAgprs = MB * NB == 16;
+  static constexpr bool kAccInAgprs = ACC_M * ACC_N == 16;
   __device__ __forceinline__ static float acc_read(float x) {
     if constexpr (!kAccInAgprs) return x;
     float v;
     asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(x));
     return v;
   }
-  __device__ __forceinline__ static void pin_acc(f32x16 (&acc)[MB][NB]) {
+  __device__ __forceinline__ static void pin_acc(f32x16 (&acc)[ACC_M][ACC_N]) {
     if constexpr (kAccInAgprs) {
 #pragma unroll
-      for (int i = 0; i < MB; ++i)
+      for (int i = 0; i < ACC_M; ++i)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) asm volatile("" : "+a"(acc[i][j]));
+        for (int j = 0; j < ACC_N; ++j) asm volatile("" : "+a"(acc[i][j]));
     }
   }
 
   // Returns true for an unmasked epilogue: every wave then issued exactly S
   // stores (see kPendStores).
-  __device__ __forceinline__ bool epilogue(const f32x16 (&acc)[MB][NB], const TileCtx& t) const {
-    if constexpr (kKS) {
-      if (ks_tile(t)) {
-        switch ((t.M - t.row0 + 31) >> 5) {
-          case 1: epilogue_ks<1, 4>(acc, t); break;
-          case 2: epilogue_ks<2, 4>(acc, t); break;
-          case 3: epilogue_ks<3, 2>(acc, t); break;
-          default: epilogue_ks<4, 2>(acc, t); break;
+  __device__ __forceinline__ bool epilogue(const f32x16 (&acc)[ACC_M][ACC_N], const TileCtx& t) const {
+    if constexpr (kKS2R) {
+      epilogue_ks_rows(acc, t);
+      return false;
+    } else if (kKS && ks_tile(t)) {
+      if constexpr (kKS) epilogue_ks_rows(acc, t);
+      return false;
+    } else {
+      if constexpr (kWide) {
+        if (wide(t)) {
+          epilogue_wide(acc, t);
+          return false;
         }
-        return false;
       }
-    }
-    if constexpr (kWide) {
-      if (wide(t)) {
-        epilogue_wide(acc, t);
-        return false;
+      // Tiles wholly inside m and n (all but the edges) store without masks,
+      // i.e. without an exec-mask branch around every store.
+      if (t.row0 + BM <= t.M && t.col0 + BN <= t.N) {
+        epilogue_impl<false>(acc, t);
+        return true;
       }
+      epilogue_impl<true>(acc, t);
+      return false;
     }
-    // Tiles wholly inside m and n (all but the edges) store without masks,
-    // i.e. without an exec-mask branch around every store.
-    if (t.row0 + BM <= t.M && t.col0 + BN <= t.N) {
-      epilogue_impl<false>(acc, t);
-      return true;
-    }
-    epilogue_impl<true>(acc, t);
-    return false;
   }
 
   // The wide layout's output: block j of a wave is columns
   // wave * WIDE_COLS + 32 j .. +31 of the tile's first 32 rows.
-  __device__ __forceinline__ void epilogue_wide(const f32x16 (&acc)[MB][NB], const TileCtx& t) const {
+  __device__ __forceinline__ void epilogue_wide(const f32x16 (&acc)[ACC_M][ACC_N], const TileCtx& t) const {
     int lro = lr, h8 = h * 8;
     asm volatile("" : "+v"(lro), "+v"(h8));
     const int col0 = t.col0 + wave * WIDE_COLS;
@@ -1492,7 +1625,7 @@ struct GemmKernel {
   }
 
   template <bool MASKED>
-  __device__ __forceinline__ void epilogue_impl(const f32x16 (&acc)[MB][NB], const TileCtx& t) const {
+  __device__ __forceinline__ void epilogue_impl(const f32x16 (&acc)[ACC_M][ACC_N], const TileCtx& t) const {
     // The lane's row and column offsets are formed here, per tile, from a copy
     // the compiler cannot see through: left to itself it hoists one offset per
     // block out of the tile loop and spills them, and each reload between
@@ -1580,7 +1713,7 @@ struct GemmKernel {
   // by the tree, so the result does not depend on timing, and no workgroup
   // ever waits for another. Each node's counter is cleared by its folder.
   // Returns true when this workgroup stored the tile's C.
-  __device__ __forceinline__ bool publish_partial(const f32x16 (&acc)[MB][NB], const TileCtx& t,
+  __device__ __forceinline__ bool publish_partial(const f32x16 (&acc)[ACC_M][ACC_N], const TileCtx& t,
                                                   const Segment& seg) const {
     const int amb = active_blocks(t);
     float* mine = slot_ptr(vwg, seg.u == unit_begin(vwg) ? 0 : 1);
@@ -1643,7 +1776,7 @@ struct GemmKernel {
 #pragma unroll
     for (int e = 0; e < 16; ++e) __hip_atomic_store(b + e * 64, x[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __device__ __forceinline__ static void acc_block(const f32x16 (&acc)[MB][NB], int i, int j, float (&x)[16]) {
+  __device__ __forceinline__ static void acc_block(const f32x16 (&acc)[ACC_M][ACC_N], int i, int j, float (&x)[16]) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) x[e] = acc_read(acc[i][j][e]);
   }
@@ -1654,7 +1787,7 @@ struct GemmKernel {
   // sum is rounded and stored to C, elsewhere it is stored (device-scope) to
   // the left child's slot, whose values were just read.
   template <bool ROOT, bool MASKED>
-  __device__ __forceinline__ void fold_node(const f32x16 (&acc)[MB][NB], const TileCtx& t, int amb, int own, int wl,
+  __device__ __forceinline__ void fold_node(const f32x16 (&acc)[ACC_M][ACC_N], const TileCtx& t, int amb, int own, int wl,
                                             int sl, int wr, int sr) const {
     int lro = lr, h8 = h * 8;
     asm volatile("" : "+v"(lro), "+v"(h8));
@@ -1669,7 +1802,7 @@ struct GemmKernel {
   }
 
   template <bool ROOT, bool MASKED, int J0>
-  __device__ __forceinline__ void fold_blocks(const f32x16 (&acc)[MB][NB], const TileCtx& t, int i, int own, float* pl,
+  __device__ __forceinline__ void fold_blocks(const f32x16 (&acc)[ACC_M][ACC_N], const TileCtx& t, int i, int own, float* pl,
                                               const float* pr, int lro, int h8) const {
     constexpr int JB = NB < 2 ? NB : 2;
     float sum[JB][16], y[JB][16];
@@ -1718,11 +1851,11 @@ struct GemmKernel {
 
   // Stream-K leaves the tiles of k = 0 groups (no units) to a strided pass.
   __device__ __forceinline__ void zero_k_tiles() const {
-    f32x16 zero[MB][NB];
+    f32x16 zero[ACC_M][ACC_N];
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
+    for (int i = 0; i < ACC_M; ++i)
 #pragma unroll
-      for (int j = 0; j < NB; ++j) zero[i][j] = f32x16{};
+      for (int j = 0; j < ACC_N; ++j) zero[i][j] = f32x16{};
     const KernelArgs& args = src.args;
     for (int gi = 0; gi < args.num_classes; ++gi) {
       if (args.cls[gi].nk != 0) continue;
@@ -1743,11 +1876,11 @@ struct GemmKernel {
       const TileCtx t = setup(seg.tile);
       const int n = seg.s1 - seg.s0;
       sub_words = t.sub_words;
-      f32x16 acc[MB][NB];
+      f32x16 acc[ACC_M][ACC_N];
 #pragma unroll
-      for (int i = 0; i < MB; ++i)
+      for (int i = 0; i < ACC_M; ++i)
 #pragma unroll
-        for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
+        for (int j = 0; j < ACC_N; ++j) acc[i][j] = f32x16{};
       // the tile's last stage, if this segment ends the tile and its last
       // scale atom is half used
       const int kpad_g = KPAD && t.kpad_group >= 0 && seg.s1 == t.nk ? g0 + n - 1 : -1;
@@ -1790,9 +1923,9 @@ __device__ __forceinline__ const KernelArgs& kernel_args() {
 // Stage layout in LDS (bytes): [A: BM rows x 64][B: BN rows x 64]
 // [scale atoms: (BM + BN) / 128 atom rows x 2 k-groups x 512]; A and B rows are
 // swizzled by lds_off, the scale atoms are stored as in global memory.
-template <int BM, int BN, int WM, int WN, int NS, bool KPAD, bool MX = false, bool SPLIT = false>
+template <int BM, int BN, int WM, int WN, int NS, bool KPAD, bool MX = false, bool SPLIT = false, bool KS2R_ALL = false>
 __global__ __launch_bounds__(kThreads, 1) void nvfp4_grouped_gemm_kernel(KernelArgs) {
-  using K = GemmKernel<BM, BN, WM, WN, NS, KernargSrc<SPLIT>, KPAD, MX>;
+  using K = GemmKernel<BM, BN, WM, WN, NS, KernargSrc<SPLIT>, KPAD, MX, KS2R_ALL>;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[K::LDS_BYTES];
   const K k(KernargSrc<SPLIT>{kernel_args()}, smem);
   k.run();
@@ -1945,11 +2078,22 @@ struct TileConfig {
   // for verification: each LDS buffer is then rewritten one stage sooner after
   // its last reads, so a missing wait or barrier shows up as a difference.
   void (*kernel_ns3[2])(KernelArgs);
+  // 256x128 only (else null): whole-tile f16 kernels that put every tile in a
+  // K-split mode ([some group with k % 64 == 32]), and their three-stage
+  // counterpart; for calls whose groups all have long K (see kKS2RMinStages).
+  void (*kernel_ks2r[2])(KernelArgs);
+  void (*kernel_ks2r_ns3)(KernelArgs);
 };
 
 constexpr int kStages = 4;  // LDS pipeline depth (4 x 36 KiB for 256x256 tiles)
 
 #define NVFP4_KERNEL(bm, bn, wm, wn, kpad, mx, split) nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, kStages, kpad, mx, split>
+// The end-of-tile exchange of a K-split tile moves 128 KiB through LDS: on
+// short tiles it costs more than the split saves (a 16-stage workload on
+// 256x128 tiles measured 62 -> 66 us with every tile split, 56-stage ones
+// gain 2-3%), so calls take the all-split kernels only when every group with
+// work has at least this many 128-K stages.
+constexpr int kKS2RMinStages = 32;
 #define NVFP4_TILE_CONFIG(bm, bn, wm, wn)                                                                       \
   { bm, bn, wm, wn,                                                                                         \
     {{{NVFP4_KERNEL(bm, bn, wm, wn, false, false, false), NVFP4_KERNEL(bm, bn, wm, wn, true, false, false)},   \
@@ -1958,11 +2102,24 @@ constexpr int kStages = 4;  // LDS pipeline depth (4 x 36 KiB for 256x256 tiles)
       {NVFP4_KERNEL(bm, bn, wm, wn, false, true, true), NVFP4_KERNEL(bm, bn, wm, wn, true, true, true)}}},     \
     nvfp4_grouped_gemm_device_kernel<bm, bn, wm, wn, kStages>, device_group_tiles<bm, bn>,                     \
     {nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, 3, true, false, false>,                                       \
-     nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, 3, true, false, true>} }
+     nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, 3, true, false, true>},                                       \
+    {nullptr, nullptr}, nullptr }
+#define NVFP4_TILE_CONFIG_KS2R(bm, bn, wm, wn)                                                                  \
+  { bm, bn, wm, wn,                                                                                         \
+    {{{NVFP4_KERNEL(bm, bn, wm, wn, false, false, false), NVFP4_KERNEL(bm, bn, wm, wn, true, false, false)},   \
+      {NVFP4_KERNEL(bm, bn, wm, wn, false, true, false), NVFP4_KERNEL(bm, bn, wm, wn, true, true, false)}},    \
+     {{NVFP4_KERNEL(bm, bn, wm, wn, false, false, true), NVFP4_KERNEL(bm, bn, wm, wn, true, false, true)},     \
+      {NVFP4_KERNEL(bm, bn, wm, wn, false, true, true), NVFP4_KERNEL(bm, bn, wm, wn, true, true, true)}}},     \
+    nvfp4_grouped_gemm_device_kernel<bm, bn, wm, wn, kStages>, device_group_tiles<bm, bn>,                     \
+    {nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, 3, true, false, false>,                                       \
+     nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, 3, true, false, true>},                                       \
+    {nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, kStages, false, false, false, true>,                          \
+     nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, kStages, true, false, false, true>},                          \
+    nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, 3, true, false, false, true> }
 const TileConfig kConfigs[] = {
     NVFP4_TILE_CONFIG(256, 256, 128, 128),
     NVFP4_TILE_CONFIG(128, 256, 64, 128),
-    NVFP4_TILE_CONFIG(256, 128, 128, 64),
+    NVFP4_TILE_CONFIG_KS2R(256, 128, 128, 64),
     NVFP4_TILE_CONFIG(128, 128, 64, 64),
     NVFP4_TILE_CONFIG(64, 64, 32, 32),
 };
@@ -2434,7 +2591,11 @@ int launch(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, vo
   bool kpad = false;
   for (int g = 0; g < G; ++g) kpad = kpad || (ps[4 * g + 2] % 64 != 0);
   void (*kernel)(KernelArgs) = tc.kernel[plan.split ? 1 : 0][mx_status ? 1 : 0][kpad ? 1 : 0];
-  if (stages == 3) kernel = tc.kernel_ns3[plan.split ? 1 : 0];
+  bool all_long = tc.kernel_ks2r[0] != nullptr && !plan.split && mx_status == nullptr;
+  for (int g = 0; g < G && all_long; ++g)
+    if (ps[4 * g + 0] > 0 && ps[4 * g + 1] > 0 && ps[4 * g + 2] > 0) all_long = group_stages(ps, g) >= kKS2RMinStages;
+  if (all_long) kernel = tc.kernel_ks2r[kpad ? 1 : 0];
+  if (stages == 3) kernel = all_long ? tc.kernel_ks2r_ns3 : tc.kernel_ns3[plan.split ? 1 : 0];
   if (plan.split) {
     int32_t* counters = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(workspace) +
                                                    partial_bytes_for(plan.cfg, plan.grid));

@@ -482,3 +482,33 @@ def test_one_row_block_tiles_every_config():
         for shape, a, b, r in zip(shapes, *outs, ref):
             assert not O.tolerance_violations(a, r["c16"], r["s"]).any(), (cfg, shape)
             assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), (cfg, shape)
+
+
+def test_long_k_split_over_waves_256x128():
+    """Calls whose groups all have at least 32 stages run the 256x128 kernels
+    that split K over the waves in every tile (128x128 wave tiles on full
+    tiles): against the oracle, and bitwise against their three-stage
+    counterpart. Row counts give every number of row blocks below m (1-8) and
+    several tile rows; one group has k % 64 == 32."""
+    cfg = next(c for c in range(mm.nvfp4_num_tile_configs())
+               if (mm.nvfp4_tile_config_info(c)["bm"], mm.nvfp4_tile_config_info(c)["bn"]) == (256, 128))
+    shapes = [(300, 264, 4096, 1), (129, 136, 4160, 1), (33, 72, 4128, 1), (256, 128, 4096, 2), (511, 8, 4096, 1),
+              (200, 392, 4096, 1), (1, 128, 4096, 1), (97, 520, 4096, 1)]
+    groups = poison_padding(shapes, synth.make_custom(shapes, seed=4242))
+    d = dev.upload(shapes, groups, c_guard=GUARD)
+    abc, sf = dev.pointer_tables(d)
+    ws = dev.workspace_for(shapes)
+    ref = O.grouped_gemm(shapes, groups)
+    outs = []
+    for stages in (4, 3):
+        announce(f"long-k split over waves cfg {cfg} stages {stages}")
+        for dd in d:
+            dd["c"].fill_(-1)
+        mm.nvfp4_grouped_gemm_stages(shapes, abc, sf, len(shapes), ws.data_ptr(), ws.numel(), cfg, 0, stages,
+                                     torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        assert dev.guards_intact(d), "store outside C"
+        outs.append([c.copy() for c in dev.c_as_numpy(shapes, d)])
+    for shape, a, b, r in zip(shapes, *outs, ref):
+        assert not O.tolerance_violations(a, r["c16"], r["s"]).any(), shape
+        assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), shape
