@@ -326,7 +326,7 @@ def test_repeat_is_bitwise_deterministic_and_streams():
         assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
 
 
-@pytest.mark.parametrize("idx,split", [(1, 0), (3, 0), (1, 1), (2, 1)])
+@pytest.mark.parametrize("idx,split", [(1, 0), (2, 0), (3, 0), (1, 1), (2, 1)])
 def test_graph_replay_matches_eager(idx, split):
     """A call captured in a HIP graph and replayed several times, with eager
     work and synchronisation between the replays, writes exactly what the
