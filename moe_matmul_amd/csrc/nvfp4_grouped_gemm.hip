@@ -950,15 +950,17 @@ struct GemmKernel {
   //    w / 2 of every stage, for all r row blocks and all 4 column blocks;
   //  * KS2C (r = 3, 4): wave w takes half w % 2 of every stage, for all r row
   //    blocks and the 2 column blocks 2 (w / 2), 2 (w / 2) + 1;
-  //  * KS2R (r >= 5): wave w takes half w % 2 of every stage, for row blocks
-  //    w / 2, w / 2 + 2, ... (as in the two-by-two layout) and all 4 column
-  //    blocks: 128x128 wave tiles, 4 VALU per MFMA.
+  //  * KS2R (r >= 5, only in the kernels that split every tile, KS2R_ALL;
+  //    the others keep the two-by-two layout there): wave w takes half w % 2
+  //    of every stage, for row blocks w / 2, w / 2 + 2, ... (as in the
+  //    two-by-two layout) and all 4 column blocks: 128x128 wave tiles, 4 VALU
+  //    per MFMA.
   // Per stage a wave dequantises 80-256 VALU where the two-by-two layout
   // needs 128-384, for the same MFMAs. At the end of the tile the partials of
   // each 32x32 block are added through LDS, in the order of their K parts, so
   // results are deterministic (and differ from the other layouts' in the last
-  // bits only). The accumulators are acc[i][j] for the wave's row block i and
-  // column block j.
+  // bits only). The wave's partial of row block i, column block j is
+  // acc_at(acc, i, j).
   enum { KS4 = 0, KS2C = 1, KS2R = 2 };
   template <int MODE>
   struct KsShape {
@@ -1102,9 +1104,8 @@ struct GemmKernel {
       dma_range<U0, U1>(*si);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (R == 0) return;
     constexpr int VALU = (R + NBK) * 8 + (CONVERT ? 2 * (R + NBK) : 0);
-    constexpr int PER = R > 0 ? (VALU + R * NBK - 1) / (R * NBK) : 0;
+    constexpr int PER = (VALU + R * NBK - 1) / (R * NBK);
     if (CONVERT) ks_convert(ssrc, src, shift);
     ks_dequant<NEXT>(fill, src, ssrc);
     ks_mfmas(acc, use);
@@ -1138,16 +1139,13 @@ struct GemmKernel {
     if (KPAD && g + 1 == kpad_g) zero_half_atom((uint32_t)(g + 1) % NS, kpad_grp);
     block_sync();
     const StageIssue si = prep_issue(ld);
-    if constexpr (R > 0) {
-      ks_read<MODE>(r, (uint32_t)(g + 1) % NS, bs);  // unused after the last stage
-      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, R + NBK + 1 + (MODE == KS2R ? (R + 1) / 2 : 1), 0);
-    }
+    ks_read<MODE>(r, (uint32_t)(g + 1) % NS, bs);  // unused after the last stage
+    __builtin_amdgcn_sched_group_barrier(kSchedDSRead, R + NBK + 1 + (MODE == KS2R ? (R + 1) / 2 : 1), 0);
     ks_step<0, true, 0, L>(acc, f1, f0, r, s, bs.shift, &si);
     ks_pin(f0, s);
     advance(ld);
   }
-  // n stages of a segment in mode MODE, R row blocks for this wave (0: it
-  // only issues its loads and meets the barriers).
+  // n stages of a segment in mode MODE, R (1 .. 4) row blocks for this wave.
   template <int MODE, int R>
   __device__ __forceinline__ void mainloop_ks(f32x16 (&acc)[ACC_M][ACC_N], int n, int g0, Loader& ld, int kpad_g,
                                               int kpad_grp, int pend) const {
@@ -1159,11 +1157,9 @@ struct GemmKernel {
     wait_first_stage(pend);
     if (KPAD && g0 == kpad_g) zero_half_atom((uint32_t)g0 % NS, kpad_grp);
     block_sync();
-    if constexpr (R > 0) {
-      ks_read<MODE>(r, (uint32_t)g0 % NS, bs);
-      ks_convert(s, r, bs.shift);
-      ks_dequant<0>(f0, r, s);
-    }
+    ks_read<MODE>(r, (uint32_t)g0 % NS, bs);
+    ks_convert(s, r, bs.shift);
+    ks_dequant<0>(f0, r, s);
     for (int kt = 0; kt < n; ++kt) ks_stage<MODE>(acc, r, s, f0, f1, bs, g0 + kt, kt, ld, kpad_g, kpad_grp, pend);
   }
   // Mode and this wave's row blocks for a tile with r row blocks below m.
