@@ -512,3 +512,24 @@ def test_long_k_split_over_waves_256x128():
     for shape, a, b, r in zip(shapes, *outs, ref):
         assert not O.tolerance_violations(a, r["c16"], r["s"]).any(), shape
         assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), shape
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_random_long_k_256x128(seed):
+    """Random long-K calls on the 256x128 tiles (seeded): every group with work
+    has k >= 4096, so whole tiles run the kernel that splits K over the waves
+    in every tile; m in [0, 600] (one to three tile rows, any row blocks below
+    m), n a multiple of 8 up to 264, k in {4096, 4128, 4160, 4224}, l in {1, 2}
+    (k = 0 groups included, which do not count against the choice). Against
+    the oracle, and stream-K on the same call for comparison."""
+    cfg = next(c for c in range(mm.nvfp4_num_tile_configs())
+               if (mm.nvfp4_tile_config_info(c)["bm"], mm.nvfp4_tile_config_info(c)["bn"]) == (256, 128))
+    rng = np.random.default_rng(7700 + seed)
+    g = int(rng.integers(2, 9))
+    shapes = [(int(rng.integers(0, 601)), 8 * int(rng.integers(1, 34)), int(rng.choice([4096, 4128, 4160, 4224])),
+               int(rng.choice([1, 1, 2]))) for _ in range(g)]
+    shapes[-1] = (shapes[-1][0], shapes[-1][1], 0, 1) if seed == 2 else shapes[-1]
+    groups = synth.make_custom(shapes, seed=int(rng.integers(1 << 30)))
+    ref = O.grouped_gemm(shapes, poison_padding(shapes, groups))
+    for split in (0, 1):
+        check(shapes, groups, tile_config=cfg, split_mode=split, ref=ref, label=f"random long k seed {seed}")
