@@ -946,10 +946,12 @@ struct GemmKernel {
   // B fragment twice for few rows. Here the four waves split the K range of
   // every stage instead, in one of three modes by the tile's row blocks below
   // m (r):
-  //  * KS4 (r <= 2): wave w takes substeps 2 (w % 2), 2 (w % 2) + 1 of half
-  //    w / 2 of every stage, for all r row blocks and all 4 column blocks;
-  //  * KS2C (r = 3, 4): wave w takes half w % 2 of every stage, for all r row
-  //    blocks and the 2 column blocks 2 (w / 2), 2 (w / 2) + 1;
+  //  * KS4 (r <= 2; r <= 4 with 4 x 4 accumulator blocks): wave w takes
+  //    substeps 2 (w % 2), 2 (w % 2) + 1 of half w / 2 of every stage, for
+  //    all r row blocks and all 4 column blocks;
+  //  * KS2C (r = 3, 4 with 4 x 2 accumulator blocks): wave w takes half
+  //    w % 2 of every stage, for all r row blocks and the 2 column blocks
+  //    2 (w / 2), 2 (w / 2) + 1;
   //  * KS2R (r >= 5, only in the kernels that split every tile, KS2R_ALL;
   //    the others keep the two-by-two layout there): wave w takes half w % 2
   //    of every stage, for row blocks w / 2, w / 2 + 2, ... (as in the
@@ -1162,14 +1164,23 @@ struct GemmKernel {
     ks_dequant<0>(f0, r, s);
     for (int kt = 0; kt < n; ++kt) ks_stage<MODE>(acc, r, s, f0, f1, bs, g0 + kt, kt, ld, kpad_g, kpad_grp, pend);
   }
+  template <int R>
+  __device__ __forceinline__ void ks_mode34(f32x16 (&acc)[ACC_M][ACC_N], int n, int g0, Loader& ld, int kpad_g,
+                                            int kpad_grp, int pend) const {
+    if constexpr (ACC_N == 4) mainloop_ks<KS4, R>(acc, n, g0, ld, kpad_g, kpad_grp, pend);
+    else mainloop_ks<KS2C, R>(acc, n, g0, ld, kpad_g, kpad_grp, pend);
+  }
   // Mode and this wave's row blocks for a tile with r row blocks below m.
   __device__ __forceinline__ void mainloop_ks_rows(f32x16 (&acc)[ACC_M][ACC_N], int r, int n, int g0, Loader& ld,
                                                    int kpad_g, int kpad_grp, int pend) const {
     switch (r) {
       case 1: mainloop_ks<KS4, 1>(acc, n, g0, ld, kpad_g, kpad_grp, pend); return;
       case 2: mainloop_ks<KS4, 2>(acc, n, g0, ld, kpad_g, kpad_grp, pend); return;
-      case 3: mainloop_ks<KS2C, 3>(acc, n, g0, ld, kpad_g, kpad_grp, pend); return;
-      case 4: mainloop_ks<KS2C, 4>(acc, n, g0, ld, kpad_g, kpad_grp, pend); return;
+      // (with 4 x 4 accumulator blocks KS4 holds up to four row blocks: a
+      // quarter of the substeps costs (r + 4) 16 VALU per stage, one half
+      // (r + 2) 32)
+      case 3: ks_mode34<3>(acc, n, g0, ld, kpad_g, kpad_grp, pend); return;
+      case 4: ks_mode34<4>(acc, n, g0, ld, kpad_g, kpad_grp, pend); return;
       default: break;
     }
     if constexpr (kKS2R) {
@@ -1294,8 +1305,8 @@ struct GemmKernel {
     switch (r) {
       case 1: epilogue_ks<KS4, 1>(acc, t); return;
       case 2: epilogue_ks<KS4, 2>(acc, t); return;
-      case 3: epilogue_ks<KS2C, 3>(acc, t); return;
-      case 4: epilogue_ks<KS2C, 4>(acc, t); return;
+      case 3: epilogue_ks<ACC_N == 4 ? KS4 : KS2C, 3>(acc, t); return;
+      case 4: epilogue_ks<ACC_N == 4 ? KS4 : KS2C, 4>(acc, t); return;
       default: break;
     }
     if constexpr (kKS2R) {
