@@ -385,17 +385,21 @@ struct GemmKernel {
   static_assert((NS - 1) * L + S < 64, "vmcnt range (counted waits across the epilogue's stores)");
   static constexpr int DUMMY_OFF = NS * STAGE_BYTES;
   static constexpr int FLAG_OFF = DUMMY_OFF + 1024;  // stream-K: a tile's arrival count, shared by the waves
-  // The whole-tile f16 256x128 kernels split K over the waves (mainloop_ks)
-  // and add the partials through 16 LDS slots of 64 lanes x 8 floats after
-  // the stages; their accumulators are 4 x 4 blocks (128x128 per wave at most).
-  static constexpr bool kKS = !Src::kCanSplit && !MX && BM == 256 && BN == 128 && WM == 128 && WN == 64;
+  // Whole-tile f16 kernels that split K over the waves (mainloop_ks) and add
+  // the partials through 16 LDS slots of 64 lanes x 8 floats after the
+  // stages: the 256x128 ones (light tiles; with KS2R_ALL every tile, fuller
+  // ones as 128x128 wave tiles), and the 128x256 ones with KS2R_ALL (every
+  // tile). With KS2R_ALL the accumulators are 4 x 4 blocks, else as in the
+  // two-by-two layout.
+  static constexpr bool kKS256x128 = BM == 256 && BN == 128 && WM == 128 && WN == 64;
+  static constexpr bool kKS128x256 = BM == 128 && BN == 256 && WM == 64 && WN == 128;
+  static constexpr bool kKS = !Src::kCanSplit && !MX && (kKS256x128 || (kKS128x256 && KS2R_ALL));
   static constexpr int EX_OFF = FLAG_OFF + 16;
   static constexpr int EX_BYTES = kKS ? 16 * 2048 : 0;
-  // KS2R_ALL: every tile in a K-split mode (fuller ones in KS2R, 128x128
-  // wave tiles: 4 x 4 accumulator blocks); else only tiles of at most four row
-  // blocks, and 4 x 2 accumulator blocks as in the two-by-two layout.
   static constexpr bool kKS2R = kKS && KS2R_ALL;
   static constexpr int ACC_M = kKS ? 4 : MB, ACC_N = kKS2R ? 4 : NB;
+  static constexpr int NCB = BN / 32;       // column blocks of a tile
+  static constexpr int CPW = NCB / 4;       // column blocks each wave stores after a K split
   static constexpr int LDS_BYTES = NS * STAGE_BYTES + 1024 + 16 + EX_BYTES;
   static_assert(NS >= 3 && NS <= 4 && LDS_BYTES <= 160 * 1024, "LDS stages");
   static_assert((NS - 2) * L < 64, "vmcnt range");
@@ -967,22 +971,23 @@ struct GemmKernel {
   template <int MODE>
   struct KsShape {
     static constexpr int KS = MODE == KS4 ? 4 : 2;
-    static constexpr int P = 8 / KS;                  // substeps per stage per wave
-    static constexpr int NBK = MODE == KS2C ? 2 : 4;  // column blocks per wave
+    static constexpr int P = 8 / KS;                          // substeps per stage per wave
+    static constexpr int NBK = MODE == KS2C ? NCB / 2 : NCB;  // column blocks per wave
   };
   __device__ __forceinline__ bool ks_tile(const TileCtx& t) const { return kKS && (kKS2R || t.M - t.row0 <= 128); }
-  // Block (i, j) of a wave's partials (NBK column blocks): with 4 x 2
-  // accumulator blocks, KS4's four column blocks of row block i (i < 2) take
-  // acc[2 i][0..1] and acc[2 i + 1][0..1].
+  // Block (i, j) of a wave's partials (NBK column blocks): when a row block's
+  // NBK blocks do not fit a row of the accumulator array, block (i, j) is
+  // element i NBK + j of it in row-major order (KS4 with 4 x 2 accumulators:
+  // acc[2 i][0..1], acc[2 i + 1][0..1]).
   template <int NBK>
   __device__ __forceinline__ static f32x16& acc_at(f32x16 (&acc)[ACC_M][ACC_N], int i, int j) {
     if constexpr (NBK <= ACC_N) return acc[i][j];
-    else return acc[2 * i + (j >> 1)][j & 1];
+    else return acc[(i * NBK + j) / ACC_N][(i * NBK + j) % ACC_N];
   }
   template <int NBK>
   __device__ __forceinline__ static const f32x16& acc_at(const f32x16 (&acc)[ACC_M][ACC_N], int i, int j) {
     if constexpr (NBK <= ACC_N) return acc[i][j];
-    else return acc[2 * i + (j >> 1)][j & 1];
+    else return acc[(i * NBK + j) / ACC_N][(i * NBK + j) % ACC_N];
   }
   __device__ __forceinline__ int ks_rows(const TileCtx& t) const {
     const int rows = t.M - t.row0;
@@ -1024,7 +1029,7 @@ struct GemmKernel {
     const int kpart = wave % KS, npart = wave / KS;
     const int kk = KS == 2 ? kpart : kpart >> 1;
     const int sub = KS == 4 ? (kpart & 1) : 0;
-    const int c0 = MODE == KS2C ? npart * 64 : 0;
+    const int c0 = MODE == KS2C ? npart * (BN / 2) : 0;
     const int r0 = MODE == KS2R ? npart * 32 : 0;
     KsBases b;
     b.a = lds_off(r0 + lr, kk * 2 + h) + sub * 8;
@@ -1056,9 +1061,14 @@ struct GemmKernel {
 #pragma unroll
       for (int i = 0; i < R; ++i) r.sa[i] = c[i];
     }
-    const ScaleVec<NBK> cb = *reinterpret_cast<const ScaleVec<NBK>*>(St + bs.sb);
+    // (at most four words per 128-column scale atom; the next atom row is 1 KiB on)
+    constexpr int NW = NBK < 4 ? NBK : 4;
 #pragma unroll
-    for (int j = 0; j < NBK; ++j) r.sb[j] = cb[j];
+    for (int a = 0; a < NBK / NW; ++a) {
+      const ScaleVec<NW> cb = *reinterpret_cast<const ScaleVec<NW>*>(St + bs.sb + a * 1024);
+#pragma unroll
+      for (int j = 0; j < NW; ++j) r.sb[a * NW + j] = cb[j];
+    }
   }
   template <int R, int NBK, int P>
   __device__ __forceinline__ static void ks_convert(KsScales<R, NBK>& s, const KsRaw<R, NBK, P>& r, int shift) {
@@ -1142,7 +1152,8 @@ struct GemmKernel {
     block_sync();
     const StageIssue si = prep_issue(ld);
     ks_read<MODE>(r, (uint32_t)(g + 1) % NS, bs);  // unused after the last stage
-    __builtin_amdgcn_sched_group_barrier(kSchedDSRead, R + NBK + 1 + (MODE == KS2R ? (R + 1) / 2 : 1), 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDSRead,
+                                         R + NBK + (NBK + 3) / 4 + (MODE == KS2R ? (R + 1) / 2 : 1), 0);
     ks_step<0, true, 0, L>(acc, f1, f0, r, s, bs.shift, &si);
     ks_pin(f0, s);
     advance(ld);
@@ -1152,6 +1163,7 @@ struct GemmKernel {
   __device__ __forceinline__ void mainloop_ks(f32x16 (&acc)[ACC_M][ACC_N], int n, int g0, Loader& ld, int kpad_g,
                                               int kpad_grp, int pend) const {
     constexpr int NBK = KsShape<MODE>::NBK, P = KsShape<MODE>::P;
+    static_assert(NBK <= ACC_N ? R <= ACC_M : R * NBK <= ACC_M * ACC_N, "partials fit the accumulators");
     const KsBases bs = ks_bases<MODE>();
     KsRaw<R, NBK, P> r;
     KsScales<R, NBK> s;
@@ -1164,18 +1176,20 @@ struct GemmKernel {
     ks_dequant<0>(f0, r, s);
     for (int kt = 0; kt < n; ++kt) ks_stage<MODE>(acc, r, s, f0, f1, bs, g0 + kt, kt, ld, kpad_g, kpad_grp, pend);
   }
+  // KS4 when its R x NCB partial blocks fit the accumulators, else KS2C.
+  template <int R>
+  static constexpr int ks_light_mode() { return R * NCB <= ACC_M * ACC_N ? KS4 : KS2C; }
   template <int R>
   __device__ __forceinline__ void ks_mode34(f32x16 (&acc)[ACC_M][ACC_N], int n, int g0, Loader& ld, int kpad_g,
                                             int kpad_grp, int pend) const {
-    if constexpr (ACC_N == 4) mainloop_ks<KS4, R>(acc, n, g0, ld, kpad_g, kpad_grp, pend);
-    else mainloop_ks<KS2C, R>(acc, n, g0, ld, kpad_g, kpad_grp, pend);
+    mainloop_ks<ks_light_mode<R>(), R>(acc, n, g0, ld, kpad_g, kpad_grp, pend);
   }
   // Mode and this wave's row blocks for a tile with r row blocks below m.
   __device__ __forceinline__ void mainloop_ks_rows(f32x16 (&acc)[ACC_M][ACC_N], int r, int n, int g0, Loader& ld,
                                                    int kpad_g, int kpad_grp, int pend) const {
     switch (r) {
-      case 1: mainloop_ks<KS4, 1>(acc, n, g0, ld, kpad_g, kpad_grp, pend); return;
-      case 2: mainloop_ks<KS4, 2>(acc, n, g0, ld, kpad_g, kpad_grp, pend); return;
+      case 1: ks_mode34<1>(acc, n, g0, ld, kpad_g, kpad_grp, pend); return;
+      case 2: ks_mode34<2>(acc, n, g0, ld, kpad_g, kpad_grp, pend); return;
       // (with 4 x 4 accumulator blocks KS4 holds up to four row blocks: a
       // quarter of the substeps costs (r + 4) 16 VALU per stage, one half
       // (r + 2) 32)
@@ -1183,7 +1197,7 @@ struct GemmKernel {
       case 4: ks_mode34<4>(acc, n, g0, ld, kpad_g, kpad_grp, pend); return;
       default: break;
     }
-    if constexpr (kKS2R) {
+    if constexpr (kKS2R && BM == 256) {
       switch ((r - wave / 2 + 1) >> 1) {  // KS2R: row blocks w / 2, w / 2 + 2, ... below m
         case 2: mainloop_ks<KS2R, 2>(acc, n, g0, ld, kpad_g, kpad_grp, pend); return;
         case 3: mainloop_ks<KS2R, 3>(acc, n, g0, ld, kpad_g, kpad_grp, pend); return;
@@ -1192,45 +1206,51 @@ struct GemmKernel {
     }
   }
 
-  // The end of a tile in modes KS4 and KS2C: for each row block i and each
-  // half p of the lane's 16 accumulator elements (one 16-column store run
-  // pair), every wave writes its partials into LDS slot (o, kp) - o the wave
-  // that stores the block (wave o stores columns 32 o .. 32 o + 31), kp the
-  // writer's K part - and after a barrier each wave adds the KS partials of
-  // its own block in K-part order and stores them. Two barriers per round;
+  // The end of a tile in modes KS4 and KS2C: wave o stores column blocks
+  // CPW o .. CPW o + CPW - 1. For each row block i, each of its column blocks
+  // q and each half p of the lane's 16 accumulator elements (one 16-column
+  // store run pair), every wave writes its partials of the blocks in that
+  // position into LDS slot (o, kp) - o the wave that stores the block, kp
+  // the writer's K part - and after a barrier each wave adds the KS partials
+  // of its own block in K-part order and stores them. Two barriers per round;
   // the slots lie past the stages (which already hold the next tile's loads).
   template <int MODE, int R>
   __device__ __forceinline__ void epilogue_ks(const f32x16 (&acc)[ACC_M][ACC_N], const TileCtx& t) const {
     constexpr int KS = KsShape<MODE>::KS, NBK = KsShape<MODE>::NBK;
     const int kpart = wave % KS, npart = wave / KS;
+    const int base = MODE == KS2C ? npart * NBK : 0;  // the wave's first column block (a multiple of CPW)
     int lro = lr, h8 = h * 8;
     asm volatile("" : "+v"(lro), "+v"(h8));
-    const int col0 = t.col0 + wave * 32;
+    const int col0 = t.col0 + wave * CPW * 32;
     typedef __attribute__((address_space(1))) uint16_t gu16;
     gu16* crow = (gu16*)t.c + (size_t)(t.row0 + lro) * t.N + col0 + h8;
     // slot (o, kp): 2 x 64 lanes x 16 bytes at EX_OFF + (o * 4 + kp) * 2048
-    f32x4* wr = reinterpret_cast<f32x4*>(smem + EX_OFF) + ((npart * NBK) * 4 + kpart) * 128 + lane;
+    f32x4* wr = reinterpret_cast<f32x4*>(smem + EX_OFF) + ((base / CPW) * 4 + kpart) * 128 + lane;
     const f32x4* rd = reinterpret_cast<const f32x4*>(smem + EX_OFF) + wave * 4 * 128 + lane;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
 #pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        // the wave's local column block j is stored by wave npart * NBK + j
+      for (int q = 0; q < CPW; ++q) {
 #pragma unroll
-        for (int j = 0; j < NBK; ++j) {
-          wr[j * 4 * 128] = acc_quad(acc_at<NBK>(acc, i, j), 8 * p);
-          wr[j * 4 * 128 + 64] = acc_quad(acc_at<NBK>(acc, i, j), 8 * p + 4);
-        }
-        block_sync();
-        f32x4 sum0 = rd[0], sum1 = rd[64];
+        for (int p = 0; p < 2; ++p) {
+          // local column block j is block (base + j) % CPW of wave (base + j) / CPW
 #pragma unroll
-        for (int kp = 1; kp < KS; ++kp) {
-          sum0 += rd[kp * 128];
-          sum1 += rd[kp * 128 + 64];
+          for (int j = q; j < NBK; j += CPW) {
+            wr[(j / CPW) * 4 * 128] = acc_quad(acc_at<NBK>(acc, i, j), 8 * p);
+            wr[(j / CPW) * 4 * 128 + 64] = acc_quad(acc_at<NBK>(acc, i, j), 8 * p + 4);
+          }
+          block_sync();
+          f32x4 sum0 = rd[0], sum1 = rd[64];
+#pragma unroll
+          for (int kp = 1; kp < KS; ++kp) {
+            sum0 += rd[kp * 128];
+            sum1 += rd[kp * 128 + 64];
+          }
+          const int cu = q * 32 + 16 * p;
+          store_run(sum0, sum1, crow + (size_t)i * 32 * t.N + cu,
+                    lro < t.M - t.row0 - i * 32 && h8 < t.N - col0 - cu);
+          block_sync();  // the slots are rewritten next round
         }
-        store_run(sum0, sum1, crow + (size_t)i * 32 * t.N + 16 * p,
-                  lro < t.M - t.row0 - i * 32 && h8 < t.N - col0 - 16 * p);
-        block_sync();  // the slots are rewritten next round
       }
     }
   }
@@ -1303,13 +1323,13 @@ struct GemmKernel {
   __device__ __forceinline__ void epilogue_ks_rows(const f32x16 (&acc)[ACC_M][ACC_N], const TileCtx& t) const {
     const int r = ks_rows(t);
     switch (r) {
-      case 1: epilogue_ks<KS4, 1>(acc, t); return;
-      case 2: epilogue_ks<KS4, 2>(acc, t); return;
-      case 3: epilogue_ks<ACC_N == 4 ? KS4 : KS2C, 3>(acc, t); return;
-      case 4: epilogue_ks<ACC_N == 4 ? KS4 : KS2C, 4>(acc, t); return;
+      case 1: epilogue_ks<ks_light_mode<1>(), 1>(acc, t); return;
+      case 2: epilogue_ks<ks_light_mode<2>(), 2>(acc, t); return;
+      case 3: epilogue_ks<ks_light_mode<3>(), 3>(acc, t); return;
+      case 4: epilogue_ks<ks_light_mode<4>(), 4>(acc, t); return;
       default: break;
     }
-    if constexpr (kKS2R) {
+    if constexpr (kKS2R && BM == 256) {
       switch ((r - wave / 2 + 1) >> 1) {
         case 2: epilogue_ks2r<2>(acc, t); return;
         case 3: epilogue_ks2r<3>(acc, t); return;
@@ -2085,9 +2105,10 @@ struct TileConfig {
   // for verification: each LDS buffer is then rewritten one stage sooner after
   // its last reads, so a missing wait or barrier shows up as a difference.
   void (*kernel_ns3[2])(KernelArgs);
-  // 256x128 only (else null): whole-tile f16 kernels that put every tile in a
-  // K-split mode ([some group with k % 64 == 32]), and their three-stage
-  // counterpart; for calls whose groups all have long K (see kKS2RMinStages).
+  // 256x128 and 128x256 only (else null): whole-tile f16 kernels that put
+  // every tile in a K-split mode ([some group with k % 64 == 32]), and their
+  // three-stage counterpart; for calls whose groups all have long K (see
+  // kKS2RMinStages).
   void (*kernel_ks2r[2])(KernelArgs);
   void (*kernel_ks2r_ns3)(KernelArgs);
 };
@@ -2125,7 +2146,7 @@ constexpr int kKS2RMinStages = 32;
     nvfp4_grouped_gemm_kernel<bm, bn, wm, wn, 3, true, false, false, true> }
 const TileConfig kConfigs[] = {
     NVFP4_TILE_CONFIG(256, 256, 128, 128),
-    NVFP4_TILE_CONFIG(128, 256, 64, 128),
+    NVFP4_TILE_CONFIG_KS2R(128, 256, 64, 128),
     NVFP4_TILE_CONFIG_KS2R(256, 128, 128, 64),
     NVFP4_TILE_CONFIG(128, 128, 64, 64),
     NVFP4_TILE_CONFIG(64, 64, 32, 32),

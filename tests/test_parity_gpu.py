@@ -484,14 +484,19 @@ def test_one_row_block_tiles_every_config():
             assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), (cfg, shape)
 
 
-def test_long_k_split_over_waves_256x128():
-    """Calls whose groups all have at least 32 stages run the 256x128 kernels
-    that split K over the waves in every tile (128x128 wave tiles on full
-    tiles): against the oracle, and bitwise against their three-stage
-    counterpart. Row counts give every number of row blocks below m (1-8) and
-    several tile rows; one group has k % 64 == 32."""
-    cfg = next(c for c in range(mm.nvfp4_num_tile_configs())
-               if (mm.nvfp4_tile_config_info(c)["bm"], mm.nvfp4_tile_config_info(c)["bn"]) == (256, 128))
+def config_of(bm, bn):
+    return next(c for c in range(mm.nvfp4_num_tile_configs())
+                if (mm.nvfp4_tile_config_info(c)["bm"], mm.nvfp4_tile_config_info(c)["bn"]) == (bm, bn))
+
+
+@pytest.mark.parametrize("tile", [(256, 128), (128, 256)])
+def test_long_k_split_over_waves(tile):
+    """Calls whose groups all have at least 32 stages run the 256x128 and
+    128x256 kernels that split K over the waves in every tile (128x128 wave
+    tiles on full tiles): against the oracle, and bitwise against their
+    three-stage counterpart. Row counts give every number of row blocks below
+    m (1-8) and several tile rows; one group has k % 64 == 32."""
+    cfg = config_of(*tile)
     shapes = [(300, 264, 4096, 1), (129, 136, 4160, 1), (33, 72, 4128, 1), (256, 128, 4096, 2), (511, 8, 4096, 1),
               (200, 392, 4096, 1), (1, 128, 4096, 1), (97, 520, 4096, 1)]
     groups = poison_padding(shapes, synth.make_custom(shapes, seed=4242))
@@ -514,16 +519,16 @@ def test_long_k_split_over_waves_256x128():
         assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), shape
 
 
+@pytest.mark.parametrize("tile", [(256, 128), (128, 256)])
 @pytest.mark.parametrize("seed", range(3))
-def test_random_long_k_256x128(seed):
-    """Random long-K calls on the 256x128 tiles (seeded): every group with work
-    has k >= 4096, so whole tiles run the kernel that splits K over the waves
-    in every tile; m in [0, 600] (one to three tile rows, any row blocks below
-    m), n a multiple of 8 up to 264, k in {4096, 4128, 4160, 4224}, l in {1, 2}
-    (k = 0 groups included, which do not count against the choice). Against
-    the oracle, and stream-K on the same call for comparison."""
-    cfg = next(c for c in range(mm.nvfp4_num_tile_configs())
-               if (mm.nvfp4_tile_config_info(c)["bm"], mm.nvfp4_tile_config_info(c)["bn"]) == (256, 128))
+def test_random_long_k_split_over_waves(seed, tile):
+    """Random long-K calls on the 256x128 and 128x256 tiles (seeded): every
+    group with work has k >= 4096, so whole tiles run the kernels that split K
+    over the waves in every tile; m in [0, 600] (several tile rows, any row
+    blocks below m), n a multiple of 8 up to 264, k in {4096, 4128, 4160,
+    4224}, l in {1, 2} (k = 0 groups included, which do not count against the
+    choice). Against the oracle, and stream-K on the same call for comparison."""
+    cfg = config_of(*tile)
     rng = np.random.default_rng(7700 + seed)
     g = int(rng.integers(2, 9))
     shapes = [(int(rng.integers(0, 601)), 8 * int(rng.integers(1, 34)), int(rng.choice([4096, 4128, 4160, 4224])),
