@@ -393,7 +393,8 @@ struct GemmKernel {
   // two-by-two layout.
   static constexpr bool kKS256x128 = BM == 256 && BN == 128 && WM == 128 && WN == 64;
   static constexpr bool kKS128x256 = BM == 128 && BN == 256 && WM == 64 && WN == 128;
-  static constexpr bool kKS = !Src::kCanSplit && !MX && (kKS256x128 || (kKS128x256 && KS2R_ALL));
+  static constexpr bool kKS128x128 = BM == 128 && BN == 128 && WM == 64 && WN == 64;
+  static constexpr bool kKS = !Src::kCanSplit && !MX && (kKS256x128 || ((kKS128x256 || kKS128x128) && KS2R_ALL));
   static constexpr int EX_OFF = FLAG_OFF + 16;
   static constexpr int EX_BYTES = kKS ? 16 * 2048 : 0;
   static constexpr bool kKS2R = kKS && KS2R_ALL;
@@ -2148,7 +2149,7 @@ const TileConfig kConfigs[] = {
     NVFP4_TILE_CONFIG(256, 256, 128, 128),
     NVFP4_TILE_CONFIG_KS2R(128, 256, 64, 128),
     NVFP4_TILE_CONFIG_KS2R(256, 128, 128, 64),
-    NVFP4_TILE_CONFIG(128, 128, 64, 64),
+    NVFP4_TILE_CONFIG_KS2R(128, 128, 64, 64),
     NVFP4_TILE_CONFIG(64, 64, 32, 32),
 };
 #undef NVFP4_TILE_CONFIG

@@ -489,7 +489,7 @@ def config_of(bm, bn):
                 if (mm.nvfp4_tile_config_info(c)["bm"], mm.nvfp4_tile_config_info(c)["bn"]) == (bm, bn))
 
 
-@pytest.mark.parametrize("tile", [(256, 128), (128, 256)])
+@pytest.mark.parametrize("tile", [(256, 128), (128, 256), (128, 128)])
 def test_long_k_split_over_waves(tile):
     """Calls whose groups all have at least 32 stages run the 256x128 and
     128x256 kernels that split K over the waves in every tile (128x128 wave
@@ -519,7 +519,7 @@ def test_long_k_split_over_waves(tile):
         assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), shape
 
 
-@pytest.mark.parametrize("tile", [(256, 128), (128, 256)])
+@pytest.mark.parametrize("tile", [(256, 128), (128, 256), (128, 128)])
 @pytest.mark.parametrize("seed", range(3))
 def test_random_long_k_split_over_waves(seed, tile):
     """Random long-K calls on the 256x128 and 128x256 tiles (seeded): every
