@@ -181,9 +181,10 @@ int nvfp4_grouped_gemm_stages(const int32_t* problem_sizes, const uint64_t* ptrs
  * the library allocates nothing.
  * The tables must stay unchanged until the kernel has finished.
  * Results are those of nvfp4_grouped_gemm with the same tile configuration,
- * bit for bit, except on calls whose groups all have k >= 4096: there the
- * by-value entry points' 256x128 and 128x256 kernels split K over the waves
- * in every tile (the host knows k), while this kernel splits it only in the
+ * bit for bit, except on calls whose groups with work all have k > 3968 (32
+ * or more 128-K stages): there the by-value entry points' 256x128, 128x256
+ * and 128x128 kernels split K over the waves in every tile (the host knows
+ * k), while this kernel splits it only in the
  * 256x128 tiles with at most four row blocks below m (as the by-value
  * kernels do on shorter calls), so the fp32 sums differ in rounding order
  * (both stay within the same bound of the exact result).
