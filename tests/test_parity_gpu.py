@@ -491,13 +491,14 @@ def config_of(bm, bn):
 
 @pytest.mark.parametrize("tile", [(256, 128), (128, 256), (128, 128)])
 def test_long_k_split_over_waves(tile):
-    """Calls whose groups all have at least 32 stages run the 256x128 and
-    128x256 kernels that split K over the waves in every tile (128x128 wave
-    tiles on full tiles): against the oracle, and bitwise against their
-    three-stage counterpart. Row counts give every number of row blocks below
-    m (1-8) and several tile rows; one group has k % 64 == 32."""
+    """Calls whose groups all have at least 32 stages run the 256x128,
+    128x256 and 128x128 kernels that split K over the waves in every tile:
+    against the oracle, and bitwise against their three-stage counterpart.
+    Row counts give every number of row blocks below m (1-8) and several tile
+    rows; two groups have k % 64 == 32, one of them k = 4000 (32 stages, the
+    shortest K that selects these kernels)."""
     cfg = config_of(*tile)
-    shapes = [(300, 264, 4096, 1), (129, 136, 4160, 1), (33, 72, 4128, 1), (256, 128, 4096, 2), (511, 8, 4096, 1),
+    shapes = [(300, 264, 4096, 1), (129, 136, 4160, 1), (33, 72, 4128, 1), (256, 128, 4096, 2), (511, 8, 4000, 1),
               (200, 392, 4096, 1), (1, 128, 4096, 1), (97, 520, 4096, 1)]
     groups = poison_padding(shapes, synth.make_custom(shapes, seed=4242))
     d = dev.upload(shapes, groups, c_guard=GUARD)
@@ -522,16 +523,17 @@ def test_long_k_split_over_waves(tile):
 @pytest.mark.parametrize("tile", [(256, 128), (128, 256), (128, 128)])
 @pytest.mark.parametrize("seed", range(3))
 def test_random_long_k_split_over_waves(seed, tile):
-    """Random long-K calls on the 256x128 and 128x256 tiles (seeded): every
-    group with work has k >= 4096, so whole tiles run the kernels that split K
-    over the waves in every tile; m in [0, 600] (several tile rows, any row
-    blocks below m), n a multiple of 8 up to 264, k in {4096, 4128, 4160,
-    4224}, l in {1, 2} (k = 0 groups included, which do not count against the
-    choice). Against the oracle, and stream-K on the same call for comparison."""
+    """Random long-K calls on the 256x128, 128x256 and 128x128 tiles (seeded):
+    every group with work has at least 32 stages, so whole tiles run the
+    kernels that split K over the waves in every tile; m in [0, 600] (several
+    tile rows, any row blocks below m), n a multiple of 8 up to 264, k in
+    {4000, 4096, 4128, 4160, 4224}, l in {1, 2} (k = 0 groups included, which
+    do not count against the choice). Against the oracle, and stream-K on the
+    same call for comparison."""
     cfg = config_of(*tile)
     rng = np.random.default_rng(7700 + seed)
     g = int(rng.integers(2, 9))
-    shapes = [(int(rng.integers(0, 601)), 8 * int(rng.integers(1, 34)), int(rng.choice([4096, 4128, 4160, 4224])),
+    shapes = [(int(rng.integers(0, 601)), 8 * int(rng.integers(1, 34)), int(rng.choice([4000, 4096, 4128, 4160, 4224])),
                int(rng.choice([1, 1, 2]))) for _ in range(g)]
     shapes[-1] = (shapes[-1][0], shapes[-1][1], 0, 1) if seed == 2 else shapes[-1]
     groups = synth.make_custom(shapes, seed=int(rng.integers(1 << 30)))
