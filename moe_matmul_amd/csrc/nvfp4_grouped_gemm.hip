@@ -1016,13 +1016,13 @@ struct GemmKernel {
     f16x8 b[NBK];
   };
   // Per-lane LDS offsets of a wave's first A and B chunk (8 bytes into the
-  // chunk for the second substep pair of KS4), of its A scale chunk(s) (for
-  // KS2R its first word there: row blocks rpart + 2i sit in atom i / 2, word
-  // rpart + 2 (i % 2)) and B scale words inside a stage; and the shift that
-  // brings the lane's scale bytes (two 16-blocks, or KS4's one) to the bottom
-  // of a word.
+  // chunk for the second substep pair of KS4), of its A scale chunk(s) and B
+  // scale words inside a stage; the shift that brings the lane's scale bytes
+  // (two 16-blocks, or KS4's one) to the bottom of a word; and, for KS2R, the
+  // wave's word in each A scale chunk (row blocks rpart + 2i sit in atom
+  // i / 2, word rpart + 2 (i % 2)).
   struct KsBases {
-    int a, b, sa, sb, shift;
+    int a, b, sa, sb, shift, rpart;
   };
   template <int MODE>
   __device__ __forceinline__ KsBases ks_bases() const {
@@ -1035,9 +1035,10 @@ struct GemmKernel {
     KsBases b;
     b.a = lds_off(r0 + lr, kk * 2 + h) + sub * 8;
     b.b = A_BYTES + lds_off(c0 + lr, kk * 2 + h) + sub * 8;
-    b.sa = A_BYTES + B_BYTES + lr * 16 + kk * 512 + (MODE == KS2R ? npart * 4 : 0);
+    b.sa = A_BYTES + B_BYTES + lr * 16 + kk * 512;
     b.sb = A_BYTES + B_BYTES + (A_ATOMS + (c0 >> 7)) * 1024 + lr * 16 + ((c0 & 127) >> 5) * 4 + kk * 512;
     b.shift = h * 16 + sub * 8;
+    b.rpart = MODE == KS2R ? npart : 0;
     return b;
   }
   template <int MODE, int R, int NBK, int P>
@@ -1045,14 +1046,28 @@ struct GemmKernel {
     typedef typename KsRaw<R, NBK, P>::chunk chunk;
     constexpr int AS = MODE == KS2R ? 64 : 32;  // rows between the wave's A blocks
     const uint8_t* St = smem + buf * STAGE_BYTES;
-    // the scales first: they are converted before the first fragment is
-    // dequantised, and LDS reads complete in issue order
+    if constexpr (kKsScalesFirst) ks_read_scales<MODE>(r, St, bs);
+#pragma unroll
+    for (int i = 0; i < R; ++i) r.a[i] = *reinterpret_cast<const chunk*>(St + bs.a + i * AS * kRowBytes);
+#pragma unroll
+    for (int j = 0; j < NBK; ++j) r.b[j] = *reinterpret_cast<const chunk*>(St + bs.b + j * 32 * kRowBytes);
+    if constexpr (!kKsScalesFirst) ks_read_scales<MODE>(r, St, bs);
+  }
+  // The scale words of ks_read. The 128x128 kernels read them before the
+  // operand chunks: they are converted before the first fragment is
+  // dequantised and LDS reads complete in issue order, so the conversion
+  // then waits for them alone (2-3% faster on long-K MoE shapes). The
+  // 256x128 kernels measured up to 4% slower that way, the 128x256 ones
+  // within +-1.5%: they read them last.
+  static constexpr bool kKsScalesFirst = BM == 128 && BN == 128;
+  template <int MODE, int R, int NBK, int P>
+  __device__ __forceinline__ void ks_read_scales(KsRaw<R, NBK, P>& r, const uint8_t* St, const KsBases& bs) const {
     if constexpr (MODE == KS2R) {
 #pragma unroll
       for (int a = 0; a < (R + 1) / 2; ++a) {
-        const uint32_t* c = reinterpret_cast<const uint32_t*>(St + bs.sa + a * 1024);
-        r.sa[2 * a] = c[0];
-        if (2 * a + 1 < R) r.sa[2 * a + 1] = c[2];
+        const u32x4 c = *reinterpret_cast<const u32x4*>(St + bs.sa + a * 1024);
+        r.sa[2 * a] = bs.rpart ? c[1] : c[0];
+        if (2 * a + 1 < R) r.sa[2 * a + 1] = bs.rpart ? c[3] : c[2];
       }
     } else {
       const u32x4 c = *reinterpret_cast<const u32x4*>(St + bs.sa);
@@ -1067,10 +1082,6 @@ struct GemmKernel {
 #pragma unroll
       for (int j = 0; j < NW; ++j) r.sb[a * NW + j] = cb[j];
     }
-#pragma unroll
-    for (int i = 0; i < R; ++i) r.a[i] = *reinterpret_cast<const chunk*>(St + bs.a + i * AS * kRowBytes);
-#pragma unroll
-    for (int j = 0; j < NBK; ++j) r.b[j] = *reinterpret_cast<const chunk*>(St + bs.b + j * 32 * kRowBytes);
   }
   template <int R, int NBK, int P>
   __device__ __forceinline__ static void ks_convert(KsScales<R, NBK>& s, const KsRaw<R, NBK, P>& r, int shift) {
@@ -1154,9 +1165,13 @@ struct GemmKernel {
     block_sync();
     const StageIssue si = prep_issue(ld);
     ks_read<MODE>(r, (uint32_t)(g + 1) % NS, bs);  // unused after the last stage
-    // the scale reads, then the operand chunks
-    __builtin_amdgcn_sched_group_barrier(kSchedDSRead, (NBK + 3) / 4 + (MODE == KS2R ? (R + 1) / 2 : 1), 0);
-    __builtin_amdgcn_sched_group_barrier(kSchedDSRead, R + NBK, 0);
+    if constexpr (kKsScalesFirst) {  // the scale reads, then the operand chunks
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, (NBK + 3) / 4 + (MODE == KS2R ? (R + 1) / 2 : 1), 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead, R + NBK, 0);
+    } else {
+      __builtin_amdgcn_sched_group_barrier(kSchedDSRead,
+                                           R + NBK + (NBK + 3) / 4 + (MODE == KS2R ? (R + 1) / 2 : 1), 0);
+    }
     ks_step<0, true, 0, L>(acc, f1, f0, r, s, bs.shift, &si);
     ks_pin(f0, s);
     advance(ld);
