@@ -253,6 +253,32 @@ struct KernargSrc {
   __device__ __forceinline__ int tile_prefix(int c) const { return args.tile_prefix[c]; }
   __device__ __forceinline__ const ClassArgs& cls(int c) const { return args.cls[c]; }
   __device__ __forceinline__ int nk(int c) const { return args.cls[c].nk; }
+  // The first tile's lookup is a chain of dependent scalar loads (grid and
+  // class count, the binary search over the tile prefix, then the class);
+  // each would miss the scalar cache in turn. One load per 64-byte line of
+  // the class table, the prefixes and the counts, all issued at once at the
+  // start, puts those lines in the cache for the price of about one miss.
+  // The 21 loads read inside the argument block. Their values are not used:
+  // every load writes the same register, and the block waits for all of them
+  // before it ends.
+  __device__ __forceinline__ void prefetch() const {
+    static_assert(offsetof(KernelArgs, whole_tiles) + 4 <= 21 * 64, "the lines below cover the counts");
+    const KernelArgs* p = &args;
+    uint32_t x;
+    asm volatile(
+        "s_load_dword %0, %1, 0x0\n s_load_dword %0, %1, 0x40\n s_load_dword %0, %1, 0x80\n"
+        "s_load_dword %0, %1, 0xc0\n s_load_dword %0, %1, 0x100\n s_load_dword %0, %1, 0x140\n"
+        "s_load_dword %0, %1, 0x180\n s_load_dword %0, %1, 0x1c0\n s_load_dword %0, %1, 0x200\n"
+        "s_load_dword %0, %1, 0x240\n s_load_dword %0, %1, 0x280\n s_load_dword %0, %1, 0x2c0\n"
+        "s_load_dword %0, %1, 0x300\n s_load_dword %0, %1, 0x340\n"
+        "s_waitcnt lgkmcnt(7)\n"  // (at most 15 in flight: the counter has four bits)
+        "s_load_dword %0, %1, 0x380\n"
+        "s_load_dword %0, %1, 0x3c0\n s_load_dword %0, %1, 0x400\n s_load_dword %0, %1, 0x440\n"
+        "s_load_dword %0, %1, 0x480\n s_load_dword %0, %1, 0x4c0\n s_load_dword %0, %1, 0x500\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&s"(x)
+        : "s"(p));
+  }
 };
 
 // ... or group tables in device memory. There the kernel makes the classes
@@ -300,6 +326,7 @@ struct DeviceSrc {
   static_assert(R >= 1 && R <= kMaxRowClasses, "row classes");
   const DeviceGroupArgs& args;
   const int32_t* prefix;  // LDS: first tile of class c for c = 0 .. R G (prefix[R G] = all tiles)
+  __device__ __forceinline__ void prefetch() const {}  // (the classes are in LDS by then)
   __device__ __forceinline__ int grid() const { return args.grid; }
   __device__ __forceinline__ bool split() const { return false; }
   __device__ __forceinline__ int total_tiles() const {
@@ -453,6 +480,7 @@ struct GemmKernel {
   }
 
   __device__ __forceinline__ GemmKernel(const Src& s, uint8_t* sm) : src(s), smem(sm) {
+    s.prefetch();
     const int tid = threadIdx.x;
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
