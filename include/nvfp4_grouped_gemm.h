@@ -304,6 +304,20 @@ int nvfp4_select_tile_config(const int32_t* problem_sizes, int num_groups, int n
 int nvfp4_launch_geometry(const int32_t* problem_sizes, int num_groups, int num_cus, int cfg, int split,
                           int64_t* total_tiles, int* grid, int* split_used, size_t* workspace_bytes);
 
+/*
+ * nvfp4_splits_k_over_waves - whether nvfp4_grouped_gemm and its _config,
+ * _ex, _scratch and _stages forms run the plan for these sizes (configuration
+ * `cfg` and split mode `split`, -1 = heuristic, as in nvfp4_launch_geometry)
+ * with the kernels that split K over the four waves of every tile: whole
+ * tiles of the 256x128, 128x256 or 128x128 configuration, every group with
+ * m, n and k > 0 having at least 32 stages of 128 K (k > 3968). Their fp32
+ * sums are then added in another order than in the kernels that split K only
+ * in light tiles, or not at all (the results differ in the last bits only,
+ * within the same bound of the exact result). Host only, no HIP call.
+ * Returns 1 or 0, or NVFP4_ERR_INVALID / NVFP4_ERR_CONFIG.
+ */
+int nvfp4_splits_k_over_waves(const int32_t* problem_sizes, int num_groups, int num_cus, int cfg, int split);
+
 /* Size in bytes of one tiled scale tensor for `rows` rows and `k` K-elements,
  * l batches: ceil(rows/128)*128 * ceil(k/64)*4 * l. Returns 0 if any is < 0. */
 size_t nvfp4_sf_bytes(int rows, int k, int l);

@@ -9,6 +9,6 @@ from ._binding import (  # noqa: F401
     NVFP4_MAX_DEVICE_GROUPS, NVFP4_MAX_GROUPS, NVFP4_OK, NVFP4_SCRATCH_BYTES, Nvfp4Error, load_library, nvfp4_device_group_tiles,
     nvfp4_error_string, nvfp4_grouped_gemm, nvfp4_grouped_gemm_config, nvfp4_grouped_gemm_device,
     nvfp4_grouped_gemm_ex, nvfp4_grouped_gemm_pow2, nvfp4_grouped_gemm_scratch, nvfp4_grouped_gemm_stages, nvfp4_grouped_gemm_validate, nvfp4_last_hip_error, nvfp4_launch_geometry,
-    nvfp4_num_tile_configs, nvfp4_select_tile_config, nvfp4_sf_bytes, nvfp4_split_plan, nvfp4_tile_config_info, nvfp4_workspace_bytes,
+    nvfp4_num_tile_configs, nvfp4_select_tile_config, nvfp4_sf_bytes, nvfp4_split_plan, nvfp4_splits_k_over_waves, nvfp4_tile_config_info, nvfp4_workspace_bytes,
     prepare,
 )

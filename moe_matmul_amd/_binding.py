@@ -53,6 +53,7 @@ def load_library() -> ctypes.CDLL:
         "nvfp4_select_tile_config": (ctypes.c_int, [i32p, ctypes.c_int, ctypes.c_int]),
         "nvfp4_launch_geometry": (ctypes.c_int, [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                  i64p, ip, ip, ctypes.POINTER(ctypes.c_size_t)]),
+        "nvfp4_splits_k_over_waves": (ctypes.c_int, [i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]),
         "nvfp4_grouped_gemm_ex": (ctypes.c_int, [i32p, u64p, u64p, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t,
                                                  ctypes.c_int, ctypes.c_int, ctypes.c_void_p]),
         "nvfp4_grouped_gemm_scratch": (ctypes.c_int, [i32p, u64p, u64p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -186,6 +187,15 @@ def nvfp4_launch_geometry(problem_sizes, num_cus: int, cfg: int = -1, split: int
     if rc < 0:
         raise Nvfp4Error(rc, "nvfp4_launch_geometry")
     return dict(config=rc, total_tiles=tiles.value, grid=grid.value, split=used.value, workspace_bytes=ws.value)
+
+
+def nvfp4_splits_k_over_waves(problem_sizes, num_cus: int, cfg: int = -1, split: int = -1, num_groups=None) -> bool:
+    """Whether the plan runs the kernels that split K over the waves in every tile."""
+    ps, g = _sizes(problem_sizes)
+    rc = load_library().nvfp4_splits_k_over_waves(ps, _groups(num_groups, ps, g), int(num_cus), int(cfg), int(split))
+    if rc < 0:
+        raise Nvfp4Error(rc, "nvfp4_splits_k_over_waves")
+    return rc == 1
 
 
 def nvfp4_grouped_gemm_ex(problem_sizes, ptrs_abc, ptrs_sfa_sfb, num_groups=None, workspace=0, workspace_bytes=0,

@@ -2248,6 +2248,18 @@ int64_t group_tiles(const int32_t* ps, int g, int cfg) {
 
 int group_stages(const int32_t* ps, int g) { return (int)ceil_div64(ps[4 * g + 2], kBK); }
 
+// Whether a whole-tile call of the general entry points on configuration cfg
+// runs the kernels that split K over the waves in every tile: cfg has them,
+// and every group with work (m, n and k > 0) has at least kKS2RMinStages
+// 128-K stages.
+bool splits_k_everywhere(const int32_t* ps, int G, int cfg) {
+  if (kConfigs[cfg].kernel_ks2r[0] == nullptr) return false;
+  for (int g = 0; g < G; ++g)
+    if (ps[4 * g + 0] > 0 && ps[4 * g + 1] > 0 && ps[4 * g + 2] > 0 && group_stages(ps, g) < kKS2RMinStages)
+      return false;
+  return true;
+}
+
 // Largest number of 32-row blocks a wave computes in a tile with `rows` rows
 // below m (row blocks alternate between the two wave rows).
 int max_active_blocks(int64_t rows, int bm) {
@@ -2665,9 +2677,7 @@ int launch(const int32_t* ps, const uint64_t* abc, const uint64_t* sf, int G, vo
   bool kpad = false;
   for (int g = 0; g < G; ++g) kpad = kpad || (ps[4 * g + 2] % 64 != 0);
   void (*kernel)(KernelArgs) = tc.kernel[plan.split ? 1 : 0][mx_status ? 1 : 0][kpad ? 1 : 0];
-  bool all_long = tc.kernel_ks2r[0] != nullptr && !plan.split && mx_status == nullptr;
-  for (int g = 0; g < G && all_long; ++g)
-    if (ps[4 * g + 0] > 0 && ps[4 * g + 1] > 0 && ps[4 * g + 2] > 0) all_long = group_stages(ps, g) >= kKS2RMinStages;
+  const bool all_long = !plan.split && mx_status == nullptr && splits_k_everywhere(ps, G, plan.cfg);
   if (all_long) kernel = tc.kernel_ks2r[kpad ? 1 : 0];
   if (stages == 3) kernel = all_long ? tc.kernel_ks2r_ns3 : tc.kernel_ns3[plan.split ? 1 : 0];
   if (plan.split) {
@@ -2787,6 +2797,13 @@ int nvfp4_tile_config_info(int cfg, int* bm, int* bn, int* bk, int* threads) {
 int nvfp4_select_tile_config(const int32_t* ps, int G, int num_cus) {
   if (sizes_ok(ps, G) != NVFP4_OK || num_cus < 1) return NVFP4_ERR_INVALID;
   return choose_plan(ps, G, num_cus, -1, -1, SIZE_MAX).cfg;
+}
+
+int nvfp4_splits_k_over_waves(const int32_t* ps, int G, int num_cus, int cfg, int split) {
+  if (sizes_ok(ps, G) != NVFP4_OK || num_cus < 1) return NVFP4_ERR_INVALID;
+  if (cfg < -1 || cfg >= kNumConfigs || split < -1 || split > 1) return NVFP4_ERR_CONFIG;
+  const Plan p = cached_plan(ps, G, num_cus, cfg, split, SIZE_MAX);
+  return !p.split && splits_k_everywhere(ps, G, p.cfg) ? 1 : 0;
 }
 
 int nvfp4_launch_geometry(const int32_t* ps, int G, int num_cus, int cfg, int split, int64_t* total_tiles,

@@ -206,6 +206,38 @@ def test_tile_configs_and_geometry():
         assert mm.nvfp4_select_tile_config(synth.workload_shapes(idx), 256) == small
 
 
+def test_k_split_over_waves_choice():
+    """Calls run the kernels that split K over the waves in every tile when
+    they take whole tiles of a 256x128, 128x256 or 128x128 configuration and
+    every group with work has at least 32 stages of 128 K (k > 3968); groups
+    with m, n or k = 0 do not count, stream-K plans and the other
+    configurations never do."""
+    n = mm.nvfp4_num_tile_configs()
+    shape_of = {(mm.nvfp4_tile_config_info(c)["bm"], mm.nvfp4_tile_config_info(c)["bn"]): c for c in range(n)}
+    split_cfgs = [shape_of[s] for s in ((256, 128), (128, 256), (128, 128))]
+    other_cfgs = [c for c in range(n) if c not in split_cfgs]
+    long_k = [(300, 264, 4096, 1), (129, 136, 4000, 1), (33, 72, 7168, 2)]
+    for c in split_cfgs:
+        assert mm.nvfp4_splits_k_over_waves(long_k, 256, c, 0)
+        assert not mm.nvfp4_splits_k_over_waves(long_k, 256, c, 1)
+        # 31 stages in one group: no
+        assert not mm.nvfp4_splits_k_over_waves(long_k + [(8, 8, 3968, 1)], 256, c, 0)
+        # the shortest K that counts: 32 stages (k = 3969 is not a valid k; 4000 is)
+        assert mm.nvfp4_splits_k_over_waves([(64, 64, 4000, 1)], 256, c, 0)
+        # empty groups of short K do not count
+        for empty in ((0, 64, 64, 1), (64, 0, 64, 1), (64, 64, 0, 1)):
+            assert mm.nvfp4_splits_k_over_waves(long_k + [empty], 256, c, 0), empty
+    for c in other_cfgs:
+        assert not mm.nvfp4_splits_k_over_waves(long_k, 256, c, 0)
+    # the heuristic's plan for the benchmark workloads: only the long-K MoE workload
+    assert [mm.nvfp4_splits_k_over_waves(synth.workload_shapes(i), 256) for i in range(5)] == [
+        False, False, True, False, False]
+    with pytest.raises(mm.Nvfp4Error):
+        mm.nvfp4_splits_k_over_waves(long_k, 256, n, 0)
+    with pytest.raises(mm.Nvfp4Error):
+        mm.nvfp4_splits_k_over_waves([(64, 64, 48, 1)], 256)  # k not a multiple of 32
+
+
 def test_split_plan_covers_every_unit_once():
     """Stream-K plans: whole rounds of one tile per workgroup, then contiguous
     (possibly empty) unit ranges in workgroup order that cover exactly the
