@@ -500,6 +500,7 @@ def test_long_k_split_over_waves(tile):
     cfg = config_of(*tile)
     shapes = [(300, 264, 4096, 1), (129, 136, 4160, 1), (33, 72, 4128, 1), (256, 128, 4096, 2), (511, 8, 4000, 1),
               (200, 392, 4096, 1), (1, 128, 4096, 1), (97, 520, 4096, 1)]
+    assert mm.nvfp4_splits_k_over_waves(shapes, torch.cuda.get_device_properties(0).multi_processor_count, cfg, 0)
     groups = poison_padding(shapes, synth.make_custom(shapes, seed=4242))
     d = dev.upload(shapes, groups, c_guard=GUARD)
     abc, sf = dev.pointer_tables(d)
@@ -536,6 +537,7 @@ def test_random_long_k_split_over_waves(seed, tile):
     shapes = [(int(rng.integers(0, 601)), 8 * int(rng.integers(1, 34)), int(rng.choice([4000, 4096, 4128, 4160, 4224])),
                int(rng.choice([1, 1, 2]))) for _ in range(g)]
     shapes[-1] = (shapes[-1][0], shapes[-1][1], 0, 1) if seed == 2 else shapes[-1]
+    assert mm.nvfp4_splits_k_over_waves(shapes, torch.cuda.get_device_properties(0).multi_processor_count, cfg, 0)
     groups = synth.make_custom(shapes, seed=int(rng.integers(1 << 30)))
     ref = O.grouped_gemm(shapes, poison_padding(shapes, groups))
     for split in (0, 1):
