@@ -187,7 +187,8 @@ int nvfp4_grouped_gemm_stages(const int32_t* problem_sizes, const uint64_t* ptrs
  * k), while this kernel splits it only in the
  * 256x128 tiles with at most four row blocks below m (as the by-value
  * kernels do on shorter calls), so the fp32 sums differ in rounding order
- * (both stay within the same bound of the exact result).
+ * (both stay within the same bound of the exact result);
+ * nvfp4_splits_k_over_waves tells which calls those are.
  * Returns NVFP4_OK once enqueued, NVFP4_ERR_HIP if the launch failed.
  */
 #define NVFP4_MAX_DEVICE_GROUPS 512
