@@ -61,13 +61,19 @@ def super_batch_shapes(seed, batches=15, per_batch=8):
 
 @pytest.mark.parametrize("cfg", [-1, 0, 1, 2, 3, 4])
 def test_device_tables_match_oracle_and_host_path(cfg):
-    """Small workloads and ragged edge cases: oracle parity, and bitwise
-    equality with the by-value entry point (whole tiles, same configuration)."""
+    """Small workloads, ragged edge cases and a long-K call: oracle parity, and
+    bitwise equality with the by-value entry point (whole tiles, same
+    configuration) except where that runs the kernels that split K over the
+    waves in every tile (long K on 256x128, 128x256 or 128x128 tiles): there
+    both are checked against the oracle."""
     cases = [synth.make_workload(0), synth.make_workload(1)]
     edge = [(127, 136, 192, 1), (0, 64, 128, 1), (129, 264, 320, 1), (40, 48, 0, 1), (64, 0, 128, 1),
             (100, 136, 192, 2), (1, 8, 64, 1), (257, 8, 128, 1)]  # at most 8: the by-value limit
     cases.append((edge, synth.make_custom(edge, seed=515)))
+    long_k = [(300, 264, 4096, 1), (129, 136, 4160, 1), (33, 72, 4000, 1)]
+    cases.append((long_k, synth.make_custom(long_k, seed=516)))
     host_cfg = 0 if cfg < 0 else cfg  # -1: the entry point's default, 256x256 tiles
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
     for shapes, groups in cases:
         announce(f"device tables cfg={cfg} shapes={shapes}")
         d = dev.upload(shapes, groups, c_guard=GUARD)
@@ -78,7 +84,11 @@ def test_device_tables_match_oracle_and_host_path(cfg):
         h = dev.upload(shapes, groups, c_guard=GUARD)
         dev.run(shapes, h, tile_config=host_cfg, split_mode=0, workspace=None)
         torch.cuda.synchronize()
-        for (m, n, k, l), a, b in zip(shapes, got, dev.c_as_numpy(shapes, h)):
+        host = dev.c_as_numpy(shapes, h)
+        if mm.nvfp4_splits_k_over_waves(shapes, cus, host_cfg, 0):
+            check_against_oracle(shapes, groups, host)
+            continue
+        for (m, n, k, l), a, b in zip(shapes, got, host):
             assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), (m, n, k, l)
 
 
